@@ -1,0 +1,311 @@
+// Batched single-token decode attention over the paged KV cache: split-K flash-decoding.
+//
+// Decode emits one token per request per step over the request's whole cache, with concurrent
+// requests packed into one batch ("Optimizing ASR Models to Transcribe 90-Minute Multi-Speaker
+// Audio", sections ASR Model Primer and Batched Inference).  With one query token per head the
+// work is two flops per KV byte, far below the MI355X ridge point, so the kernels are built to
+// stream K/V from HBM once, with coalesced 16-byte loads, and keep every other cost off the
+// memory critical path.
+//
+// decode_split: one wavefront per work item = (request b, split s, KV head g), where split s is
+//   the logical tokens [512 s, min(512 s + 512, L_b)).  Items are numbered densely: the flat split
+//   index f counts the splits of requests 0..b-1 first (ceil(L/512) each), so the grid is
+//   8 * sum_b ceil(L_b / 512) waves plus a tail of waves that find f beyond the total and exit.
+//   Both query heads of the GQA group (2g, 2g+1) are served from the same K/V loads.  The wave
+//   writes the split's normalised partial output and its log-sum-exp.
+// decode_merge: one wavefront per (request, query head) combines that request's partials with
+//   weights exp(lse_s - LSE).
+//
+// Lane layout inside decode_split for one 64-token page: lane = 8*sg + o.  The lane handles the
+// 8 slots {8a + sg : a = 0..7} and, of each slot row (128 dims = 256 bytes), the two 16-byte
+// chunks o and 8 + o (dims 8o..8o+7 and 64+8o..64+8o+7).  One load instruction therefore reads 8
+// whole 128-byte lines.  A slot's score is the sum over its 8 lanes (three DPP steps); values are
+// accumulated with packed bf16 dot products pairing two slots per instruction.
+#include "device_util.h"
+#include "mtd_internal.h"
+
+namespace mtd {
+namespace {
+
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// Locate flat split f: request b, split s within b, and b's KV length.  Wave-uniform.
+// kv_lens are clamped to [0, max_kv_len] so the number of partials never exceeds the workspace.
+__device__ __forceinline__ bool locate_split(const int32_t* __restrict__ kv_lens, int batch,
+                                             int max_kv_len, int f, int lane, int& b, int& s,
+                                             int& len_b) {
+  int carry = 0;
+  for (int c0 = 0; c0 < batch; c0 += 64) {
+    const int idx = c0 + lane;
+    int len = idx < batch ? kv_lens[idx] : 0;
+    len = min(max(len, 0), max_kv_len);
+    const int n = (len + kSplit - 1) / kSplit;
+    const int incl = wave_incl_scan(n, lane);
+    const int chunk_total = __shfl(incl, 63, 64);
+    if (f < carry + chunk_total) {
+      const unsigned long long hit = __ballot(carry + incl > f);
+      const int lb = __ffsll(hit) - 1;
+      b = c0 + lb;
+      s = f - (carry + __shfl(incl - n, lb, 64));
+      len_b = __shfl(len, lb, 64);
+      return true;
+    }
+    carry += chunk_total;
+  }
+  return false;
+}
+
+__global__ __launch_bounds__(64) void decode_split_kernel(
+    const uint16_t* __restrict__ k_pages, const uint16_t* __restrict__ v_pages, int num_pages,
+    const uint16_t* __restrict__ q, const int32_t* __restrict__ kv_lens,
+    const int32_t* __restrict__ block_tables, int bt_stride, int batch, int max_kv_len,
+    float scale_log2, float* __restrict__ part_o, float* __restrict__ part_lse) {
+  const int lane = threadIdx.x;
+  const int f = blockIdx.x / kKvHeads;
+  const int g = blockIdx.x % kKvHeads;
+  int b, s, len;
+  if (!locate_split(kv_lens, batch, max_kv_len, f, lane, b, s, len)) return;
+
+  const int sg = lane >> 3;  // slot group: slots 8a + sg
+  const int o = lane & 7;    // chunks o and 8 + o of each row
+
+  // Query rows of heads 2g and 2g+1, this lane's 16 dims of each (as packed bf16 pairs).
+  uint4 qv[2][2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const uint16_t* qrow = q + ((size_t)b * kQHeads + kGroup * g + hh) * kHeadDim;
+    qv[hh][0] = *reinterpret_cast<const uint4*>(qrow + 8 * o);
+    qv[hh][1] = *reinterpret_cast<const uint4*>(qrow + 64 + 8 * o);
+  }
+
+  float m[2] = {kNegInf, kNegInf};  // running max (log2 units) over this lane's slots
+  float l[2] = {0.f, 0.f};          // running sum of exp2(x - m)
+  float acc[2][2][8];               // [head][chunk][dim] unnormalised output
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[hh][c][e] = 0.f;
+
+  const int tok0 = s * kSplit;
+  const int tok1 = min(tok0 + kSplit, len);
+  const int32_t* bt_row = block_tables + (size_t)b * bt_stride;
+
+  for (int e0 = tok0 / kPage; e0 * kPage < tok1; ++e0) {
+    const int page = bt_row[e0];
+    if (page < 0 || page >= num_pages) continue;
+    const int nvalid = min(kPage, tok1 - e0 * kPage);
+    const size_t blk = ((size_t)page * kKvHeads + g) * (kPage * kHeadDim);
+    const uint16_t* kb = k_pages + blk;
+    const uint16_t* vb = v_pages + blk;
+
+    uint4 kr[8][2], vr[8][2];
+#pragma unroll
+    for (int a = 0; a < 8; ++a)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        kr[a][c] = *reinterpret_cast<const uint4*>(kb + (8 * a + sg) * kHeadDim + (8 * c + o) * 8);
+#pragma unroll
+    for (int a = 0; a < 8; ++a)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        vr[a][c] = *reinterpret_cast<const uint4*>(vb + (8 * a + sg) * kHeadDim + (8 * c + o) * 8);
+
+    // Scores of slots 8a + sg for both heads, in log2 units.
+    float x[2][8];
+#pragma unroll
+    for (int a = 0; a < 8; ++a) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        float d = 0.f;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          d = dot2_bf16(kr[a][c].x, c == 0 ? qv[hh][0].x : qv[hh][1].x, d);
+          d = dot2_bf16(kr[a][c].y, c == 0 ? qv[hh][0].y : qv[hh][1].y, d);
+          d = dot2_bf16(kr[a][c].z, c == 0 ? qv[hh][0].z : qv[hh][1].z, d);
+          d = dot2_bf16(kr[a][c].w, c == 0 ? qv[hh][0].w : qv[hh][1].w, d);
+        }
+        x[hh][a] = sum8(d) * scale_log2;
+      }
+    }
+    if (nvalid < kPage) {  // partial last page: slots >= nvalid hold no token of this request
+#pragma unroll
+      for (int a = 0; a < 8; ++a) {
+        const bool ok = 8 * a + sg < nvalid;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) x[hh][a] = ok ? x[hh][a] : kNegInf;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          vr[a][c].x = ok ? vr[a][c].x : 0u;
+          vr[a][c].y = ok ? vr[a][c].y : 0u;
+          vr[a][c].z = ok ? vr[a][c].z : 0u;
+          vr[a][c].w = ok ? vr[a][c].w : 0u;
+        }
+      }
+    }
+
+    uint32_t pp[2][4];  // probabilities as bf16 pairs (slots 2k, 2k+1)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      float mx = x[hh][0];
+#pragma unroll
+      for (int a = 1; a < 8; ++a) mx = fmaxf(mx, x[hh][a]);
+      const float m_new = fmaxf(m[hh], mx);
+      const float m_use = m_new == kNegInf ? 0.f : m_new;
+      const float alpha = fast_exp2(m[hh] - m_use);
+      m[hh] = m_new;
+      float p[8];
+      float psum = 0.f;
+#pragma unroll
+      for (int a = 0; a < 8; ++a) {
+        p[a] = fast_exp2(x[hh][a] - m_use);
+        psum += p[a];
+      }
+      l[hh] = l[hh] * alpha + psum;
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[hh][c][e] *= alpha;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) pp[hh][k] = pack_bf16x2(p[2 * k], p[2 * k + 1]);
+    }
+
+    // acc[h][c][d] += p[2k] * v[slot 2k][d] + p[2k+1] * v[slot 2k+1][d]
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const uint32_t xw[4] = {vr[2 * k][c].x, vr[2 * k][c].y, vr[2 * k][c].z, vr[2 * k][c].w};
+        const uint32_t yw[4] = {vr[2 * k + 1][c].x, vr[2 * k + 1][c].y, vr[2 * k + 1][c].z,
+                                vr[2 * k + 1][c].w};
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t lo = pack_lo16(xw[w], yw[w]);
+          const uint32_t hi = pack_hi16(xw[w], yw[w]);
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            acc[hh][c][2 * w] = dot2_bf16(lo, pp[hh][k], acc[hh][c][2 * w]);
+            acc[hh][c][2 * w + 1] = dot2_bf16(hi, pp[hh][k], acc[hh][c][2 * w + 1]);
+          }
+        }
+      }
+    }
+  }
+
+  // Combine the 8 slot groups (lanes xor 8, 16, 32) and write the split's partial.
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    float mm = m[hh];
+    mm = fmaxf(mm, __shfl_xor(mm, 8, 64));
+    mm = fmaxf(mm, __shfl_xor(mm, 16, 64));
+    mm = fmaxf(mm, __shfl_xor(mm, 32, 64));
+    const float w = m[hh] == kNegInf ? 0.f : fast_exp2(m[hh] - mm);
+    float ll = l[hh] * w;
+    ll += __shfl_xor(ll, 8, 64);
+    ll += __shfl_xor(ll, 16, 64);
+    ll += __shfl_xor(ll, 32, 64);
+    const float inv = 1.f / ll;
+    float* orow = part_o + ((size_t)f * kQHeads + kGroup * g + hh) * kHeadDim;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      float r[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float v = acc[hh][c][e] * w;
+        v += __shfl_xor(v, 8, 64);
+        v += __shfl_xor(v, 16, 64);
+        v += __shfl_xor(v, 32, 64);
+        r[e] = v * inv;
+      }
+      if (sg == 0) {
+        float4* dst = reinterpret_cast<float4*>(orow + 64 * c + 8 * o);
+        dst[0] = make_float4(r[0], r[1], r[2], r[3]);
+        dst[1] = make_float4(r[4], r[5], r[6], r[7]);
+      }
+    }
+    if (lane == 0) part_lse[(size_t)f * kQHeads + kGroup * g + hh] = (mm + log2f(ll)) * kLn2;
+  }
+}
+
+// One wavefront per (request b, query head h); 4 heads per workgroup.
+__global__ __launch_bounds__(256) void decode_merge_kernel(
+    const int32_t* __restrict__ kv_lens, int batch, int max_kv_len,
+    const float* __restrict__ part_o, const float* __restrict__ part_lse, float* __restrict__ out,
+    float* __restrict__ lse_out) {
+  const int lane = threadIdx.x & 63;
+  const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int b = blockIdx.y;
+  // First flat split of request b = sum over earlier requests of ceil(L / 512).
+  int first = 0, len = 0;
+  for (int c0 = 0; c0 <= b; c0 += 64) {
+    const int idx = c0 + lane;
+    int ln = idx < batch ? kv_lens[idx] : 0;
+    ln = min(max(ln, 0), max_kv_len);
+    const int n = (ln + kSplit - 1) / kSplit;
+    if (b < c0 + 64) {
+      const int before = idx < b ? n : 0;
+      first += wave_sum_int(before);
+      len = __shfl(ln, b - c0, 64);
+    } else {
+      first += wave_sum_int(n);
+    }
+  }
+  const int n_parts = (len + kSplit - 1) / kSplit;
+  float* orow = out + ((size_t)b * kQHeads + h) * kHeadDim;
+  if (n_parts == 0) {  // no keys: defined as zero output and LSE = -inf
+    reinterpret_cast<float2*>(orow)[lane] = make_float2(0.f, 0.f);
+    if (lane == 0) lse_out[(size_t)b * kQHeads + h] = kNegInf;
+    return;
+  }
+  // Max LSE over the parts (natural log), then weights.
+  float mx = kNegInf;
+  for (int p = lane; p < n_parts; p += 64)
+    mx = fmaxf(mx, part_lse[(size_t)(first + p) * kQHeads + h]);
+  mx = wave_max(mx);
+  float wsum = 0.f;
+  float2 acc = make_float2(0.f, 0.f);
+  for (int p0 = 0; p0 < n_parts; p0 += 64) {
+    const int p = p0 + lane;
+    const float w = p < n_parts ? fast_exp2((part_lse[(size_t)(first + p) * kQHeads + h] - mx) * kLog2e) : 0.f;
+    wsum += w;
+    const int cnt = min(64, n_parts - p0);
+    for (int j = 0; j < cnt; ++j) {
+      const float wj = __shfl(w, j, 64);
+      const float2 v = reinterpret_cast<const float2*>(
+          part_o + ((size_t)(first + p0 + j) * kQHeads + h) * kHeadDim)[lane];
+      acc.x += wj * v.x;
+      acc.y += wj * v.y;
+    }
+  }
+  wsum = wave_sum(wsum);
+  const float inv = 1.f / wsum;
+  reinterpret_cast<float2*>(orow)[lane] = make_float2(acc.x * inv, acc.y * inv);
+  if (lane == 0) lse_out[(size_t)b * kQHeads + h] = mx + logf(wsum);
+}
+
+}  // namespace
+
+size_t decode_workspace_bytes(int batch, int max_kv_len) {
+  const size_t parts = (size_t)batch * (size_t)((max_kv_len + kSplit - 1) / kSplit);
+  return parts * kQHeads * (kHeadDim + 1) * sizeof(float);
+}
+
+hipError_t launch_decode(const KvPools& kv, const uint16_t* q, const int32_t* kv_lens,
+                         const int32_t* block_tables, int bt_stride, int batch, int max_kv_len,
+                         float scale, void* workspace, float* out, float* lse, hipStream_t stream) {
+  const size_t parts = (size_t)batch * (size_t)((max_kv_len + kSplit - 1) / kSplit);
+  float* part_o = static_cast<float*>(workspace);
+  float* part_lse = part_o + parts * kQHeads * kHeadDim;
+  const unsigned n_waves = (unsigned)(parts * kKvHeads);
+  decode_split_kernel<<<dim3(n_waves), dim3(64), 0, stream>>>(
+      kv.k, kv.v, kv.num_pages, q, kv_lens, block_tables, bt_stride, batch, max_kv_len,
+      scale * kLog2e, part_o, part_lse);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  decode_merge_kernel<<<dim3(kQHeads / 4, batch), dim3(256), 0, stream>>>(
+      kv_lens, batch, max_kv_len, part_o, part_lse, out, lse);
+  return hipGetLastError();
+}
+
+}  // namespace mtd

@@ -1,0 +1,169 @@
+// C-ABI layer of libmtd: argument validation on the host, then kernel launches on the caller's
+// stream.  Every check below runs before any HIP call, so each error path can be exercised on a
+// machine without a GPU.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/mtd.h"
+#include "mtd_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return MTD_OK;
+}
+
+int hip_status(hipError_t err, const char* what) {
+  if (err == hipSuccess) return ok();
+  return fail(MTD_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
+}
+
+// Checks shared by all calls on the layer description.
+int check_layer(const mtd_kv_layer_t* kv) {
+  if (kv == nullptr) return fail(MTD_ERR_INVALID_ARG, "kv is NULL");
+  if (kv->k_pages == nullptr || kv->v_pages == nullptr)
+    return fail(MTD_ERR_INVALID_ARG, "kv->k_pages / kv->v_pages is NULL");
+  if (kv->num_pages <= 0) return fail(MTD_ERR_INVALID_ARG, "kv->num_pages = %d", kv->num_pages);
+  if (kv->page_size != mtd::kPage)
+    return fail(MTD_ERR_UNSUPPORTED, "page_size %d (supported: %d)", kv->page_size, mtd::kPage);
+  if (kv->num_kv_heads != mtd::kKvHeads)
+    return fail(MTD_ERR_UNSUPPORTED, "num_kv_heads %d (supported: %d)", kv->num_kv_heads, mtd::kKvHeads);
+  if (kv->head_dim != mtd::kHeadDim)
+    return fail(MTD_ERR_UNSUPPORTED, "head_dim %d (supported: %d)", kv->head_dim, mtd::kHeadDim);
+  return MTD_OK;
+}
+
+int check_heads(int32_t num_q_heads, int32_t num_kv_heads) {
+  if (num_q_heads <= 0) return fail(MTD_ERR_INVALID_ARG, "num_q_heads = %d", num_q_heads);
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(MTD_ERR_UNSUPPORTED, "num_q_heads %d is not a multiple of num_kv_heads %d",
+                num_q_heads, num_kv_heads);
+  if (num_q_heads != mtd::kQHeads)
+    return fail(MTD_ERR_UNSUPPORTED, "num_q_heads %d (supported: %d)", num_q_heads, mtd::kQHeads);
+  return MTD_OK;
+}
+
+int check_scale(float scale) {
+  if (!(scale > 0.f) || !isfinite(scale)) return fail(MTD_ERR_INVALID_ARG, "scale must be finite and > 0");
+  return MTD_OK;
+}
+
+mtd::KvPools pools(const mtd_kv_layer_t* kv) {
+  return mtd::KvPools{static_cast<uint16_t*>(kv->k_pages), static_cast<uint16_t*>(kv->v_pages),
+                      kv->num_pages};
+}
+
+}  // namespace
+
+extern "C" {
+
+int mtd_kv_append(const mtd_kv_layer_t* kv, const void* k_new, const void* v_new,
+                  const int32_t* cu_new, const int32_t* start_pos, const int32_t* block_tables,
+                  int32_t bt_stride, int32_t n_req, int32_t n_new, void* stream) {
+  int st = check_layer(kv);
+  if (st != MTD_OK) return st;
+  if (n_req <= 0) return fail(MTD_ERR_INVALID_ARG, "n_req = %d", n_req);
+  if (n_new < 0) return fail(MTD_ERR_INVALID_ARG, "n_new = %d", n_new);
+  if (bt_stride <= 0) return fail(MTD_ERR_INVALID_ARG, "bt_stride = %d", bt_stride);
+  if (n_new > 0 && (k_new == nullptr || v_new == nullptr))
+    return fail(MTD_ERR_INVALID_ARG, "k_new / v_new is NULL");
+  if (cu_new == nullptr || start_pos == nullptr || block_tables == nullptr)
+    return fail(MTD_ERR_INVALID_ARG, "cu_new / start_pos / block_tables is NULL");
+  if (n_new == 0) return ok();
+  return hip_status(mtd::launch_kv_append(pools(kv), static_cast<const uint16_t*>(k_new),
+                                          static_cast<const uint16_t*>(v_new), cu_new, start_pos,
+                                          block_tables, bt_stride, n_req, n_new,
+                                          static_cast<hipStream_t>(stream)),
+                    "kv_append launch");
+}
+
+int mtd_attn_prefill_chunk(const mtd_kv_layer_t* kv, const void* q, int32_t chunk_len,
+                           int32_t prefix_len, const int32_t* block_table, int32_t block_table_len,
+                           int32_t num_q_heads, float scale, float* out, float* lse, void* stream) {
+  int st = check_layer(kv);
+  if (st != MTD_OK) return st;
+  if ((st = check_heads(num_q_heads, kv->num_kv_heads)) != MTD_OK) return st;
+  if ((st = check_scale(scale)) != MTD_OK) return st;
+  if (q == nullptr || block_table == nullptr || out == nullptr || lse == nullptr)
+    return fail(MTD_ERR_INVALID_ARG, "q / block_table / out / lse is NULL");
+  if (chunk_len <= 0) return fail(MTD_ERR_INVALID_ARG, "chunk_len = %d", chunk_len);
+  if (prefix_len < 0) return fail(MTD_ERR_INVALID_ARG, "prefix_len = %d", prefix_len);
+  const int64_t total = (int64_t)prefix_len + chunk_len;
+  if (total > MTD_MAX_CONTEXT)
+    return fail(MTD_ERR_CAPACITY, "prefix_len + chunk_len = %lld exceeds %d", (long long)total,
+                MTD_MAX_CONTEXT);
+  const int64_t pages = (total + mtd::kPage - 1) / mtd::kPage;
+  if (block_table_len < pages)
+    return fail(MTD_ERR_CAPACITY, "block_table_len %d < %lld pages needed", block_table_len,
+                (long long)pages);
+  return hip_status(mtd::launch_prefill(pools(kv), static_cast<const uint16_t*>(q), chunk_len,
+                                        prefix_len, block_table, scale, out, lse,
+                                        static_cast<hipStream_t>(stream)),
+                    "prefill launch");
+}
+
+size_t mtd_attn_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t max_kv_len,
+                                       int32_t head_dim) {
+  if (batch <= 0 || num_q_heads != mtd::kQHeads || head_dim != mtd::kHeadDim) return 0;
+  if (max_kv_len <= 0 || max_kv_len > MTD_MAX_CONTEXT) return 0;
+  return mtd::decode_workspace_bytes(batch, max_kv_len);
+}
+
+int mtd_attn_decode(const mtd_kv_layer_t* kv, const void* q, const int32_t* kv_lens,
+                    const int32_t* block_tables, int32_t bt_stride, int32_t batch,
+                    int32_t max_kv_len, int32_t num_q_heads, float scale, void* workspace,
+                    size_t workspace_bytes, float* out, float* lse, void* stream) {
+  int st = check_layer(kv);
+  if (st != MTD_OK) return st;
+  if ((st = check_heads(num_q_heads, kv->num_kv_heads)) != MTD_OK) return st;
+  if ((st = check_scale(scale)) != MTD_OK) return st;
+  if (q == nullptr || kv_lens == nullptr || block_tables == nullptr || out == nullptr || lse == nullptr)
+    return fail(MTD_ERR_INVALID_ARG, "q / kv_lens / block_tables / out / lse is NULL");
+  if (batch <= 0) return fail(MTD_ERR_INVALID_ARG, "batch = %d", batch);
+  if (max_kv_len <= 0) return fail(MTD_ERR_INVALID_ARG, "max_kv_len = %d", max_kv_len);
+  if (max_kv_len > MTD_MAX_CONTEXT)
+    return fail(MTD_ERR_CAPACITY, "max_kv_len %d exceeds %d", max_kv_len, MTD_MAX_CONTEXT);
+  const int64_t pages = ((int64_t)max_kv_len + mtd::kPage - 1) / mtd::kPage;
+  if (bt_stride < pages)
+    return fail(MTD_ERR_CAPACITY, "bt_stride %d < %lld pages for max_kv_len %d", bt_stride,
+                (long long)pages, max_kv_len);
+  const size_t need = mtd::decode_workspace_bytes(batch, max_kv_len);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(MTD_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  return hip_status(mtd::launch_decode(pools(kv), static_cast<const uint16_t*>(q), kv_lens,
+                                       block_tables, bt_stride, batch, max_kv_len, scale,
+                                       workspace, out, lse, static_cast<hipStream_t>(stream)),
+                    "decode launch");
+}
+
+const char* mtd_status_string(int status) {
+  switch (status) {
+    case MTD_OK: return "ok";
+    case MTD_ERR_INVALID_ARG: return "invalid argument";
+    case MTD_ERR_UNSUPPORTED: return "unsupported shape";
+    case MTD_ERR_CAPACITY: return "capacity exceeded";
+    case MTD_ERR_WORKSPACE: return "workspace too small";
+    case MTD_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* mtd_last_error(void) { return g_last_error; }
+
+int mtd_abi_version(void) { return MTD_ABI_VERSION; }
+
+}  // extern "C"

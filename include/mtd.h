@@ -1,0 +1,180 @@
+/*
+ * mtd.h - paged causal grouped-query attention for a Qwen3-style decoder on AMD MI355X (gfx950).
+ *
+ * The decoder these kernels serve is the Qwen3 text decoder of an audio LLM: 28 layers, hidden size
+ * 1024, grouped-query attention with 16 query heads over 8 key/value heads ("Optimizing ASR Models
+ * to Transcribe 90-Minute Multi-Speaker Audio", section ASR Model Primer, component table; the
+ * "MOSS-Transcribe-Diarize" cookbook, section Model Architecture).  head_dim is 128.  Its KV cache
+ * holds tens of thousands of audio tokens per request (up to a 128K context, cookbook section Model
+ * Architecture).  Three operations carry the attention work:
+ *
+ *   mtd_kv_append           write the K/V rows of new tokens into their cache pages
+ *   mtd_attn_prefill_chunk  causal attention of one prefill chunk over the paged cache
+ *                           ("Optimizing ASR Models ...", section Chunked Prefill for Long Audio:
+ *                           4096-token pieces, each attending to everything before it and to
+ *                           itself causally)
+ *   mtd_attn_decode         one query token per request over that request's whole cache, for a
+ *                           batch of requests ("Optimizing ASR Models ...", section ASR Model
+ *                           Primer, Autoregressive Decode, and section Batched Inference)
+ *
+ * Everything computed is exact softmax attention:
+ *     s_j = scale * <q, k_j>  for visible keys j;  LSE = ln sum_j exp(s_j);  O = sum_j exp(s_j - LSE) v_j
+ * Query head h reads KV head h / (num_q_heads / num_kv_heads).
+ *
+ * ---------------------------------------------------------------------------------------------
+ * Conventions shared by every call
+ * ---------------------------------------------------------------------------------------------
+ * Memory.  Every pointer argument is a DEVICE pointer (memory of the GPU that is current on the
+ *   calling thread) unless the comment says "host".  The caller owns all memory; the library
+ *   allocates none and keeps no state other than a per-thread error string.
+ * Streams.  `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue work on it,
+ *   in order, and never synchronise the host.
+ * bf16.  bfloat16 values are 2-byte IEEE-754 binary32 upper halves.
+ * Page layout.  K and V live in separate pools, each
+ *       bf16 [num_pages][num_kv_heads][page_size][head_dim]   (row-major, contiguous),
+ *   so the rows of one (page, KV head) form one contiguous block of page_size*head_dim*2 bytes.
+ *   Logical token p of a request is stored at page block_table[p / page_size], slot p % page_size.
+ * Block tables.  int32 [n][bt_stride], row r lists request r's physical page ids in logical order.
+ *   Entries a call does not need are never read.
+ * Supported shape (this version).  num_q_heads = 16, num_kv_heads = 8, head_dim = 128,
+ *   page_size = 64; anything else returns MTD_ERR_UNSUPPORTED.
+ * Errors.  Every argument that lives on the host is checked before any work is enqueued; a failed
+ *   check returns a negative MTD_ERR_* code, enqueues nothing and leaves all memory untouched.
+ *   Values that live on the device (table entries, lengths, offsets) are trusted: if they are
+ *   inconsistent with the sizes given on the host the results are unspecified, but no kernel reads
+ *   or writes outside the pools, the inputs and the outputs (page ids outside [0, num_pages) are
+ *   skipped).  A failed kernel launch returns MTD_ERR_HIP; mtd_last_error() gives the detail.
+ */
+#ifndef MTD_H
+#define MTD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MTD_ABI_VERSION 1
+
+/* Status codes. */
+#define MTD_OK               0
+#define MTD_ERR_INVALID_ARG (-1) /* null pointer, negative or zero size where one is required     */
+#define MTD_ERR_UNSUPPORTED (-2) /* head count, head_dim or page size this version does not build */
+#define MTD_ERR_CAPACITY    (-3) /* tokens beyond the block-table capacity or the 128K context    */
+#define MTD_ERR_WORKSPACE   (-4) /* workspace missing or smaller than the required size           */
+#define MTD_ERR_HIP         (-5) /* the HIP runtime reported an error (see mtd_last_error)        */
+
+/* Longest KV a request may hold (128K context). */
+#define MTD_MAX_CONTEXT 131072
+
+/* One layer's paged KV cache.  The struct itself lives on the host; the pools on the device. */
+typedef struct mtd_kv_layer {
+  void*   k_pages;      /* device, bf16 [num_pages][num_kv_heads][page_size][head_dim]          */
+  void*   v_pages;      /* device, same layout                                                   */
+  int32_t num_pages;    /* > 0                                                                   */
+  int32_t page_size;    /* tokens per page: 64                                                   */
+  int32_t num_kv_heads; /* 8                                                                     */
+  int32_t head_dim;     /* 128                                                                   */
+} mtd_kv_layer_t;
+
+/*
+ * mtd_kv_append - store the K/V rows of new tokens in their pages.
+ *
+ * Prefill writes the prompt's keys and values into the KV cache and every decode step adds the
+ * new token's ("Optimizing ASR Models ...", section ASR Model Primer: "LLM Prefill" builds the KV
+ * cache, "Autoregressive Decode" extends it; cookbook section Inference Pipeline).
+ *
+ *   kv          host pointer to the layer's pools (pools are modified in place)
+ *   k_new       bf16 [n_new][num_kv_heads][head_dim], the new keys, requests back to back
+ *   v_new       bf16 [n_new][num_kv_heads][head_dim], the new values
+ *   cu_new      int32 [n_req + 1], cu_new[0] = 0, nondecreasing, cu_new[n_req] = n_new: request r
+ *               owns new rows cu_new[r] .. cu_new[r+1]-1
+ *   start_pos   int32 [n_req], logical position of request r's first new token
+ *   block_tables, bt_stride   int32 [n_req][bt_stride]; entry (start_pos[r] + i) / page_size of
+ *               row r must be valid for every new token i of request r
+ *   n_req       >= 1;  n_new >= 0 (0 enqueues nothing)
+ *
+ * Effect: for every new token t of request r at position p = start_pos[r] + (t - cu_new[r]) and
+ * every KV head g, the head_dim values of k_new[t][g] are copied bit for bit to
+ * k_pages[block_tables[r][p / page_size]][g][p % page_size], and likewise for V.  No other byte of
+ * the pools changes.  Positions at or beyond MTD_MAX_CONTEXT are skipped.
+ */
+int mtd_kv_append(const mtd_kv_layer_t* kv, const void* k_new, const void* v_new,
+                  const int32_t* cu_new, const int32_t* start_pos, const int32_t* block_tables,
+                  int32_t bt_stride, int32_t n_req, int32_t n_new, void* stream);
+
+/*
+ * mtd_attn_prefill_chunk - causal attention of one prefill chunk over the paged cache.
+ *
+ * Long prompts are prefilled in 4096-token chunks, one per scheduler step; each chunk attends to
+ * all keys before it and to itself causally ("Optimizing ASR Models ...", section Chunked Prefill
+ * for Long Audio; cookbook section Inference Pipeline).  A short prompt is one chunk with
+ * prefix_len = 0 (one-shot prefill).  The chunk's own K/V must already be in the pages
+ * (mtd_kv_append first, on the same stream).
+ *
+ *   q               bf16 [chunk_len][num_q_heads][head_dim], chunk query i is at absolute
+ *                   position prefix_len + i and sees keys 0 .. prefix_len + i
+ *   chunk_len       >= 1;  prefix_len >= 0;  prefix_len + chunk_len <= MTD_MAX_CONTEXT
+ *   block_table     int32 [block_table_len], the request's page ids in logical order
+ *   block_table_len host: capacity of block_table in entries; must be at least
+ *                   ceil((prefix_len + chunk_len) / page_size), else MTD_ERR_CAPACITY
+ *   num_q_heads     16;  scale > 0 and finite (1/sqrt(head_dim) for the Qwen3 decoder)
+ *   out             float32 [chunk_len][num_q_heads][head_dim], written
+ *   lse             float32 [chunk_len][num_q_heads], written: natural-log sum of exp(s_j)
+ */
+int mtd_attn_prefill_chunk(const mtd_kv_layer_t* kv, const void* q, int32_t chunk_len,
+                           int32_t prefix_len, const int32_t* block_table, int32_t block_table_len,
+                           int32_t num_q_heads, float scale, float* out, float* lse, void* stream);
+
+/*
+ * mtd_attn_decode_workspace_bytes - device workspace mtd_attn_decode needs for a batch whose
+ * longest request holds at most max_kv_len tokens.  Returns 0 for arguments mtd_attn_decode would
+ * reject.  The size grows with batch * ceil(max_kv_len / 512) (split-K partial results).
+ */
+size_t mtd_attn_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t max_kv_len,
+                                       int32_t head_dim);
+
+/*
+ * mtd_attn_decode - one query token per request against that request's whole KV.
+ *
+ * Autoregressive decode emits one token per request per step over the request's whole cache, with
+ * concurrent requests packed into one batch ("Optimizing ASR Models ...", sections ASR Model Primer
+ * and Batched Inference; cookbook section Inference Pipeline, step 3).  The token of this step must
+ * already be appended, and kv_lens counts it, so the query sits at position kv_lens[b] - 1 and sees
+ * all kv_lens[b] keys.
+ *
+ *   q               bf16 [batch][num_q_heads][head_dim]
+ *   kv_lens         int32 [batch], each in [1, max_kv_len]
+ *   block_tables, bt_stride   int32 [batch][bt_stride], bt_stride >= ceil(max_kv_len / page_size)
+ *                   (else MTD_ERR_CAPACITY)
+ *   batch           >= 1;  max_kv_len: host upper bound of kv_lens, 1 .. MTD_MAX_CONTEXT
+ *   num_q_heads     16;  scale > 0 and finite
+ *   workspace       device scratch of at least mtd_attn_decode_workspace_bytes(batch, num_q_heads,
+ *                   max_kv_len, head_dim) bytes, owned by the caller, contents ignored on entry and
+ *                   unspecified on return; calls on different streams need different workspaces
+ *   out             float32 [batch][num_q_heads][head_dim], written
+ *   lse             float32 [batch][num_q_heads], written (natural log)
+ *
+ * The result of request b depends only on its own query, length and pages: it is bitwise the same
+ * whatever the rest of the batch holds and wherever its pages sit in the pool.
+ */
+int mtd_attn_decode(const mtd_kv_layer_t* kv, const void* q, const int32_t* kv_lens,
+                    const int32_t* block_tables, int32_t bt_stride, int32_t batch,
+                    int32_t max_kv_len, int32_t num_q_heads, float scale, void* workspace,
+                    size_t workspace_bytes, float* out, float* lse, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* mtd_status_string(int status);
+
+/* Detail of the last failed call on the calling thread ("" if none).  Valid until the next call. */
+const char* mtd_last_error(void);
+
+/* MTD_ABI_VERSION of the built library. */
+int mtd_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MTD_H */

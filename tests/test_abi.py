@@ -1,0 +1,196 @@
+"""C-ABI library checks that need no GPU: the library loads, exports every declared symbol, binds
+to the one HIP runtime torch loaded, and rejects every invalid host-side argument with the
+documented status before anything is enqueued (so no kernel is ever launched here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mtd.h")
+
+mtd = pytest.importorskip("gqa_kv_cache_qwen3_amd")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(mtd.LIB_PATH):
+        pytest.skip("libmtd.so not built")
+    return mtd.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mtd_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_three_calls():
+    names = declared_functions()
+    for n in ("mtd_kv_append", "mtd_attn_prefill_chunk", "mtd_attn_decode",
+              "mtd_attn_decode_workspace_bytes", "mtd_status_string", "mtd_last_error",
+              "mtd_abi_version"):
+        assert n in names
+
+
+def test_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in mtd.h but not exported"
+
+
+def test_abi_version(lib):
+    text = open(HEADER).read()
+    want = int(re.search(r"#define MTD_ABI_VERSION (\d+)", text).group(1))
+    assert lib.mtd_abi_version() == want
+
+
+def test_single_hip_runtime(lib):
+    maps = open("/proc/self/maps").read().splitlines()
+    paths = {line.split()[-1] for line in maps if "libamdhip64" in line}
+    assert len(paths) == 1, paths
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4, -5):
+        s = lib.mtd_status_string(code).decode()
+        assert s and s != "unknown status"
+    assert lib.mtd_status_string(7).decode() == "unknown status"
+
+
+FAKE = 0x1000  # non-null placeholder; every call below fails validation before using it
+
+
+def layer(**kw):
+    base = dict(k_pages=FAKE, v_pages=FAKE, num_pages=10, page_size=64, num_kv_heads=8, head_dim=128)
+    base.update(kw)
+    return mtd.KvLayer(**base)
+
+
+def append(lib, kv, **kw):
+    a = dict(k_new=FAKE, v_new=FAKE, cu_new=FAKE, start_pos=FAKE, bt=FAKE, bt_stride=4, n_req=1, n_new=3)
+    a.update(kw)
+    return lib.mtd_kv_append(ctypes.byref(kv) if kv is not None else None, a["k_new"], a["v_new"],
+                             a["cu_new"], a["start_pos"], a["bt"], a["bt_stride"], a["n_req"],
+                             a["n_new"], None)
+
+
+def prefill(lib, kv, **kw):
+    a = dict(q=FAKE, chunk=10, prefix=0, bt=FAKE, bt_len=4, hq=16, scale=0.088, out=FAKE, lse=FAKE)
+    a.update(kw)
+    return lib.mtd_attn_prefill_chunk(ctypes.byref(kv) if kv is not None else None, a["q"],
+                                      a["chunk"], a["prefix"], a["bt"], a["bt_len"], a["hq"],
+                                      a["scale"], a["out"], a["lse"], None)
+
+
+def decode(lib, kv, **kw):
+    a = dict(q=FAKE, lens=FAKE, bt=FAKE, stride=16, batch=2, max_len=1000, hq=16, scale=0.088,
+             ws=FAKE, ws_bytes=None, out=FAKE, lse=FAKE)
+    a.update(kw)
+    if a["ws_bytes"] is None:
+        a["ws_bytes"] = lib.mtd_attn_decode_workspace_bytes(max(a["batch"], 1), 16, max(min(a["max_len"], 131072), 1), 128)
+    return lib.mtd_attn_decode(ctypes.byref(kv) if kv is not None else None, a["q"], a["lens"],
+                               a["bt"], a["stride"], a["batch"], a["max_len"], a["hq"], a["scale"],
+                               a["ws"], a["ws_bytes"], a["out"], a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k_pages=None), mtd.MTD_ERR_INVALID_ARG),
+    (dict(v_pages=None), mtd.MTD_ERR_INVALID_ARG),
+    (dict(num_pages=0), mtd.MTD_ERR_INVALID_ARG),
+    (dict(page_size=32), mtd.MTD_ERR_UNSUPPORTED),
+    (dict(num_kv_heads=4), mtd.MTD_ERR_UNSUPPORTED),
+    (dict(head_dim=64), mtd.MTD_ERR_UNSUPPORTED),
+])
+def test_layer_validation(lib, kw, code):
+    kv = layer(**kw)
+    assert append(lib, kv) == code
+    assert prefill(lib, kv) == code
+    assert decode(lib, kv) == code
+    assert lib.mtd_last_error().decode() != ""
+
+
+def test_null_layer(lib):
+    assert append(lib, None) == mtd.MTD_ERR_INVALID_ARG
+    assert prefill(lib, None) == mtd.MTD_ERR_INVALID_ARG
+    assert decode(lib, None) == mtd.MTD_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_req=0), mtd.MTD_ERR_INVALID_ARG),
+    (dict(n_new=-1), mtd.MTD_ERR_INVALID_ARG),
+    (dict(bt_stride=0), mtd.MTD_ERR_INVALID_ARG),
+    (dict(k_new=None), mtd.MTD_ERR_INVALID_ARG),
+    (dict(v_new=None), mtd.MTD_ERR_INVALID_ARG),
+    (dict(cu_new=None), mtd.MTD_ERR_INVALID_ARG),
+    (dict(start_pos=None), mtd.MTD_ERR_INVALID_ARG),
+    (dict(bt=None), mtd.MTD_ERR_INVALID_ARG),
+])
+def test_append_validation(lib, kw, code):
+    assert append(lib, layer(), **kw) == code
+
+
+def test_append_empty_is_noop(lib):
+    # n_new = 0 enqueues nothing (and needs no k_new / v_new)
+    assert append(lib, layer(), n_new=0, k_new=None, v_new=None) == mtd.MTD_OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(hq=0), mtd.MTD_ERR_INVALID_ARG),
+    (dict(hq=12), mtd.MTD_ERR_UNSUPPORTED),
+    (dict(hq=32), mtd.MTD_ERR_UNSUPPORTED),
+    (dict(scale=0.0), mtd.MTD_ERR_INVALID_ARG),
+    (dict(scale=-1.0), mtd.MTD_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), mtd.MTD_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), mtd.MTD_ERR_INVALID_ARG),
+    (dict(q=None), mtd.MTD_ERR_INVALID_ARG),
+    (dict(bt=None), mtd.MTD_ERR_INVALID_ARG),
+    (dict(out=None), mtd.MTD_ERR_INVALID_ARG),
+    (dict(lse=None), mtd.MTD_ERR_INVALID_ARG),
+    (dict(chunk=0), mtd.MTD_ERR_INVALID_ARG),
+    (dict(prefix=-1), mtd.MTD_ERR_INVALID_ARG),
+    (dict(prefix=131072 - 9, chunk=10, bt_len=2048), mtd.MTD_ERR_CAPACITY),
+    (dict(prefix=200, chunk=57, bt_len=4), mtd.MTD_ERR_CAPACITY),   # 257 tokens need 5 pages
+])
+def test_prefill_validation(lib, kw, code):
+    assert prefill(lib, layer(), **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(hq=8), mtd.MTD_ERR_UNSUPPORTED),
+    (dict(scale=float("nan")), mtd.MTD_ERR_INVALID_ARG),
+    (dict(q=None), mtd.MTD_ERR_INVALID_ARG),
+    (dict(lens=None), mtd.MTD_ERR_INVALID_ARG),
+    (dict(bt=None), mtd.MTD_ERR_INVALID_ARG),
+    (dict(out=None), mtd.MTD_ERR_INVALID_ARG),
+    (dict(lse=None), mtd.MTD_ERR_INVALID_ARG),
+    (dict(batch=0), mtd.MTD_ERR_INVALID_ARG),
+    (dict(max_len=0), mtd.MTD_ERR_INVALID_ARG),
+    (dict(max_len=131073, stride=4096), mtd.MTD_ERR_CAPACITY),
+    (dict(max_len=1025, stride=16), mtd.MTD_ERR_CAPACITY),           # 1025 tokens need 17 pages
+    (dict(ws=None), mtd.MTD_ERR_WORKSPACE),
+    (dict(ws_bytes=100), mtd.MTD_ERR_WORKSPACE),
+])
+def test_decode_validation(lib, kw, code):
+    assert decode(lib, layer(), **kw) == code
+
+
+def test_workspace_size_formula(lib):
+    # partials: batch * ceil(max_kv_len / 512) splits, each 16 heads x (128 + 1) floats
+    for batch, max_len in [(1, 1), (1, 512), (1, 513), (16, 30000), (64, 131072)]:
+        parts = batch * ((max_len + 511) // 512)
+        assert lib.mtd_attn_decode_workspace_bytes(batch, 16, max_len, 128) == parts * 16 * 129 * 4
+    assert lib.mtd_attn_decode_workspace_bytes(0, 16, 100, 128) == 0
+    assert lib.mtd_attn_decode_workspace_bytes(1, 16, 0, 128) == 0
+    assert lib.mtd_attn_decode_workspace_bytes(1, 16, 131073, 128) == 0
+    assert lib.mtd_attn_decode_workspace_bytes(1, 8, 100, 128) == 0
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    cpu = torch.zeros((2, 8, 64, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        mtd.kv_layer(cpu, cpu)
+    with pytest.raises(TypeError):
+        mtd.kv_layer(cpu.float(), cpu.float())

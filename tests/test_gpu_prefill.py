@@ -1,0 +1,175 @@
+"""mtd_attn_prefill_chunk on the GPU against the fp64 oracle: one-shot and chunked prefill over
+pages written by mtd_kv_append, at small ragged shapes in full and at the 90-minute and
+mixed-step sizes on sampled rows; plus chunked == one-shot and decode == 1-row prefill."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_common import bits, compare, log, new_pool, request_pages_host
+
+pytestmark = pytest.mark.gpu
+
+mtd = pytest.importorskip("gqa_kv_cache_qwen3_amd")
+
+
+class Request:
+    """One request's paged KV, filled through mtd_kv_append (the path under test)."""
+
+    def __init__(self, total: int, tag: int, lowrank: bool = False, spare: int = 2):
+        self.total = total
+        tables, self.num_pages, self.spare = W.place_pages([total], tag, 0, spare=spare)
+        self.table_np = tables[0]
+        self.table = torch.as_tensor(self.table_np, device="cuda")
+        self.k = new_pool(self.num_pages, "cuda")
+        self.v = new_pool(self.num_pages, "cuda")
+        if lowrank:
+            self.k_log = W.lowrank_keys(total, W.torch_seed(tag, 1), "cuda")
+        else:
+            self.k_log = W.normal_bf16((total, W.HKV, W.HEAD_DIM), W.torch_seed(tag, 1), "cuda")
+        self.v_log = W.normal_bf16((total, W.HKV, W.HEAD_DIM), W.torch_seed(tag, 2), "cuda")
+        self.q_log = W.normal_bf16((total, W.HQ, W.HEAD_DIM), W.torch_seed(tag, 3), "cuda")
+        self.filled = 0
+
+    def append_to(self, end: int):
+        start = self.filled
+        if end <= start:
+            return
+        mtd.mtd_kv_append(self.k, self.v, self.k_log[start:end].contiguous(),
+                          self.v_log[start:end].contiguous(),
+                          torch.tensor([0, end - start], dtype=torch.int32, device="cuda"),
+                          torch.tensor([start], dtype=torch.int32, device="cuda"),
+                          self.table[None, :].contiguous())
+        self.filled = end
+
+    def prefill(self, prefix: int, chunk: int):
+        self.append_to(prefix + chunk)
+        out, lse = mtd.mtd_attn_prefill_chunk(self.k, self.v, self.q_log[prefix:prefix + chunk].contiguous(),
+                                              prefix, self.table, W.SCALE)
+        torch.cuda.synchronize()
+        return out, lse
+
+    def reference(self, prefix: int, chunk: int, rows=None):
+        """Oracle over the request's pages as they sit on the device (rows: chunk-local indices)."""
+        kc, vc, ident = request_pages_host(self.k, self.v, self.table_np, prefix + chunk)
+        q = bits(self.q_log[prefix:prefix + chunk])
+        if rows is None:
+            return oracle.prefill_chunk(q, kc, vc, ident, prefix, W.SCALE)
+        rows = np.asarray(rows)
+        k = oracle.gather_logical(kc, ident, prefix + chunk)
+        v = oracle.gather_logical(vc, ident, prefix + chunk)
+        return oracle.attention(oracle.bf16_to_f64(q[rows]), k, v, prefix + rows, W.SCALE)
+
+
+@pytest.mark.parametrize("prefix,chunk", [(0, 1), (0, 64), (0, 65), (5, 1), (63, 2), (100, 37),
+                                          (64, 64), (1000, 300), (0, 439), (4096, 4096)])
+def test_prefill_small_full_compare(prefix, chunk):
+    log(f"prefill prefix={prefix} chunk={chunk}")
+    req = Request(prefix + chunk, 200 + prefix + 7 * chunk)
+    out, lse = req.prefill(prefix, chunk)
+    o_ref, l_ref = req.reference(prefix, chunk)
+    compare(out, lse, o_ref, l_ref, f"prefill P={prefix} C={chunk}")
+
+
+def test_tiny_one_shot_then_decode_steps():
+    """30 s of audio + 64 prompt tokens: one-shot 439-token prefill, then 32 decode steps, each
+    appending its token first; every step against the oracle."""
+    prompt, steps = W.TINY.params["prompt"], W.TINY.params["decode_steps"]
+    req = Request(prompt + steps, W.TINY.tag)
+    log("tiny one-shot prefill")
+    out, lse = req.prefill(0, prompt)
+    o_ref, l_ref = req.reference(0, prompt)
+    compare(out, lse, o_ref, l_ref, "tiny one-shot")
+    for s in range(steps):
+        n = prompt + s + 1
+        req.append_to(n)
+        q = req.q_log[n - 1:n].contiguous()
+        log(f"tiny decode step {s}")
+        o, l = mtd.mtd_attn_decode(req.k, req.v, q, torch.tensor([n], dtype=torch.int32, device="cuda"),
+                                   req.table[None, :].contiguous(), n, W.SCALE)
+        torch.cuda.synchronize()
+        kc, vc, ident = request_pages_host(req.k, req.v, req.table_np, n)
+        o_ref, l_ref = oracle.decode(bits(q), kc, vc, [n], [ident], W.SCALE)
+        compare(o, l, o_ref, l_ref, f"tiny decode step {s}")
+
+
+def test_gpu_chunked_matches_gpu_one_shot():
+    """The tiny prompt as chunks of 128 + 128 + 128 + 55 against one 439-token call."""
+    req = Request(439, 301)
+    one_o, one_l = req.prefill(0, 439)
+    parts_o, parts_l = [], []
+    for start, c in [(0, 128), (128, 128), (256, 128), (384, 55)]:
+        o, l = req.prefill(start, c)
+        parts_o.append(o)
+        parts_l.append(l)
+    o = torch.cat(parts_o)
+    l = torch.cat(parts_l)
+    assert float((o - one_o).abs().max()) <= 1e-2 * 0.1
+    assert float((l - one_l).abs().max()) <= 1e-3 * 0.1
+
+
+def test_decode_equals_one_row_prefill():
+    req = Request(3000, 302)
+    o_p, l_p = req.prefill(2999, 1)
+    q = req.q_log[2999:3000].contiguous()
+    o_d, l_d = mtd.mtd_attn_decode(req.k, req.v, q, torch.tensor([3000], dtype=torch.int32, device="cuda"),
+                                   req.table[None, :].contiguous(), 3000, W.SCALE)
+    torch.cuda.synchronize()
+    assert float((o_p - o_d).abs().max()) <= 1e-3
+    assert float((l_p - l_d).abs().max()) <= 1e-4
+
+
+def sample_rows(chunk: int, tag: int, n: int = 40) -> np.ndarray:
+    """First, last, a few around the 64-row tile edges, and seeded random rows."""
+    fixed = [0, 1, 15, 16, 63, 64, chunk // 2, chunk - 2, chunk - 1]
+    rnd = W.rng(9, tag).choice(chunk, size=min(n, chunk), replace=False).tolist()
+    return np.array(sorted({r for r in fixed + rnd if 0 <= r < chunk}))
+
+
+def test_prefill_90_minutes_chunked_sampled():
+    """67,500 tokens in 17 chunks of 4096 (last 1,964), K with a rank-4 per-head component so the
+    softmax is peaked; every chunk is checked on sampled rows against the oracle."""
+    p = W.PREFILL90.params
+    total, chunk = p["total"], p["chunk"]
+    req = Request(total, W.PREFILL90.tag, lowrank=True)
+    req.append_to(total)
+    torch.cuda.synchronize()
+    kc, vc, ident = request_pages_host(req.k, req.v, req.table_np, total)
+    k = oracle.gather_logical(kc, ident, total)
+    v = oracle.gather_logical(vc, ident, total)
+    qb = bits(req.q_log)
+    for ci, start in enumerate(range(0, total, chunk)):
+        c = min(chunk, total - start)
+        log(f"prefill90 chunk {ci} prefix={start} len={c}")
+        out, lse = req.prefill(start, c)
+        rows = sample_rows(c, ci)
+        o_ref, l_ref = oracle.attention(oracle.bf16_to_f64(qb[start + rows]), k, v, start + rows, W.SCALE)
+        compare(out[rows], lse[rows], o_ref, l_ref, f"prefill90 chunk {ci}")
+
+
+def test_mixed_step_prefill_part_sampled():
+    """The mixed step's chunk: 4096 tokens of request A at prefix 32,768."""
+    p = W.MIXED.params
+    prefix, chunk = p["prefix"], p["chunk"]
+    req = Request(prefix + chunk, W.MIXED.tag)
+    log("mixed prefill part")
+    out, lse = req.prefill(prefix, chunk)
+    rows = sample_rows(chunk, 99, 64)
+    o_ref, l_ref = req.reference(prefix, chunk, rows)
+    compare(out[rows], lse[rows], o_ref, l_ref, "mixed prefill part")
+
+
+def test_prefill_deterministic_and_placement_invariant():
+    a = Request(5000, 303)
+    o1, l1 = a.prefill(1000, 4000)
+    o2, l2 = a.prefill(1000, 4000)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    # same logical data, different page placement
+    b = Request(5000, 303)
+    tables, _, _ = W.place_pages([5000], 304, 0, spare=2)
+    b.table_np = tables[0]
+    b.table = torch.as_tensor(b.table_np, device="cuda")
+    o3, l3 = b.prefill(1000, 4000)
+    assert torch.equal(o1, o3) and torch.equal(l1, l3)
