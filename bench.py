@@ -1,0 +1,453 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged GQA attention path on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input.  The default workload
+is the mixed scheduler step: one 4096-token prefill chunk of request A at prefix 32,768 plus one
+decode token for each of 31 other requests (KV lengths log-uniform in [2000, 68000]), all in one
+shared pool of 64-token pages.  Per step:
+    mtd_kv_append           4096 chunk tokens of A + 31 decode tokens, one call
+    mtd_attn_prefill_chunk  A's chunk over its 36,864 keys
+    mtd_attn_decode         31 requests (split-K + merge)
+Other workloads (--workload): decode16 (16 requests, L in [27000, 30000]), prefill90min (17 chunks
+of a 67,500-token request), fulldepth_decode (28 layers x 64 requests, 128K cap).
+
+Prints one JSON line.  `value` is decode-attention HBM throughput (algorithmic bytes / time) and
+`prefill` carries the chunked-prefill TFLOP/s; `roofline` is for the kernel that takes the most
+time in the step, timed with HIP events on the stream the library launches on.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+METRIC = "decode-attn HBM GB/s + chunked-prefill TFLOP/s on 1 MI355X, % of roofline"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+
+# Algorithmic byte / flop counts (per call).
+KV_BYTES_PER_TOKEN = 2 * W.HKV * W.HEAD_DIM * 2          # K + V, all KV heads, bf16
+Q_BYTES = W.HQ * W.HEAD_DIM * 2                          # one query token, all heads
+OUT_BYTES = W.HQ * W.HEAD_DIM * 4 + W.HQ * 4              # fp32 O + LSE per query token
+
+
+def decode_bytes(lens) -> int:
+    lens = np.asarray(lens, dtype=np.int64)
+    table = 4 * ((lens + W.PAGE - 1) // W.PAGE)
+    return int((KV_BYTES_PER_TOKEN * lens + Q_BYTES + OUT_BYTES + table + 4).sum())
+
+
+def prefill_flops(prefix: int, chunk: int) -> float:
+    """4 * Hq * d flops per attended (query, key) pair; causal pairs only."""
+    pairs = chunk * prefix + chunk * (chunk + 1) / 2
+    return 4.0 * W.HQ * W.HEAD_DIM * pairs
+
+
+def fill_normal_(t, seed, slab=1 << 28):
+    import torch
+    gen = torch.Generator(device=t.device)
+    gen.manual_seed(seed)
+    flat = t.view(-1)
+    for lo in range(0, flat.numel(), slab):
+        hi = min(lo + slab, flat.numel())
+        flat[lo:hi] = torch.randn(hi - lo, generator=gen, device=t.device, dtype=torch.float32).to(torch.bfloat16)
+    return t
+
+
+class Timer:
+    """HIP events recorded on the library's stream (torch's current stream)."""
+
+    def __init__(self, names):
+        import torch
+        self.torch = torch
+        self.names = names
+        self.samples = {n: [] for n in names}
+
+    def step_events(self):
+        return [self.torch.cuda.Event(enable_timing=True) for _ in range(len(self.names) + 1)]
+
+    def collect(self, events):
+        for i, n in enumerate(self.names):
+            self.samples[n].append(events[i].elapsed_time(events[i + 1]))
+
+    def mean_ms(self, name):
+        return float(np.mean(self.samples[name]))
+
+
+# --------------------------------------------------------------------------------------------
+# mixed scheduler step
+# --------------------------------------------------------------------------------------------
+
+class MixedStep:
+    name = "mixed_step"
+
+    def __init__(self, dev):
+        import torch
+        import gqa_kv_cache_qwen3_amd as mtd
+        self.mtd, self.torch = mtd, torch
+        p = W.MIXED.params
+        self.prefix, self.chunk = p["prefix"], p["chunk"]
+        self.lens = W.loguniform_lengths(p["batch"], p["lo"], p["hi"], W.MIXED.tag, 0)
+        final = np.concatenate([[self.prefix + self.chunk], self.lens])
+        tables, n_pages, _ = W.place_pages(final, W.MIXED.tag, 0)
+        self.n_pages = n_pages
+        self.k = torch.empty((n_pages, W.HKV, W.PAGE, W.HEAD_DIM), dtype=torch.bfloat16, device=dev)
+        self.v = torch.empty_like(self.k)
+        fill_normal_(self.k, W.torch_seed(W.MIXED.tag, 1))
+        fill_normal_(self.v, W.torch_seed(W.MIXED.tag, 2))
+        self.bt_all = torch.as_tensor(tables, device=dev)
+        self.bt_a = self.bt_all[0].contiguous()
+        self.bt_dec = self.bt_all[1:].contiguous()
+        n_new = self.chunk + len(self.lens)
+        self.k_new = torch.empty((n_new, W.HKV, W.HEAD_DIM), dtype=torch.bfloat16, device=dev)
+        self.v_new = torch.empty_like(self.k_new)
+        fill_normal_(self.k_new, W.torch_seed(W.MIXED.tag, 3))
+        fill_normal_(self.v_new, W.torch_seed(W.MIXED.tag, 4))
+        cu = np.concatenate([[0, self.chunk], self.chunk + np.arange(1, len(self.lens) + 1)]).astype(np.int32)
+        start = np.concatenate([[self.prefix], self.lens - 1]).astype(np.int32)
+        self.cu = torch.as_tensor(cu, device=dev)
+        self.start = torch.as_tensor(start, device=dev)
+        self.q_a = torch.empty((self.chunk, W.HQ, W.HEAD_DIM), dtype=torch.bfloat16, device=dev)
+        self.q_d = torch.empty((len(self.lens), W.HQ, W.HEAD_DIM), dtype=torch.bfloat16, device=dev)
+        fill_normal_(self.q_a, W.torch_seed(W.MIXED.tag, 5))
+        fill_normal_(self.q_d, W.torch_seed(W.MIXED.tag, 6))
+        self.kv_lens = torch.as_tensor(self.lens.astype(np.int32), device=dev)
+        self.max_len = int(self.lens.max())
+        self.ws = torch.empty(mtd.decode_workspace_bytes(len(self.lens), self.max_len), dtype=torch.uint8, device=dev)
+        self.o_a = torch.empty((self.chunk, W.HQ, W.HEAD_DIM), dtype=torch.float32, device=dev)
+        self.l_a = torch.empty((self.chunk, W.HQ), dtype=torch.float32, device=dev)
+        self.o_d = torch.empty((len(self.lens), W.HQ, W.HEAD_DIM), dtype=torch.float32, device=dev)
+        self.l_d = torch.empty((len(self.lens), W.HQ), dtype=torch.float32, device=dev)
+        self.timer = Timer(["append", "prefill", "decode"])
+        self.work = {
+            "append_bytes": 2 * n_new * W.HKV * W.HEAD_DIM * 2 * 2,
+            "prefill_flops": prefill_flops(self.prefix, self.chunk),
+            "decode_bytes": decode_bytes(self.lens),
+        }
+
+    def step(self, events=None):
+        mtd = self.mtd
+        if events: events[0].record()
+        mtd.mtd_kv_append(self.k, self.v, self.k_new, self.v_new, self.cu, self.start, self.bt_all)
+        if events: events[1].record()
+        mtd.mtd_attn_prefill_chunk(self.k, self.v, self.q_a, self.prefix, self.bt_a, W.SCALE, self.o_a, self.l_a)
+        if events: events[2].record()
+        mtd.mtd_attn_decode(self.k, self.v, self.q_d, self.kv_lens, self.bt_dec, self.max_len, W.SCALE,
+                            self.ws, self.o_d, self.l_d)
+        if events: events[3].record()
+
+    def config(self):
+        return {"workload": "mixed_step: one 4096-token prefill chunk at prefix 32768 + decode of 31 requests "
+                            "(KV lengths log-uniform in [2000, 68000]), shared pool of 64-token pages",
+                "num_q_heads": W.HQ, "num_kv_heads": W.HKV, "head_dim": W.HEAD_DIM, "page_size": W.PAGE,
+                "chunk": self.chunk, "prefix": self.prefix, "decode_batch": len(self.lens),
+                "decode_kv_tokens": int(self.lens.sum()), "pool_pages": self.n_pages}
+
+    def results(self):
+        t = self.timer
+        dec_ms, pre_ms, app_ms = t.mean_ms("decode"), t.mean_ms("prefill"), t.mean_ms("append")
+        dec_gbs = self.work["decode_bytes"] / (dec_ms * 1e-3) / 1e9
+        pre_tfs = self.work["prefill_flops"] / (pre_ms * 1e-3) / 1e12
+        return {
+            "decode": {"value": dec_gbs, "unit": "GB/s", "frac": dec_gbs / HBM_PEAK_GBS, "ms": dec_ms,
+                       "bytes": self.work["decode_bytes"], "kernels": "decode_split_kernel + decode_merge_kernel"},
+            "prefill": {"value": pre_tfs, "unit": "TFLOP/s", "frac": pre_tfs / MFMA_BF16_PEAK_TFLOPS, "ms": pre_ms,
+                        "flops": self.work["prefill_flops"], "kernels": "prefill_kernel"},
+            "append": {"ms": app_ms, "bytes": self.work["append_bytes"], "kernels": "kv_append_kernel"},
+        }
+
+    def dominant(self, res):
+        if res["prefill"]["ms"] >= res["decode"]["ms"]:
+            return {"kernel": "prefill_kernel", "bound": "mfma", "achieved": res["prefill"]["value"],
+                    "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "per_launch": res["prefill"]["flops"],
+                    "ms": res["prefill"]["ms"]}
+        return {"kernel": "decode_split_kernel+decode_merge_kernel", "bound": "hbm", "achieved": res["decode"]["value"],
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "per_launch": res["decode"]["bytes"], "ms": res["decode"]["ms"]}
+
+    # ---- CPU baseline: the fp64 oracle on a bounded sample of the same step ----
+    def cpu_baseline(self, budget_s=20.0):
+        import torch
+        import oracle
+        rows_total = 0
+        t_pre = t_dec = 0.0
+        pre_flops = dec_bytes = 0.0
+        torch.cuda.synchronize()
+        host = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+        def pages_of(table_row, n):
+            used = (n + W.PAGE - 1) // W.PAGE
+            idx = torch.as_tensor(np.asarray(table_row[:used].cpu().numpy(), dtype=np.int64), device=self.k.device)
+            return host(self.k.index_select(0, idx)), host(self.v.index_select(0, idx)), np.arange(used)
+
+        # decode sample: requests in seeded order until half the budget is used
+        order = W.rng(4, 77).permutation(len(self.lens))
+        qd = host(self.q_d)
+        n_dec = 0
+        for b in order:
+            n = int(self.lens[b])
+            kc, vc, ident = pages_of(self.bt_dec[b], n)
+            t0 = time.perf_counter()
+            oracle.decode(qd[b:b + 1], kc, vc, [n], [ident], W.SCALE)
+            t_dec += time.perf_counter() - t0
+            dec_bytes += KV_BYTES_PER_TOKEN * n
+            n_dec += 1
+            if t_dec > budget_s / 2:
+                break
+        # prefill sample: blocks of 64 chunk rows, seeded order
+        total = self.prefix + self.chunk
+        kc, vc, ident = pages_of(self.bt_a, total)
+        qa = host(self.q_a)
+        blocks = W.rng(4, 78).permutation(self.chunk // 64)
+        for blk in blocks:
+            rows = np.arange(64 * blk, 64 * blk + 64)
+            t0 = time.perf_counter()
+            k = oracle.gather_logical(kc, ident, int(self.prefix + rows.max() + 1))
+            v = oracle.gather_logical(vc, ident, int(self.prefix + rows.max() + 1))
+            oracle.attention(oracle.bf16_to_f64(qa[rows]), k, v, self.prefix + rows, W.SCALE)
+            t_pre += time.perf_counter() - t0
+            pre_flops += 4.0 * W.HQ * W.HEAD_DIM * float((self.prefix + rows + 1).sum())
+            rows_total += 64
+            if t_pre > budget_s / 2:
+                break
+        return {
+            "value": dec_bytes / t_dec / 1e9, "unit": "GB/s",
+            "prefill_tflops": pre_flops / t_pre / 1e12,
+            "cores": blas_threads(), "kind": "oracle",
+            "sample": f"decode of {n_dec} of the 31 requests ({int(dec_bytes / KV_BYTES_PER_TOKEN)} KV tokens, "
+                      f"{t_dec:.1f} s) + {rows_total} of the 4096 prefill rows ({t_pre:.1f} s); fp64 numpy",
+        }
+
+
+# --------------------------------------------------------------------------------------------
+# decode16 and prefill90min as standalone steps (secondary workloads)
+# --------------------------------------------------------------------------------------------
+
+class Decode16:
+    name = "decode16"
+
+    def __init__(self, dev):
+        import torch
+        import gqa_kv_cache_qwen3_amd as mtd
+        self.mtd = mtd
+        p = W.DECODE16.params
+        self.lens = W.uniform_lengths(p["batch"], p["lo"], p["hi"], W.DECODE16.tag, 0)
+        tables, n_pages, _ = W.place_pages(self.lens, W.DECODE16.tag, 0)
+        self.k = torch.empty((n_pages, W.HKV, W.PAGE, W.HEAD_DIM), dtype=torch.bfloat16, device=dev)
+        self.v = torch.empty_like(self.k)
+        fill_normal_(self.k, W.torch_seed(W.DECODE16.tag, 1))
+        fill_normal_(self.v, W.torch_seed(W.DECODE16.tag, 2))
+        b = len(self.lens)
+        self.bt = torch.as_tensor(tables, device=dev)
+        self.q = torch.empty((b, W.HQ, W.HEAD_DIM), dtype=torch.bfloat16, device=dev)
+        fill_normal_(self.q, W.torch_seed(W.DECODE16.tag, 3))
+        self.k_new = torch.empty((b, W.HKV, W.HEAD_DIM), dtype=torch.bfloat16, device=dev)
+        self.v_new = torch.empty_like(self.k_new)
+        fill_normal_(self.k_new, 5)
+        fill_normal_(self.v_new, 6)
+        self.cu = torch.arange(b + 1, dtype=torch.int32, device=dev)
+        self.start = torch.as_tensor((self.lens - 1).astype(np.int32), device=dev)
+        self.kv_lens = torch.as_tensor(self.lens.astype(np.int32), device=dev)
+        self.max_len = int(self.lens.max())
+        self.ws = torch.empty(mtd.decode_workspace_bytes(b, self.max_len), dtype=torch.uint8, device=dev)
+        self.o = torch.empty((b, W.HQ, W.HEAD_DIM), dtype=torch.float32, device=dev)
+        self.l = torch.empty((b, W.HQ), dtype=torch.float32, device=dev)
+        self.timer = Timer(["append", "decode"])
+        self.bytes = decode_bytes(self.lens)
+
+    def step(self, events=None):
+        mtd = self.mtd
+        if events: events[0].record()
+        mtd.mtd_kv_append(self.k, self.v, self.k_new, self.v_new, self.cu, self.start, self.bt)
+        if events: events[1].record()
+        mtd.mtd_attn_decode(self.k, self.v, self.q, self.kv_lens, self.bt, self.max_len, W.SCALE, self.ws, self.o, self.l)
+        if events: events[2].record()
+
+    def config(self):
+        return {"workload": "decode16: batched decode of 16 requests, KV lengths uniform in [27000, 30000]",
+                "decode_kv_tokens": int(self.lens.sum())}
+
+    def results(self):
+        ms = self.timer.mean_ms("decode")
+        gbs = self.bytes / (ms * 1e-3) / 1e9
+        return {"decode": {"value": gbs, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "ms": ms, "bytes": self.bytes},
+                "append": {"ms": self.timer.mean_ms("append")}}
+
+    def dominant(self, res):
+        return {"kernel": "decode_split_kernel+decode_merge_kernel", "bound": "hbm", "achieved": res["decode"]["value"],
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "per_launch": self.bytes, "ms": res["decode"]["ms"]}
+
+
+class Prefill90:
+    name = "prefill90min"
+
+    def __init__(self, dev):
+        import torch
+        import gqa_kv_cache_qwen3_amd as mtd
+        self.mtd = mtd
+        p = W.PREFILL90.params
+        self.total, self.chunk = p["total"], p["chunk"]
+        tables, n_pages, _ = W.place_pages([self.total], W.PREFILL90.tag, 0)
+        self.k = torch.zeros((n_pages, W.HKV, W.PAGE, W.HEAD_DIM), dtype=torch.bfloat16, device=dev)
+        self.v = torch.zeros_like(self.k)
+        self.bt = torch.as_tensor(tables, device=dev)
+        self.k_log = W.lowrank_keys(self.total, W.torch_seed(W.PREFILL90.tag, 1), dev)
+        self.v_log = torch.empty((self.total, W.HKV, W.HEAD_DIM), dtype=torch.bfloat16, device=dev)
+        fill_normal_(self.v_log, W.torch_seed(W.PREFILL90.tag, 2))
+        self.q = torch.empty((self.total, W.HQ, W.HEAD_DIM), dtype=torch.bfloat16, device=dev)
+        fill_normal_(self.q, W.torch_seed(W.PREFILL90.tag, 3))
+        self.o = torch.empty((self.chunk, W.HQ, W.HEAD_DIM), dtype=torch.float32, device=dev)
+        self.l = torch.empty((self.chunk, W.HQ), dtype=torch.float32, device=dev)
+        self.chunks = [(s, min(self.chunk, self.total - s)) for s in range(0, self.total, self.chunk)]
+        self.cu = [torch.tensor([0, c], dtype=torch.int32, device=dev) for _, c in self.chunks]
+        self.st = [torch.tensor([s], dtype=torch.int32, device=dev) for s, _ in self.chunks]
+        self.timer = Timer(["append", "prefill"])
+        self.flops = sum(prefill_flops(s, c) for s, c in self.chunks)
+
+    def step(self, events=None):
+        mtd = self.mtd
+        for i, (s, c) in enumerate(self.chunks):
+            mtd.mtd_kv_append(self.k, self.v, self.k_log[s:s + c], self.v_log[s:s + c], self.cu[i], self.st[i], self.bt)
+            mtd.mtd_attn_prefill_chunk(self.k, self.v, self.q[s:s + c], s, self.bt[0], W.SCALE, self.o[:c], self.l[:c])
+
+    def timed_step(self):
+        """Per-chunk events (append and prefill separately)."""
+        import torch
+        mtd = self.mtd
+        evs = []
+        for i, (s, c) in enumerate(self.chunks):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record()
+            mtd.mtd_kv_append(self.k, self.v, self.k_log[s:s + c], self.v_log[s:s + c], self.cu[i], self.st[i], self.bt)
+            e[1].record()
+            mtd.mtd_attn_prefill_chunk(self.k, self.v, self.q[s:s + c], s, self.bt[0], W.SCALE, self.o[:c], self.l[:c])
+            e[2].record()
+            evs.append(e)
+        return evs
+
+    def config(self):
+        return {"workload": "prefill90min: 67,500-token request as 17 chunks of 4096 (last 1,964), K with a rank-4 "
+                            "per-head component", "flops_causal": self.flops}
+
+    def results(self):
+        ms = self.timer.mean_ms("prefill")
+        tfs = self.flops / (ms * 1e-3) / 1e12
+        return {"prefill": {"value": tfs, "unit": "TFLOP/s", "frac": tfs / MFMA_BF16_PEAK_TFLOPS, "ms": ms, "flops": self.flops},
+                "append": {"ms": self.timer.mean_ms("append")}}
+
+    def dominant(self, res):
+        return {"kernel": "prefill_kernel", "bound": "mfma", "achieved": res["prefill"]["value"],
+                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "per_launch": self.flops / len(self.chunks),
+                "ms": res["prefill"]["ms"] / len(self.chunks)}
+
+
+WORKLOAD_CLASSES = {c.name: c for c in (MixedStep, Decode16, Prefill90)}
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"]
+        return int(max(n)) if n else 1
+    except Exception:
+        return 1
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="mixed_step", choices=sorted(WORKLOAD_CLASSES))
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing on the host")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for cpu_baseline")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
+              "(multi-GPU sharding is a design note only)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gqa_kv_cache_qwen3_amd as mtd
+    mtd.lib()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    wl = WORKLOAD_CLASSES[args.workload](dev)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        wl.step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps between synchronisations; per-call events inside
+    t0 = time.perf_counter()
+    if isinstance(wl, Prefill90):
+        all_evs = []
+        for _ in range(args.steps):
+            all_evs.append(wl.timed_step())
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        for evs in all_evs:
+            app = sum(e[0].elapsed_time(e[1]) for e in evs)
+            pre = sum(e[1].elapsed_time(e[2]) for e in evs)
+            wl.timer.samples["append"].append(app)
+            wl.timer.samples["prefill"].append(pre)
+    else:
+        all_evs = []
+        for _ in range(args.steps):
+            evs = wl.timer.step_events()
+            wl.step(evs)
+            all_evs.append(evs)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        for evs in all_evs:
+            wl.timer.collect(evs)
+    ms_per_step = wall * 1e3 / args.steps
+
+    res = wl.results()
+    dom = wl.dominant(res)
+    if "decode" in res:
+        value, unit = res["decode"]["value"], "GB/s"
+    else:
+        value, unit = res["prefill"]["value"], "TFLOP/s"
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 Q/K/V, seeded page placement; no trained weights)",
+        "config": wl.config(),
+        "roofline": {
+            "kernel": dom["kernel"], "bound": dom["bound"], "achieved": round(dom["achieved"], 3),
+            "peak": dom["peak"], "unit": dom["unit"], "frac": round(dom["achieved"] / dom["peak"], 4),
+            "traffic": None, "avg_ms": round(dom["ms"], 5), "per_launch": dom["per_launch"],
+        },
+    }
+    for k in ("decode", "prefill", "append"):
+        if k in res:
+            line[k] = {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in res[k].items()}
+    if not args.no_cpu_baseline and hasattr(wl, "cpu_baseline"):
+        line["cpu_baseline"] = wl.cpu_baseline(args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -13,8 +13,8 @@
 //   8 * sum_b ceil(L_b / 512) waves plus a tail of waves that find f beyond the total and exit.
 //   Both query heads of the GQA group (2g, 2g+1) are served from the same K/V loads.  The wave
 //   writes the split's normalised partial output and its log-sum-exp.
-// decode_merge: one wavefront per (request, query head) combines that request's partials with
-//   weights exp(lse_s - LSE).
+// decode_merge: one workgroup per (request, query head) combines that request's partials with
+//   weights exp(lse_s - LSE), reducing over wavefronts and LDS.
 //
 // Lane layout inside decode_split for one 64-token page: lane = 8*sg + o.  The lane handles the
 // 8 slots {8a + sg : a = 0..7} and, of each slot row (128 dims = 256 bytes), the two 16-byte
@@ -228,60 +228,103 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
   }
 }
 
-// One wavefront per (request b, query head h); 4 heads per workgroup.
+// One workgroup (4 wavefronts) per (request b, query head h).  The split weights
+// w_s = exp(lse_s - LSE) go to LDS; then 16 lane groups of 16 lanes each take every 16th partial
+// (a lane covers 8 dims with two 16-byte loads), so all partial rows of the request are in flight
+// at once instead of one after another; the 16 group sums are added in LDS.
+constexpr int kMaxParts = kMaxContext / kSplit;  // partials of one request
+
 __global__ __launch_bounds__(256) void decode_merge_kernel(
     const int32_t* __restrict__ kv_lens, int batch, int max_kv_len,
     const float* __restrict__ part_o, const float* __restrict__ part_lse, float* __restrict__ out,
     float* __restrict__ lse_out) {
-  const int lane = threadIdx.x & 63;
-  const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int b = blockIdx.y;
-  // First flat split of request b = sum over earlier requests of ceil(L / 512).
-  int first = 0, len = 0;
-  for (int c0 = 0; c0 <= b; c0 += 64) {
-    const int idx = c0 + lane;
-    int ln = idx < batch ? kv_lens[idx] : 0;
-    ln = min(max(ln, 0), max_kv_len);
-    const int n = (ln + kSplit - 1) / kSplit;
-    if (b < c0 + 64) {
-      const int before = idx < b ? n : 0;
-      first += wave_sum_int(before);
-      len = __shfl(ln, b - c0, 64);
-    } else {
-      first += wave_sum_int(n);
+  __shared__ float s_w[kMaxParts];
+  __shared__ float s_red[16][kHeadDim];
+  __shared__ float s_wave[4];
+  __shared__ int s_first, s_n;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int h = blockIdx.x % kQHeads;
+  const int b = blockIdx.x / kQHeads;
+
+  if (wave == 0) {
+    // first flat split of request b = sum over earlier requests of ceil(L / 512)
+    int first = 0, len = 0;
+    for (int c0 = 0; c0 <= b; c0 += 64) {
+      const int idx = c0 + lane;
+      int ln = idx < batch ? kv_lens[idx] : 0;
+      ln = min(max(ln, 0), max_kv_len);
+      const int n = (ln + kSplit - 1) / kSplit;
+      if (b < c0 + 64) {
+        first += wave_sum_int(idx < b ? n : 0);
+        len = __shfl(ln, b - c0, 64);
+      } else {
+        first += wave_sum_int(n);
+      }
+    }
+    if (lane == 0) {
+      s_first = first;
+      s_n = (len + kSplit - 1) / kSplit;
     }
   }
-  const int n_parts = (len + kSplit - 1) / kSplit;
+  __syncthreads();
+  const int first = s_first;
+  const int n_parts = s_n;
   float* orow = out + ((size_t)b * kQHeads + h) * kHeadDim;
-  if (n_parts == 0) {  // no keys: defined as zero output and LSE = -inf
-    reinterpret_cast<float2*>(orow)[lane] = make_float2(0.f, 0.f);
-    if (lane == 0) lse_out[(size_t)b * kQHeads + h] = kNegInf;
+  if (n_parts == 0) {  // no keys: zero output, LSE = -inf
+    if (tid < kHeadDim) orow[tid] = 0.f;
+    if (tid == 0) lse_out[(size_t)b * kQHeads + h] = kNegInf;
     return;
   }
-  // Max LSE over the parts (natural log), then weights.
+
+  // LSE of every part -> LDS, block max
   float mx = kNegInf;
-  for (int p = lane; p < n_parts; p += 64)
-    mx = fmaxf(mx, part_lse[(size_t)(first + p) * kQHeads + h]);
-  mx = wave_max(mx);
-  float wsum = 0.f;
-  float2 acc = make_float2(0.f, 0.f);
-  for (int p0 = 0; p0 < n_parts; p0 += 64) {
-    const int p = p0 + lane;
-    const float w = p < n_parts ? fast_exp2((part_lse[(size_t)(first + p) * kQHeads + h] - mx) * kLog2e) : 0.f;
-    wsum += w;
-    const int cnt = min(64, n_parts - p0);
-    for (int j = 0; j < cnt; ++j) {
-      const float wj = __shfl(w, j, 64);
-      const float2 v = reinterpret_cast<const float2*>(
-          part_o + ((size_t)(first + p0 + j) * kQHeads + h) * kHeadDim)[lane];
-      acc.x += wj * v.x;
-      acc.y += wj * v.y;
-    }
+  for (int p = tid; p < n_parts; p += 256) {
+    const float v = part_lse[(size_t)(first + p) * kQHeads + h];
+    s_w[p] = v;
+    mx = fmaxf(mx, v);
   }
-  wsum = wave_sum(wsum);
-  const float inv = 1.f / wsum;
-  reinterpret_cast<float2*>(orow)[lane] = make_float2(acc.x * inv, acc.y * inv);
-  if (lane == 0) lse_out[(size_t)b * kQHeads + h] = mx + logf(wsum);
+  mx = wave_max(mx);
+  if (lane == 0) s_wave[wave] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(s_wave[0], s_wave[1]), fmaxf(s_wave[2], s_wave[3]));
+  __syncthreads();
+  // weights and their sum
+  float ws = 0.f;
+  for (int p = tid; p < n_parts; p += 256) {
+    const float w = fast_exp2((s_w[p] - mx) * kLog2e);
+    s_w[p] = w;
+    ws += w;
+  }
+  ws = wave_sum(ws);
+  if (lane == 0) s_wave[wave] = ws;
+  __syncthreads();
+  ws = s_wave[0] + s_wave[1] + s_wave[2] + s_wave[3];
+
+  // weighted sum of the partial outputs
+  const int grp = tid >> 4;       // parts grp, grp + 16, ...
+  const int c = tid & 15;         // dims 8c .. 8c+7
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int p = grp; p < n_parts; p += 16) {
+    const float w = s_w[p];
+    const float4* src = reinterpret_cast<const float4*>(part_o + ((size_t)(first + p) * kQHeads + h) * kHeadDim + 8 * c);
+    const float4 v0 = src[0];
+    const float4 v1 = src[1];
+    acc[0] += w * v0.x; acc[1] += w * v0.y; acc[2] += w * v0.z; acc[3] += w * v0.w;
+    acc[4] += w * v1.x; acc[5] += w * v1.y; acc[6] += w * v1.z; acc[7] += w * v1.w;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s_red[grp][8 * c + e] = acc[e];
+  __syncthreads();
+  if (tid < kHeadDim) {
+    float sum = 0.f;
+#pragma unroll
+    for (int g2 = 0; g2 < 16; ++g2) sum += s_red[g2][tid];
+    orow[tid] = sum / ws;
+  }
+  if (tid == 0) lse_out[(size_t)b * kQHeads + h] = mx + logf(ws);
 }
 
 }  // namespace
@@ -303,7 +346,7 @@ hipError_t launch_decode(const KvPools& kv, const uint16_t* q, const int32_t* kv
       scale * kLog2e, part_o, part_lse);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  decode_merge_kernel<<<dim3(kQHeads / 4, batch), dim3(256), 0, stream>>>(
+  decode_merge_kernel<<<dim3(batch * kQHeads), dim3(256), 0, stream>>>(
       kv_lens, batch, max_kv_len, part_o, part_lse, out, lse);
   return hipGetLastError();
 }
