@@ -351,7 +351,106 @@ class Prefill90:
                 "ms": res["prefill"]["ms"] / len(self.chunks)}
 
 
-WORKLOAD_CLASSES = {c.name: c for c in (MixedStep, Decode16, Prefill90)}
+class FullDepth:
+    """28 layers x 64 requests, all layers resident; a step appends one token per request and
+    runs decode attention, layer after layer (128 steps in a full pass)."""
+    name = "fulldepth_decode"
+
+    def __init__(self, dev):
+        import torch
+        import gqa_kv_cache_qwen3_amd as mtd
+        self.mtd, self.torch = mtd, torch
+        free, _ = torch.cuda.mem_get_info(dev)
+        self.lens0, self.seeds_tried, self.need_bytes = W.fulldepth_draw(free)
+        self.inp = W.build_fulldepth(dev, self.lens0)
+        self.layers, self.steps = self.inp["layers"], self.inp["steps"]
+        b = len(self.lens0)
+        self.bt = torch.as_tensor(self.inp["tables"], device=dev)
+        self.cu = torch.arange(b + 1, dtype=torch.int32, device=dev)
+        self.start = [torch.as_tensor((self.lens0 + s).astype(np.int32), device=dev) for s in range(self.steps)]
+        self.kv_lens = [torch.as_tensor((self.lens0 + s + 1).astype(np.int32), device=dev) for s in range(self.steps)]
+        self.max_len = int(self.lens0.max()) + self.steps
+        self.ws = torch.empty(mtd.decode_workspace_bytes(b, self.max_len), dtype=torch.uint8, device=dev)
+        self.o = torch.empty((b, W.HQ, W.HEAD_DIM), dtype=torch.float32, device=dev)
+        self.l = torch.empty((b, W.HQ), dtype=torch.float32, device=dev)
+        self.step_idx = 0
+        self.timer = Timer(["append", "decode"])
+        self.bytes_per_step = [self.layers * decode_bytes(self.lens0 + s + 1) for s in range(self.steps)]
+        self.timed_bytes = 0
+
+    def step(self, events=None):
+        mtd, inp = self.mtd, self.inp
+        s = self.step_idx % self.steps
+        self.step_idx += 1
+        app = dec = 0.0
+        evs = []
+        for layer in range(self.layers):
+            kp, vp = inp["k_pools"][layer], inp["v_pools"][layer]
+            e = [self.torch.cuda.Event(enable_timing=True) for _ in range(3)] if events is not None else None
+            if e: e[0].record()
+            mtd.mtd_kv_append(kp, vp, inp["k_new"][s, layer], inp["v_new"][s, layer], self.cu, self.start[s], self.bt)
+            if e: e[1].record()
+            mtd.mtd_attn_decode(kp, vp, inp["q"][s, layer], self.kv_lens[s], self.bt, self.max_len, W.SCALE,
+                                self.ws, self.o, self.l)
+            if e: e[2].record()
+            if e: evs.append(e)
+        if events is not None:
+            events.append(evs)
+            self.timed_bytes += self.bytes_per_step[s]
+
+    def collect(self, step_events):
+        for evs in step_events:
+            self.timer.samples["append"].append(sum(e[0].elapsed_time(e[1]) for e in evs))
+            self.timer.samples["decode"].append(sum(e[1].elapsed_time(e[2]) for e in evs))
+
+    def config(self):
+        return {"workload": "fulldepth_decode: 28 layers x 64 requests, initial KV lengths log-uniform in "
+                            "[4000, 131072-128], all layers resident; per step and layer: append 1 token per "
+                            "request, then decode", "layers": self.layers, "batch": len(self.lens0),
+                "initial_kv_tokens": int(self.lens0.sum()), "pool_pages_per_layer": int(self.inp["num_pages"]),
+                "hbm_input_bytes": int(self.need_bytes), "seeds_tried": self.seeds_tried}
+
+    def results(self):
+        dec_ms = float(np.sum(self.timer.samples["decode"]))
+        calls = len(self.timer.samples["decode"]) * self.layers
+        gbs = self.timed_bytes / (dec_ms * 1e-3) / 1e9
+        return {"decode": {"value": gbs, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                           "ms": dec_ms / calls, "bytes": self.timed_bytes / calls,
+                           "kernels": "decode_split_kernel + decode_merge_kernel (per layer call)"},
+                "append": {"ms": float(np.sum(self.timer.samples["append"])) / calls}}
+
+    def dominant(self, res):
+        return {"kernel": "decode_split_kernel+decode_merge_kernel", "bound": "hbm", "achieved": res["decode"]["value"],
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "per_launch": res["decode"]["bytes"], "ms": res["decode"]["ms"]}
+
+    def cpu_baseline(self, budget_s=20.0):
+        import torch
+        import oracle
+        torch.cuda.synchronize()
+        host = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        # sample: requests of the layer-0 call of the last timed step, seeded order, within budget
+        s = (self.step_idx - 1) % self.steps
+        kp, vp = self.inp["k_pools"][0], self.inp["v_pools"][0]
+        q = host(self.inp["q"][s, 0])
+        t_dec, nbytes, n_req = 0.0, 0.0, 0
+        for b in W.rng(5, 77).permutation(len(self.lens0)):
+            n = int(self.lens0[b]) + s + 1
+            used = (n + W.PAGE - 1) // W.PAGE
+            idx = torch.as_tensor(self.inp["tables"][b][:used].astype(np.int64), device=kp.device)
+            kc, vc = host(kp.index_select(0, idx)), host(vp.index_select(0, idx))
+            t0 = time.perf_counter()
+            oracle.decode(q[b:b + 1], kc, vc, [n], [np.arange(used)], W.SCALE)
+            t_dec += time.perf_counter() - t0
+            nbytes += KV_BYTES_PER_TOKEN * n
+            n_req += 1
+            if t_dec > budget_s:
+                break
+        return {"value": nbytes / t_dec / 1e9, "unit": "GB/s", "cores": blas_threads(), "kind": "oracle",
+                "sample": f"decode of {n_req} of the 64 requests of one layer call ({int(nbytes / KV_BYTES_PER_TOKEN)} "
+                          f"KV tokens, {t_dec:.1f} s); fp64 numpy"}
+
+
+WORKLOAD_CLASSES = {c.name: c for c in (MixedStep, Decode16, Prefill90, FullDepth)}
 
 
 def blas_threads() -> int:
@@ -366,13 +465,15 @@ def blas_threads() -> int:
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default 20; 128 for fulldepth_decode)")
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mixed_step", choices=sorted(WORKLOAD_CLASSES))
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing on the host")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for cpu_baseline")
     args = ap.parse_args()
 
+    if args.steps is None:
+        args.steps = 128 if args.workload == "fulldepth_decode" else 20
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
               "(multi-GPU sharding is a design note only)", file=sys.stderr)
@@ -389,10 +490,19 @@ def main():
     for _ in range(args.warmup):
         wl.step()
     torch.cuda.synchronize()
+    if isinstance(wl, FullDepth):
+        wl.step_idx = 0  # the timed pass starts again at step 0 (appends rewrite the same slots)
 
     # timed region: exactly K steps between synchronisations; per-call events inside
     t0 = time.perf_counter()
-    if isinstance(wl, Prefill90):
+    if isinstance(wl, FullDepth):
+        step_events = []
+        for _ in range(args.steps):
+            wl.step(step_events)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        wl.collect(step_events)
+    elif isinstance(wl, Prefill90):
         all_evs = []
         for _ in range(args.steps):
             all_evs.append(wl.timed_step())

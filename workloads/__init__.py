@@ -156,3 +156,62 @@ FULLDEPTH = Workload(
 )
 
 WORKLOADS = {w.name: w for w in (TINY, DECODE16, PREFILL90, MIXED, FULLDEPTH)}
+
+
+# --------------------------------------------------------------------------------------
+# Full-depth decode inputs (28 layers x 64 requests, all layers resident in HBM)
+# --------------------------------------------------------------------------------------
+
+def fulldepth_bytes(lens0, steps: int, layers: int) -> int:
+    """Exact HBM bytes of the full-depth inputs: every layer's K+V pools, the per-step queries and
+    new K/V rows, and one decode workspace."""
+    b = len(lens0)
+    pages = int(pages_needed(np.asarray(lens0) + steps).sum()) + 1
+    pools = layers * pages * 2 * HKV * PAGE * HEAD_DIM * 2
+    qs = steps * layers * b * HQ * HEAD_DIM * 2
+    new = steps * layers * b * HKV * HEAD_DIM * 2 * 2
+    max_len = int(np.max(lens0)) + steps
+    ws = b * ((max_len + 511) // 512) * HQ * (HEAD_DIM + 1) * 4
+    return pools + qs + new + ws
+
+
+def fulldepth_draw(free_bytes: int, fraction: float = 0.95, max_tries: int = 8):
+    """Draw initial KV lengths log-uniform in [4000, 131072 - steps]; if the inputs would not fit
+    in fraction * free_bytes, redraw with the next seed (never truncating lengths).
+    Returns (lens0, seeds_tried, bytes_needed)."""
+    p = FULLDEPTH.params
+    tried = []
+    for t in range(max_tries):
+        lens0 = loguniform_lengths(p["batch"], p["lo"], p["hi"] - p["steps"], FULLDEPTH.tag, t)
+        need = fulldepth_bytes(lens0, p["steps"], p["layers"])
+        tried.append(t)
+        if need <= fraction * free_bytes:
+            return lens0, tried, need
+    raise MemoryError(f"full-depth inputs do not fit in {fraction} x {free_bytes} bytes after seeds {tried}")
+
+
+def build_fulldepth(device, lens0, steps: int | None = None, layers: int | None = None):
+    """Seeded full-depth tensors on `device`.
+
+    Layer 0's pools are N(0,1) bf16 in every slot; layer l's pools are layer 0's rolled by l pages
+    (so every layer holds different data at the cost of a copy instead of fresh draws).  All
+    layers share one block table (same page ids, separate pools).  Queries and new K/V rows for
+    every (step, layer) are drawn up front.
+    """
+    import torch
+    p = FULLDEPTH.params
+    steps = p["steps"] if steps is None else steps
+    layers = p["layers"] if layers is None else layers
+    b = len(lens0)
+    tables, num_pages, spare = place_pages(np.asarray(lens0) + steps, FULLDEPTH.tag, 1)
+    base_k = normal_bf16((num_pages, HKV, PAGE, HEAD_DIM), torch_seed(FULLDEPTH.tag, 1), device)
+    base_v = normal_bf16((num_pages, HKV, PAGE, HEAD_DIM), torch_seed(FULLDEPTH.tag, 2), device)
+    k_pools, v_pools = [base_k], [base_v]
+    for layer in range(1, layers):
+        k_pools.append(torch.roll(base_k, shifts=layer, dims=0))
+        v_pools.append(torch.roll(base_v, shifts=layer, dims=0))
+    q = normal_bf16((steps, layers, b, HQ, HEAD_DIM), torch_seed(FULLDEPTH.tag, 3), device)
+    k_new = normal_bf16((steps, layers, b, HKV, HEAD_DIM), torch_seed(FULLDEPTH.tag, 4), device)
+    v_new = normal_bf16((steps, layers, b, HKV, HEAD_DIM), torch_seed(FULLDEPTH.tag, 5), device)
+    return dict(tables=tables, num_pages=num_pages, spare=spare, k_pools=k_pools, v_pools=v_pools,
+                q=q, k_new=k_new, v_new=v_new, steps=steps, layers=layers)
