@@ -19,6 +19,7 @@ time in the step, timed with HIP events on the stream the library launches on.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -40,6 +41,40 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 KV_BYTES_PER_TOKEN = 2 * W.HKV * W.HEAD_DIM * 2          # K + V, all KV heads, bf16
 Q_BYTES = W.HQ * W.HEAD_DIM * 2                          # one query token, all heads
 OUT_BYTES = W.HQ * W.HEAD_DIM * 4 + W.HQ * 4              # fp32 O + LSE per query token
+
+
+# HBM traffic per launch measured with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE (scaled by the same
+# counters on a copy kernel of known size) is recorded in profiles/traffic.md together with a digest
+# of the kernel's sources; it is reported only while the sources still match.
+TRAFFIC_TABLE = os.path.join(ROOT, "profiles", "traffic.md")
+KERNEL_SOURCES = {
+    "prefill_kernel": ["prefill.hip"],
+    "decode_split_kernel+decode_merge_kernel": ["decode.hip"],
+}
+COMMON_SOURCES = ["device_util.h", "mtd_internal.h"]
+
+
+def source_digest(kernel: str) -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES.get(kernel, []) + COMMON_SOURCES:
+        with open(os.path.join(ROOT, "gqa_kv_cache_qwen3_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from profiles/traffic.md if recorded for these exact sources, else None."""
+    if not os.path.exists(TRAFFIC_TABLE):
+        return None
+    digest = source_digest(kernel)
+    for line in open(TRAFFIC_TABLE):
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) >= 4 and cells[0] == kernel and cells[1] == workload and cells[2] == digest:
+            try:
+                return float(cells[3])
+            except ValueError:
+                return None
+    return None
 
 
 def decode_bytes(lens) -> int:
@@ -462,6 +497,20 @@ def blas_threads() -> int:
         return 1
 
 
+def calibrate_copy():
+    """A plain copy kernel of known size: 1 GiB read + 1 GiB written per launch, 5 launches."""
+    import torch
+    n = 1 << 28  # float32 elements = 1 GiB
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        torch.mul(a, 1.0, out=b)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy": {"read_bytes_per_launch": 4 * n, "write_bytes_per_launch": 4 * n,
+                                         "launches": 5, "kernel": "vectorized_elementwise_kernel (mul)"}}))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -470,7 +519,12 @@ def main():
     ap.add_argument("--workload", default="mixed_step", choices=sorted(WORKLOAD_CLASSES))
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing on the host")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a 1 GiB elementwise copy 5 times (reference for HBM byte counters)")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
 
     if args.steps is None:
         args.steps = 128 if args.workload == "fulldepth_decode" else 20
@@ -548,7 +602,8 @@ def main():
         "roofline": {
             "kernel": dom["kernel"], "bound": dom["bound"], "achieved": round(dom["achieved"], 3),
             "peak": dom["peak"], "unit": dom["unit"], "frac": round(dom["achieved"] / dom["peak"], 4),
-            "traffic": None, "avg_ms": round(dom["ms"], 5), "per_launch": dom["per_launch"],
+            "traffic": recorded_traffic(dom["kernel"], wl.name), "avg_ms": round(dom["ms"], 5),
+            "per_launch": dom["per_launch"], "source_digest": source_digest(dom["kernel"]),
         },
     }
     for k in ("decode", "prefill", "append"):
