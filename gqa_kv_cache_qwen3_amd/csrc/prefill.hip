@@ -15,9 +15,11 @@
 // K/V staging.  A 64-key tile is one page of the KV head: 16 KiB of K and 16 KiB of V, each
 // brought into LDS by 16-byte direct-to-LDS loads (global_load_lds_dwordx4, no registers, no
 // VALU) into one of two stages, so tile kt+1 streams in while tile kt is computed; one barrier per
-// tile.  Both tiles stay row-major [key][dim] in LDS with 16-byte slots XOR-swizzled per row
-// (slot of row r, chunk c = 16 r + (c ^ swz(r))), which keeps the K fragment reads and the
-// transposed V reads free of bank conflicts.
+// tile.  In LDS a tile is four column groups of 64 bytes (dims 32j .. 32j+31) of 64 rows each:
+// 16-byte slot of (row r, chunk c) = 256 (c/4) + 4 r + ((c%4) ^ g(r)), g(r) = (r/4)%4 for K and
+// 0 for V.  That layout makes both read patterns free of bank conflicts and every read address a
+// per-lane base plus a compile-time offset, and each load instruction still fetches 16 rows x
+// 64 contiguous bytes.
 //
 // Per tile:
 //   S^T = K Q^T   v_mfma_f32_32x32x16_bf16, keys as rows: a lane holds one query column and 16
@@ -47,22 +49,18 @@ typedef __attribute__((address_space(3))) short4_t lds_short4_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef const __attribute__((address_space(1))) void global_cvoid_t;
 
-// XOR swizzle of the 16 slots of a 256-byte row: rows within any 16 consecutive rows get distinct
-// values (conflict-free 16-byte K reads), and any 4 consecutive aligned rows differ in the two
-// high bits (conflict-free 8-byte transposed V reads).
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
-__device__ __forceinline__ int slot_of(int r, int c) { return 16 * r + (c ^ swz(r)); }
-
-// Direct-to-LDS load of one K or V tile, 4 instructions per wave: instruction inst fills slots
-// 64 inst .. 64 inst + 63, i.e. rows 4 inst .. 4 inst + 3; lane l writes slot 64 inst + l and
-// therefore fetches row 4 inst + l/16, chunk (l % 16) ^ swz(row).  Rows >= nvalid fetch row 0.
+// Direct-to-LDS load of one K or V tile, 4 instructions per wave.  Instruction inst fills slots
+// 64 inst .. 64 inst + 63 = column group inst/4, rows 16 (inst%4) .. +15; lane l writes slot
+// 64 inst + l and so fetches row 16 (inst%4) + l/4, chunk 4 (inst/4) + ((l%4) ^ g(row)), where
+// g = (row/4)%4 for K (kSwizzle) and 0 for V.  Rows >= nvalid fetch row 0 instead.
+template <bool kSwizzle>
 __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ blk, uint8_t* lds, int wave,
                                          int lane, int nvalid) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int inst = 4 * wave + j;
-    const int r = 4 * inst + (lane >> 4);
-    const int c = (lane & 15) ^ swz(r);
+    const int r = 16 * (inst & 3) + (lane >> 2);
+    const int c = 4 * (inst >> 2) + ((lane & 3) ^ (kSwizzle ? ((r >> 2) & 3) : 0));
     const int rs = r < nvalid ? r : 0;
     __builtin_amdgcn_global_load_lds((global_cvoid_t*)(blk + rs * kHeadDim + c * 8),
                                      (lds_void_t*)(lds + inst * 1024), 16, 0, 0);
@@ -75,16 +73,21 @@ struct TileArgs {
   const uint16_t* k_pages;
   const uint16_t* v_pages;
   const int32_t* block_table;
-  int num_pages, g, total, wave, lane;
+  int num_pages, g, total, wave, lane, n_tiles;
 };
 
-__device__ __forceinline__ void issue_tile(const TileArgs& a, int kt, uint8_t* k_lds, uint8_t* v_lds) {
-  int page = a.block_table[kt];
+// Page id of tile kt (loaded one tile ahead of its DMA so the scalar load is never waited on).
+__device__ __forceinline__ int tile_page(const TileArgs& a, int kt) {
+  return kt < a.n_tiles ? a.block_table[kt] : 0;
+}
+
+__device__ __forceinline__ void issue_tile(const TileArgs& a, int kt, int page, uint8_t* k_lds,
+                                           uint8_t* v_lds) {
   if (page < 0 || page >= a.num_pages) page = 0;  // out-of-pool ids: defined reads, unspecified result
   const size_t blk = ((size_t)page * kKvHeads + a.g) * (kPage * kHeadDim);
   const int nvalid = min(kBK, a.total - kt * kBK);
-  dma_tile(a.k_pages + blk, k_lds, a.wave, a.lane, nvalid);
-  dma_tile(a.v_pages + blk, v_lds, a.wave, a.lane, nvalid);
+  dma_tile<true>(a.k_pages + blk, k_lds, a.wave, a.lane, nvalid);
+  dma_tile<false>(a.v_pages + blk, v_lds, a.wave, a.lane, nvalid);
 }
 
 struct SoftmaxState {
@@ -93,101 +96,118 @@ struct SoftmaxState {
   float l;              // running sum of exp2(x - m) over this lane's keys
 };
 
-// One 64-key tile: S^T, online softmax, O^T update.  Reads only k_lds / v_lds.
-__device__ __forceinline__ void compute_tile(SoftmaxState& st_, const bf16x8_t (&qf)[8],
-                                             const uint8_t* k_lds, const uint8_t* v_lds, int kt,
-                                             int n, int hk, int lane, bool need_mask, int qabs,
-                                             float scale_log2) {
-  floatx16_t st[2];
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-    for (int v = 0; v < 16; ++v) st[mt][v] = 0.f;
-    const int r = 32 * mt + n;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const bf16x8_t a = __builtin_bit_cast(
-          bf16x8_t, *reinterpret_cast<const uint4*>(k_lds + 16 * slot_of(r, 2 * ks + hk)));
-      st[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], st[mt], 0, 0, 0);
-    }
-  }
+// Per-lane LDS byte bases; every read adds a compile-time offset to one of them.
+//   kbase[ks%2]: K fragment of row n, chunk 2ks + hk  -> + 4096 (ks/2) + 2048 mt
+//   vbase:       transposed V read of keys 4hk + (l%16)/4, dims 16((l/16)%2) + 4(l%4) .. +3
+//                -> + 4096 dt + 64 (32 mt + 16 t + 8 sec)
+struct LdsOffsets {
+  int kbase[2];
+  int vbase;
+};
 
-  // Accumulator element v of block mt is key 32mt + 8(v/4) + 4hk + v%4.
+__device__ __forceinline__ LdsOffsets make_offsets(int lane) {
+  LdsOffsets o;
+  const int n = lane & 31, hk = lane >> 5, gi = lane & 15, half = (lane >> 4) & 1;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) o.kbase[e] = 64 * n + 16 * ((2 * e + hk) ^ ((n >> 2) & 3));
+  o.vbase = 64 * (4 * hk + (gi >> 2)) + 16 * (2 * half + ((gi & 3) >> 1)) + 8 * (gi & 1);
+  return o;
+}
+
+// S^T block mt (keys 32mt .. 32mt+31 of the tile) for this wave's 32 query columns.
+__device__ __forceinline__ floatx16_t scores(const bf16x8_t (&qf)[8], const uint8_t* k_lds,
+                                             const LdsOffsets& off, int mt) {
+  floatx16_t st;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) st[v] = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    const bf16x8_t a = __builtin_bit_cast(
+        bf16x8_t, *reinterpret_cast<const uint4*>(k_lds + off.kbase[ks & 1] + 4096 * (ks >> 1) + 2048 * mt));
+    st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], st, 0, 0, 0);
+  }
+  return st;
+}
+
+// Online-softmax update with one 32-key block and its P^T operands (two 16-key k-steps).
+template <bool kMask>
+__device__ __forceinline__ void softmax_block(SoftmaxState& sm, floatx16_t& st, bf16x8_t (&pf)[2],
+                                              int key0, int hk, int qabs, float scale_log2) {
+  // Accumulator element v is key key0 + 8(v/4) + 4hk + v%4.
   float smax = kNegInf;
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      float x = st[mt][v];
-      if (need_mask) {
-        const int key = kt * kBK + 32 * mt + 8 * (v >> 2) + 4 * hk + (v & 3);
-        x = key <= qabs ? x : kNegInf;
-      }
-      st[mt][v] = x;
-      smax = fmaxf(smax, x);
+  for (int v = 0; v < 16; ++v) {
+    float x = st[v];
+    if (kMask) {
+      const int key = key0 + 8 * (v >> 2) + 4 * hk + (v & 3);
+      x = key <= qabs ? x : kNegInf;
+      st[v] = x;
     }
+    smax = fmaxf(smax, x);
   }
   smax = fmaxf(smax, __shfl_xor(smax, 32, 64));
-  const float tmax = smax * scale_log2;
   // Exact running max, so the largest weight of a column is exactly 1 before its bf16 rounding
-  // (peaked softmaxes stay accurate); the output accumulators are rescaled only on the tiles
-  // where some column's max actually grew (about 1/t of the tiles at depth t).
-  const float m_new = fmaxf(st_.m, tmax);
-  if (__any(m_new > st_.m)) {
-    const float alpha = m_new == st_.m ? 1.f : fast_exp2(st_.m - m_new);
-    st_.l *= alpha;
+  // (peaked softmaxes stay accurate); the output accumulators are rescaled only on the blocks
+  // where some column's max actually grew.
+  const float m_new = fmaxf(sm.m, smax * scale_log2);
+  if (__any(m_new > sm.m)) {
+    const float alpha = m_new == sm.m ? 1.f : fast_exp2(sm.m - m_new);
+    sm.l *= alpha;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) st_.o_acc[dt][v] *= alpha;
+      for (int v = 0; v < 16; ++v) sm.o_acc[dt][v] *= alpha;
   }
-  st_.m = m_new;
+  sm.m = m_new;
   const float m_use = m_new == kNegInf ? 0.f : m_new;
   float psum = 0.f;
-  bf16x8_t pf[2][2];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
+  for (int t = 0; t < 2; ++t) {
+    uint32_t w[4];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      uint32_t w[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float p0 = fast_exp2(fmaf(st[mt][8 * t + 2 * j], scale_log2, -m_use));
-        const float p1 = fast_exp2(fmaf(st[mt][8 * t + 2 * j + 1], scale_log2, -m_use));
-        psum += p0 + p1;
-        w[j] = pack_bf16x2(p0, p1);
-      }
-      pf[mt][t] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
+    for (int j = 0; j < 4; ++j) {
+      const float p0 = fast_exp2(fmaf(st[8 * t + 2 * j], scale_log2, -m_use));
+      const float p1 = fast_exp2(fmaf(st[8 * t + 2 * j + 1], scale_log2, -m_use));
+      psum += p0 + p1;
+      w[j] = pack_bf16x2(p0, p1);
     }
+    pf[t] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
   }
-  st_.l += psum;
+  sm.l += psum;
+}
 
-  // O^T += V^T P^T.  Block mt, k-step t: this lane's 8 keys are 32mt + 16t + 4hk + {0..3} and the
-  // same + 8; lane (l % 16) of 16-lane group G addresses key base + (l%16)/4, dims
-  // 32dt + 16(G % 2) + 4(l % 4) .. +3, and receives the 4 keys of dim 32dt + l % 32.
-  const int gi = lane & 15;
-  const int half = (lane >> 4) & 1;
+// O^T += V^T P^T for 32-key block mt.  k-step t: this lane's 8 keys are 32mt + 16t + 4hk + {0..3}
+// and the same + 8, read transposed from the row-major V tile (two 8-byte reads per MFMA).
+__device__ __forceinline__ void accumulate_block(SoftmaxState& sm, const bf16x8_t (&pf)[2],
+                                                 const uint8_t* v_lds, const LdsOffsets& off,
+                                                 int mt) {
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) {
-    const int dim = 32 * dt + 16 * half + 4 * (gi & 3);
-    const int chunk = dim >> 3;
-    const int byte_in = (dim & 7) * 2;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int key0 = 32 * mt + 16 * t + 4 * hk + (gi >> 2);
-        const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_short4_t*)(v_lds + 16 * slot_of(key0, chunk) + byte_in));
-        const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_short4_t*)(v_lds + 16 * slot_of(key0 + 8, chunk) + byte_in));
-        const bf16x8_t a = __builtin_bit_cast(
-            bf16x8_t, make_uint4(__builtin_bit_cast(uint2, lo).x, __builtin_bit_cast(uint2, lo).y,
-                                 __builtin_bit_cast(uint2, hi).x, __builtin_bit_cast(uint2, hi).y));
-        st_.o_acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[mt][t], st_.o_acc[dt], 0, 0, 0);
-      }
+    for (int t = 0; t < 2; ++t) {
+      const int base = off.vbase + 4096 * dt + 64 * (32 * mt + 16 * t);
+      const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(v_lds + base));
+      const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(v_lds + base + 64 * 8));
+      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      sm.o_acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[t], sm.o_acc[dt], 0, 0, 0);
     }
   }
+}
+
+// One 64-key tile as two 32-key blocks (S^T, softmax, O^T update each); the two waves sharing a
+// SIMD interleave their MFMA and VALU phases.
+template <bool kMask>
+__device__ __forceinline__ void compute_tile(SoftmaxState& sm, const bf16x8_t (&qf)[8],
+                                             const uint8_t* k_lds, const uint8_t* v_lds,
+                                             const LdsOffsets& off, int kt, int hk, int qabs,
+                                             float scale_log2) {
+  bf16x8_t p0[2], p1[2];
+  floatx16_t s0 = scores(qf, k_lds, off, 0);
+  softmax_block<kMask>(sm, s0, p0, kt * kBK, hk, qabs, scale_log2);
+  accumulate_block(sm, p0, v_lds, off, 0);
+  floatx16_t s1 = scores(qf, k_lds, off, 1);
+  softmax_block<kMask>(sm, s1, p1, kt * kBK + 32, hk, qabs, scale_log2);
+  accumulate_block(sm, p1, v_lds, off, 1);
 }
 
 __global__ __launch_bounds__(256, 2) void prefill_kernel(
@@ -195,6 +215,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
     const uint16_t* __restrict__ q, int chunk_len, int prefix_len,
     const int32_t* __restrict__ block_table, float scale_log2, float* __restrict__ out,
     float* __restrict__ lse, int n_qtiles) {
+  // Two stages of (K, V) tiles.  Separate arrays, so the compiler can see that the DMA into one
+  // stage never aliases the reads of the other and adds no wait of its own between them.
   __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t v_lds0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t k_lds1[kTileBytes];
@@ -216,10 +238,12 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
 
   const int kv_end = min(prefix_len + q0 + kBQ, total);
   const int n_tiles = (kv_end + kBK - 1) / kBK;
-  const int wave_first = prefix_len + q0 + 16 * wave;  // smallest query position of the wave
-  const TileArgs ta{k_pages, v_pages, block_table, num_pages, g, total, wave, lane};
+  // Tiles whose keys all precede the workgroup's first query need no causal mask.
+  const int n_plain = (prefix_len + q0 + 1) / kBK;
+  const TileArgs ta{k_pages, v_pages, block_table, num_pages, g, total, wave, lane, n_tiles};
 
-  issue_tile(ta, 0, k_lds0, v_lds0);
+  issue_tile(ta, 0, tile_page(ta, 0), k_lds0, v_lds0);
+  int next_page = tile_page(ta, 1);
 
   // Q^T fragments: k-step ks covers dims 16ks..16ks+15; this lane holds dims 16ks+8hk..+7.
   bf16x8_t qf[8];
@@ -232,6 +256,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
       qf[ks] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
+  const LdsOffsets off = make_offsets(lane);
 
   SoftmaxState sm;
 #pragma unroll
@@ -241,21 +266,31 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   sm.m = kNegInf;
   sm.l = 0.f;
 
-  // Two tiles per trip: stage 0 then stage 1.  At the top of each tile: own DMAs done, barrier
-  // (everyone's DMAs visible, everyone done with the other stage), start the next tile's DMA into
-  // the other stage, compute this one.
-  for (int kt = 0; kt < n_tiles; kt += 2) {
+  // Tile kt lives in stage kt % 2.  At the top of each tile: own DMAs done, barrier (everyone's
+  // DMAs visible, everyone done with the other stage), start the next tile's DMA into the other
+  // stage, compute this one.  Main loop: pairs of tiles below the workgroup's first query (no
+  // causal mask), stages fixed at compile time.  Tail: the last one to three tiles, masked.
+  int kt = 0;
+  for (; kt + 1 < n_plain; kt += 2) {
     wait_dma();
     __syncthreads();
-    if (kt + 1 < n_tiles) issue_tile(ta, kt + 1, k_lds1, v_lds1);
-    compute_tile(sm, qf, k_lds0, v_lds0, kt, n, hk, lane, kt * kBK + kBK - 1 > wave_first, qabs,
-                 scale_log2);
-    if (kt + 1 >= n_tiles) break;
+    issue_tile(ta, kt + 1, next_page, k_lds1, v_lds1);
+    next_page = tile_page(ta, kt + 2);
+    compute_tile<false>(sm, qf, k_lds0, v_lds0, off, kt, hk, qabs, scale_log2);
     wait_dma();
     __syncthreads();
-    if (kt + 2 < n_tiles) issue_tile(ta, kt + 2, k_lds0, v_lds0);
-    compute_tile(sm, qf, k_lds1, v_lds1, kt + 1, n, hk, lane,
-                 (kt + 1) * kBK + kBK - 1 > wave_first, qabs, scale_log2);
+    if (kt + 2 < n_tiles) issue_tile(ta, kt + 2, next_page, k_lds0, v_lds0);
+    next_page = tile_page(ta, kt + 3);
+    compute_tile<false>(sm, qf, k_lds1, v_lds1, off, kt + 1, hk, qabs, scale_log2);
+  }
+  for (; kt < n_tiles; ++kt) {
+    const bool odd = kt & 1;
+    wait_dma();
+    __syncthreads();
+    if (kt + 1 < n_tiles) issue_tile(ta, kt + 1, next_page, odd ? k_lds0 : k_lds1, odd ? v_lds0 : v_lds1);
+    next_page = tile_page(ta, kt + 2);
+    compute_tile<true>(sm, qf, odd ? k_lds1 : k_lds0, odd ? v_lds1 : v_lds0, off, kt, hk, qabs,
+                       scale_log2);
   }
 
   const float l_tot = sm.l + __shfl_xor(sm.l, 32, 64);
