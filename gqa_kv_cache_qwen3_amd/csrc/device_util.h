@@ -57,6 +57,25 @@ __device__ __forceinline__ float sum8(float x) {
   return x;
 }
 
+// The value of lane l ^ 32, for every lane, without a trip through LDS.  v_permlane32_swap with
+// both operands holding x leaves x[l % 32] in the first and x[l % 32 + 32] in the second register
+// (checked on gfx950); one of the two is x[l ^ 32] and the other x[l] itself, so max / sum of the
+// pair is the pair reduction.  Written as inline asm because the compiler folds the intrinsic
+// with two equal operands to a no-op.  The s_nop pairs cover the VALU-write -> permlane hazard.
+__device__ __forceinline__ void swap_halves(float& a, float& b) {
+  asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  float y = x;
+  swap_halves(x, y);
+  return fmaxf(x, y);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  float y = x;
+  swap_halves(x, y);
+  return x + y;
+}
+
 // Inclusive prefix sum across the 64 lanes of a wave.
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 #pragma unroll

@@ -145,7 +145,7 @@ __device__ __forceinline__ void softmax_block(SoftmaxState& sm, floatx16_t& st, 
     }
     smax = fmaxf(smax, x);
   }
-  smax = fmaxf(smax, __shfl_xor(smax, 32, 64));
+  smax = max_xor32(smax);
   // Exact running max, so the largest weight of a column is exactly 1 before its bf16 rounding
   // (peaked softmaxes stay accurate); the output accumulators are rescaled only on the blocks
   // where some column's max actually grew.
@@ -293,7 +293,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
                        scale_log2);
   }
 
-  const float l_tot = sm.l + __shfl_xor(sm.l, 32, 64);
+  const float l_tot = sum_xor32(sm.l);
   if (qvalid) {
     const float inv = 1.f / l_tot;
     float* orow = out + ((size_t)qpos * kQHeads + head) * kHeadDim;
