@@ -39,7 +39,8 @@
 namespace mtd {
 namespace {
 
-constexpr int kBQ = 64;   // chunk positions per workgroup
+constexpr int kBQ = 128;  // chunk positions per workgroup (8 waves x 16 positions x 2 heads)
+constexpr int kWaves = 8;
 constexpr int kBK = 64;   // keys per tile (one page)
 constexpr int kTileBytes = kBK * kHeadDim * 2;  // 16 KiB
 constexpr float kNegInf = -__builtin_huge_valf();
@@ -49,7 +50,7 @@ typedef __attribute__((address_space(3))) short4_t lds_short4_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef const __attribute__((address_space(1))) void global_cvoid_t;
 
-// Direct-to-LDS load of one K or V tile, 4 instructions per wave.  Instruction inst fills slots
+// Direct-to-LDS load of one K or V tile, 2 instructions per wave.  Instruction inst fills slots
 // 64 inst .. 64 inst + 63 = column group inst/4, rows 16 (inst%4) .. +15; lane l writes slot
 // 64 inst + l and so fetches row 16 (inst%4) + l/4, chunk 4 (inst/4) + ((l%4) ^ g(row)), where
 // g = (row/4)%4 for K (kSwizzle) and 0 for V.  Rows >= nvalid fetch row 0 instead.
@@ -57,8 +58,8 @@ template <bool kSwizzle>
 __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ blk, uint8_t* lds, int wave,
                                          int lane, int nvalid) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int inst = 4 * wave + j;
+  for (int j = 0; j < 2; ++j) {
+    const int inst = 2 * wave + j;
     const int r = 16 * (inst & 3) + (lane >> 2);
     const int c = 4 * (inst >> 2) + ((lane & 3) ^ (kSwizzle ? ((r >> 2) & 3) : 0));
     const int rs = r < nvalid ? r : 0;
@@ -67,7 +68,23 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ blk, uint8
   }
 }
 
-__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8; the
+// counters not waited on are left at their maximum).  As builtins, so the compiler's own wait
+// tracking knows which DMAs they retire.
+constexpr int kWaitVm0 = 0x0F70;  // vmcnt(0)
+constexpr int kWaitVm4 = 0x0F74;  // vmcnt(4): all but the most recent tile's 4 DMAs per wave
+__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(kWaitVm0); }
+__device__ __forceinline__ void wait_dma_keep_one() { __builtin_amdgcn_s_waitcnt(kWaitVm4); }
+// Workgroup barrier without a memory fence: __syncthreads() would also drain the DMA still in
+// flight for the next tile.  Ordering is explicit instead: each wave waits for its own DMAs of the
+// tile about to be read (above), every LDS read of the previous tile has been consumed by an MFMA
+// before its wave arrives, and the empty asm statements keep the compiler from moving memory
+// operations across the barrier.
+__device__ __forceinline__ void tile_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 struct TileArgs {
   const uint16_t* k_pages;
@@ -210,13 +227,13 @@ __device__ __forceinline__ void compute_tile(SoftmaxState& sm, const bf16x8_t (&
   accumulate_block(sm, p1, v_lds, off, 1);
 }
 
-__global__ __launch_bounds__(256, 2) void prefill_kernel(
+__global__ __launch_bounds__(512, 1) void prefill_kernel(
     const uint16_t* __restrict__ k_pages, const uint16_t* __restrict__ v_pages, int num_pages,
     const uint16_t* __restrict__ q, int chunk_len, int prefix_len,
     const int32_t* __restrict__ block_table, float scale_log2, float* __restrict__ out,
     float* __restrict__ lse, int n_qtiles) {
-  // Two stages of (K, V) tiles.  Separate arrays, so the compiler can see that the DMA into one
-  // stage never aliases the reads of the other and adds no wait of its own between them.
+  // Two stages of (K, V) tiles, 64 KiB.  Separate arrays, so the compiler can see that the DMA
+  // into one stage never aliases the reads of the other and adds no wait of its own between them.
   __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t v_lds0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t k_lds1[kTileBytes];
@@ -239,9 +256,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   const int kv_end = min(prefix_len + q0 + kBQ, total);
   const int n_tiles = (kv_end + kBK - 1) / kBK;
   // Tiles whose keys all precede the workgroup's first query need no causal mask.
-  const int n_plain = (prefix_len + q0 + 1) / kBK;
+  const int n_plain = min((prefix_len + q0 + 1) / kBK, n_tiles);
   const TileArgs ta{k_pages, v_pages, block_table, num_pages, g, total, wave, lane, n_tiles};
 
+  // Tiles 0 and 1 in flight before anything else.
   issue_tile(ta, 0, tile_page(ta, 0), k_lds0, v_lds0);
   int next_page = tile_page(ta, 1);
 
@@ -266,32 +284,30 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   sm.m = kNegInf;
   sm.l = 0.f;
 
-  // Tile kt lives in stage kt % 2.  At the top of each tile: own DMAs done, barrier (everyone's
-  // DMAs visible, everyone done with the other stage), start the next tile's DMA into the other
-  // stage, compute this one.  Main loop: pairs of tiles below the workgroup's first query (no
-  // causal mask), stages fixed at compile time.  Tail: the last one to three tiles, masked.
+  // Tile kt lives in stage kt % 2.  At the top of tile kt: wait for this wave's DMAs of tile kt,
+  // barrier (everyone's DMAs of tile kt visible, everyone done with tile kt-1), start tile kt+1's
+  // DMA into the stage tile kt-1 used, compute tile kt.  Main loop: two tiles per trip with
+  // compile-time stages, none of them reaching the workgroup's first query (no causal mask).
+  // Tail: the rest, masked.
+#define MTD_PREFILL_STEP(KT, CUR_K, CUR_V, NXT_K, NXT_V, MASK)                          \
+  {                                                                                     \
+    wait_dma();                                                                         \
+    tile_barrier();                                                                     \
+    if ((KT) + 1 < n_tiles) issue_tile(ta, (KT) + 1, next_page, NXT_K, NXT_V);          \
+    next_page = tile_page(ta, (KT) + 2);                                                \
+    compute_tile<MASK>(sm, qf, CUR_K, CUR_V, off, (KT), hk, qabs, scale_log2);          \
+  }
   int kt = 0;
   for (; kt + 1 < n_plain; kt += 2) {
-    wait_dma();
-    __syncthreads();
-    issue_tile(ta, kt + 1, next_page, k_lds1, v_lds1);
-    next_page = tile_page(ta, kt + 2);
-    compute_tile<false>(sm, qf, k_lds0, v_lds0, off, kt, hk, qabs, scale_log2);
-    wait_dma();
-    __syncthreads();
-    if (kt + 2 < n_tiles) issue_tile(ta, kt + 2, next_page, k_lds0, v_lds0);
-    next_page = tile_page(ta, kt + 3);
-    compute_tile<false>(sm, qf, k_lds1, v_lds1, off, kt + 1, hk, qabs, scale_log2);
+    MTD_PREFILL_STEP(kt, k_lds0, v_lds0, k_lds1, v_lds1, false)
+    MTD_PREFILL_STEP(kt + 1, k_lds1, v_lds1, k_lds0, v_lds0, false)
   }
   for (; kt < n_tiles; ++kt) {
     const bool odd = kt & 1;
-    wait_dma();
-    __syncthreads();
-    if (kt + 1 < n_tiles) issue_tile(ta, kt + 1, next_page, odd ? k_lds0 : k_lds1, odd ? v_lds0 : v_lds1);
-    next_page = tile_page(ta, kt + 2);
-    compute_tile<true>(sm, qf, odd ? k_lds1 : k_lds0, odd ? v_lds1 : v_lds0, off, kt, hk, qabs,
-                       scale_log2);
+    MTD_PREFILL_STEP(kt, odd ? k_lds1 : k_lds0, odd ? v_lds1 : v_lds0, odd ? k_lds0 : k_lds1,
+                     odd ? v_lds0 : v_lds1, true)
   }
+#undef MTD_PREFILL_STEP
 
   const float l_tot = sum_xor32(sm.l);
   if (qvalid) {
@@ -315,7 +331,7 @@ hipError_t launch_prefill(const KvPools& kv, const uint16_t* q, int chunk_len, i
                           const int32_t* block_table, float scale, float* out, float* lse,
                           hipStream_t stream) {
   const int n_qtiles = (chunk_len + kBQ - 1) / kBQ;
-  prefill_kernel<<<dim3(n_qtiles * kKvHeads), dim3(256), 0, stream>>>(
+  prefill_kernel<<<dim3(n_qtiles * kKvHeads), dim3(64 * kWaves), 0, stream>>>(
       kv.k, kv.v, kv.num_pages, q, chunk_len, prefix_len, block_table, scale * kLog2e, out, lse,
       n_qtiles);
   return hipGetLastError();
