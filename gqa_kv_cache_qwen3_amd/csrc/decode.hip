@@ -4,8 +4,8 @@
 // requests packed into one batch ("Optimizing ASR Models to Transcribe 90-Minute Multi-Speaker
 // Audio", sections ASR Model Primer and Batched Inference).  With one query token per head the
 // work is two flops per KV byte, far below the MI355X ridge point, so the kernels are built to
-// stream K/V from HBM once, with coalesced 16-byte loads, and keep every other cost off the
-// memory critical path.
+// stream K/V from HBM once, with coalesced 16-byte non-temporal loads, and keep every other cost
+// off the memory critical path.
 //
 // decode_split: one wavefront per work item = (request b, split s, KV head g), where split s is
 //   the logical tokens [512 s, min(512 s + 512, L_b)).  Items are numbered densely: the flat split
@@ -28,6 +28,14 @@ namespace mtd {
 namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
+
+// 16-byte load marked non-temporal: every K/V byte of a decode call is read exactly once, so the
+// loads should stream through the caches instead of displacing other data.
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 stream_load16(const uint16_t* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 // Locate flat split f: request b, split s within b, and b's KV length.  Wave-uniform.
 // kv_lens are clamped to [0, max_kv_len] so the number of partials never exceeds the workspace.
@@ -105,12 +113,12 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
     for (int a = 0; a < 8; ++a)
 #pragma unroll
       for (int c = 0; c < 2; ++c)
-        kr[a][c] = *reinterpret_cast<const uint4*>(kb + (8 * a + sg) * kHeadDim + (8 * c + o) * 8);
+        kr[a][c] = stream_load16(kb + (8 * a + sg) * kHeadDim + (8 * c + o) * 8);
 #pragma unroll
     for (int a = 0; a < 8; ++a)
 #pragma unroll
       for (int c = 0; c < 2; ++c)
-        vr[a][c] = *reinterpret_cast<const uint4*>(vb + (8 * a + sg) * kHeadDim + (8 * c + o) * 8);
+        vr[a][c] = stream_load16(vb + (8 * a + sg) * kHeadDim + (8 * c + o) * 8);
 
     // Scores of slots 8a + sg for both heads, in log2 units.
     float x[2][8];
