@@ -511,11 +511,16 @@ def calibrate_copy():
                                          "launches": 5, "kernel": "vectorized_elementwise_kernel (mul)"}}))
 
 
+# Untimed steps per workload, each about 50 ms of GPU work or more.
+WARMUP_DEFAULT = {"mixed_step": 40, "decode16": 500, "prefill90min": 3, "fulldepth_decode": 5}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None, help="timed steps (default 20; 128 for fulldepth_decode)")
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps (default: enough for ~50 ms of GPU work, past the clock ramp)")
     ap.add_argument("--workload", default="mixed_step", choices=sorted(WORKLOAD_CLASSES))
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing on the host")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for cpu_baseline")
@@ -528,6 +533,10 @@ def main():
 
     if args.steps is None:
         args.steps = 128 if args.workload == "fulldepth_decode" else 20
+    if args.warmup is None:
+        # From idle the shader clock needs about 20 ms of sustained work to reach its steady level
+        # (measured on MI355X); the default warmup covers that with margin.
+        args.warmup = WARMUP_DEFAULT[args.workload]
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
               "(multi-GPU sharding is a design note only)", file=sys.stderr)

@@ -6,33 +6,37 @@
 // prompt is one chunk at P = 0.  No score matrix is ever materialised: the scores of one 64-key
 // tile live in registers and are folded into the output with an fp32 online softmax.
 //
-// Work split.  One workgroup (4 wavefronts) owns 64 chunk positions of one KV head and serves
-// both query heads of its GQA group, so every K/V tile staged in LDS feeds 128 query rows.
-// Wave w takes positions 16w .. 16w+15 of the tile for both heads: 32 query columns.  Workgroup
-// id = 8 * (tile, longest first) + KV head, so the dispatcher's round-robin over the 8 XCDs keeps
-// all tiles of one KV head on one XCD and its L2 serves the K/V re-reads.
+// Work split.  One workgroup (8 wavefronts, two per SIMD) owns 128 chunk positions of one KV
+// head and serves both query heads of its GQA group, so every K/V tile staged in LDS feeds 256
+// query rows.  Wave w takes positions 16w .. 16w+15 for both heads: 32 query columns.  Workgroup
+// id = 8 * (position tile, longest first) + KV head, so the dispatcher's round-robin over the 8
+// XCDs keeps all tiles of one KV head on one XCD and its L2 serves the K/V re-reads.
 //
 // K/V staging.  A 64-key tile is one page of the KV head: 16 KiB of K and 16 KiB of V, each
 // brought into LDS by 16-byte direct-to-LDS loads (global_load_lds_dwordx4, no registers, no
-// VALU) into one of two stages, so tile kt+1 streams in while tile kt is computed; one barrier per
-// tile.  In LDS a tile is four column groups of 64 bytes (dims 32j .. 32j+31) of 64 rows each:
-// 16-byte slot of (row r, chunk c) = 256 (c/4) + 4 r + ((c%4) ^ g(r)), g(r) = (r/4)%4 for K and
-// 0 for V.  That layout makes both read patterns free of bank conflicts and every read address a
-// per-lane base plus a compile-time offset, and each load instruction still fetches 16 rows x
-// 64 contiguous bytes.
+// VALU) into one of three stages: the tile being computed, the next one in flight, and the one
+// the DMA after that will overwrite.  In LDS a tile is four column groups of 64 bytes (dims
+// 32j .. 32j+31) of 64 rows each: 16-byte slot of (row r, chunk c) = 256 (c/4) + 4 r +
+// ((c%4) ^ g(r)), g(r) = (r/4)%4 for K and 0 for V.  That layout makes both read patterns free
+// of bank conflicts and every read address a per-lane base plus a compile-time offset, and each
+// load instruction still fetches 16 rows x 64 contiguous bytes.
 //
-// Per tile:
+// Per 32-key block:
 //   S^T = K Q^T   v_mfma_f32_32x32x16_bf16, keys as rows: a lane holds one query column and 16
-//                 of the 32 keys of each 32-key block, so the softmax over keys is mostly in-lane
-//                 (one exchange with lane ^ 32).  K fragments: ds_read_b128.
+//                 of the 32 keys of the block, so the softmax over keys is mostly in-lane (one
+//                 exchange with lane ^ 32).  K fragments: ds_read_b128.
 //   online softmax in fp32 (exp2, scale folded into one FMA); P rounded to bf16.
 //   O^T += V^T P^T  the P^T operand is exactly the S^T accumulator layout, so P never leaves the
 //                 registers.  The V^T operand comes straight from the row-major V tile through
 //                 ds_read_b64_tr_b16 (each 16-lane group receives the transpose of the 4 x 16
 //                 block its lanes address), two reads per MFMA.
-// Causal masking is applied only on tiles that reach past the wave's first position.  Keys past
-// the request's last token (tail of the last page) are loaded from the page's first row instead
-// of their slots, so V stays finite where their weight is exactly zero.
+// Software pipeline: the softmax of block b (VALU) is issued between the MFMAs of block b+1's
+// scores and of block b-1's output update, so one wave keeps the matrix pipe and the vector ALU
+// busy at once; block b's V^T fragments are read one step before their MFMAs.  One barrier per
+// tile, between its two blocks.
+// Causal masking is applied only on tiles that reach past the workgroup's first position.  Keys
+// past the request's last token (tail of the last page) are loaded from the page's first row
+// instead of their slots, so V stays finite where their weight is exactly zero.
 #include "device_util.h"
 #include "mtd_internal.h"
 
@@ -44,6 +48,7 @@ constexpr int kWaves = 8;
 constexpr int kBK = 64;   // keys per tile (one page)
 constexpr int kTileBytes = kBK * kHeadDim * 2;  // 16 KiB
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kMaxFloor = -1e30f;  // initial running max: below any real scaled score
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4_t lds_short4_t;
@@ -68,18 +73,16 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ blk, uint8
   }
 }
 
-// s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8; the
-// counters not waited on are left at their maximum).  As builtins, so the compiler's own wait
-// tracking knows which DMAs they retire.
-constexpr int kWaitVm0 = 0x0F70;  // vmcnt(0)
-constexpr int kWaitVm4 = 0x0F74;  // vmcnt(4): all but the most recent tile's 4 DMAs per wave
+// s_waitcnt vmcnt(0) (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8; the
+// counters not waited on are left at their maximum).  As a builtin, so the compiler's own wait
+// tracking knows which DMAs it retires.
+constexpr int kWaitVm0 = 0x0F70;
 __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(kWaitVm0); }
-__device__ __forceinline__ void wait_dma_keep_one() { __builtin_amdgcn_s_waitcnt(kWaitVm4); }
 // Workgroup barrier without a memory fence: __syncthreads() would also drain the DMA still in
 // flight for the next tile.  Ordering is explicit instead: each wave waits for its own DMAs of the
-// tile about to be read (above), every LDS read of the previous tile has been consumed by an MFMA
-// before its wave arrives, and the empty asm statements keep the compiler from moving memory
-// operations across the barrier.
+// tile about to be read (above), every LDS read of the stage about to be refilled has been
+// consumed by an MFMA before its wave arrives, and the empty asm statements keep the compiler from
+// moving memory operations across the barrier.
 __device__ __forceinline__ void tile_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
@@ -109,8 +112,10 @@ __device__ __forceinline__ void issue_tile(const TileArgs& a, int kt, int page, 
 
 struct SoftmaxState {
   floatx16_t o_acc[4];  // O^T tiles: dims 32dt .. 32dt+31 x 32 query columns
-  float m;              // running max of the column, log2 units (same in both halves)
+  float m;              // running max of the column, log2 units (same in both halves); starts
+                        // at a finite floor so that no step needs a special case for -inf
   float l;              // running sum of exp2(x - m) over this lane's keys
+  float alpha;          // rescale of o_acc still owed for the last block's max (1 = none)
 };
 
 // Per-lane LDS byte bases; every read adds a compile-time offset to one of them.
@@ -131,53 +136,80 @@ __device__ __forceinline__ LdsOffsets make_offsets(int lane) {
   return o;
 }
 
-// S^T block mt (keys 32mt .. 32mt+31 of the tile) for this wave's 32 query columns.
-__device__ __forceinline__ floatx16_t scores(const bf16x8_t (&qf)[8], const uint8_t* k_lds,
-                                             const LdsOffsets& off, int mt) {
+// K fragments of 32-key block mt (keys 32mt .. 32mt+31 of the tile), one per k-step.
+__device__ __forceinline__ void load_k(bf16x8_t (&kf)[8], const uint8_t* k_lds, const LdsOffsets& off,
+                                       int mt) {
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks)
+    kf[ks] = __builtin_bit_cast(
+        bf16x8_t, *reinterpret_cast<const uint4*>(k_lds + off.kbase[ks & 1] + 4096 * (ks >> 1) + 2048 * mt));
+}
+
+// V^T fragments of block mt: k-step t of dim tile dt holds this lane's 8 keys 32mt + 16t + 4hk +
+// {0..3} and the same + 8, read transposed from the row-major V tile (two 8-byte reads each).
+__device__ __forceinline__ void load_v(bf16x8_t (&vf)[8], const uint8_t* v_lds, const LdsOffsets& off,
+                                       int mt) {
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int base = off.vbase + 4096 * dt + 64 * (32 * mt + 16 * t);
+      const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(v_lds + base));
+      const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(v_lds + base + 64 * 8));
+      vf[2 * dt + t] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+}
+
+// max(a, b) for values that are never NaN, as one v_med3_f32 with no operand canonicalisation.
+__device__ __forceinline__ float max_nn(float a, float b) {
+  return __builtin_amdgcn_fmed3f(a, b, __builtin_huge_valf());
+}
+
+// S^T block = K Q^T for this wave's 32 query columns.
+__device__ __forceinline__ floatx16_t mma_scores(const bf16x8_t (&kf)[8], const bf16x8_t (&qf)[8]) {
   floatx16_t st;
 #pragma unroll
   for (int v = 0; v < 16; ++v) st[v] = 0.f;
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    const bf16x8_t a = __builtin_bit_cast(
-        bf16x8_t, *reinterpret_cast<const uint4*>(k_lds + off.kbase[ks & 1] + 4096 * (ks >> 1) + 2048 * mt));
-    st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], st, 0, 0, 0);
-  }
+  for (int ks = 0; ks < 8; ++ks) st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], st, 0, 0, 0);
   return st;
 }
 
-// Online-softmax update with one 32-key block and its P^T operands (two 16-key k-steps).
+// O^T += V^T P^T for one 32-key block.
+__device__ __forceinline__ void mma_pv(floatx16_t (&o)[4], const bf16x8_t (&vf)[8], const bf16x8_t (&pf)[2]) {
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[2 * dt + t], pf[t], o[dt], 0, 0, 0);
+}
+
+// New running max (log2 units) of the column after one block.  Accumulator element v is key
+// key0 + 8(v/4) + 4hk + v%4; with kMask, keys after the column's position become -inf.
 template <bool kMask>
-__device__ __forceinline__ void softmax_block(SoftmaxState& sm, floatx16_t& st, bf16x8_t (&pf)[2],
-                                              int key0, int hk, int qabs, float scale_log2) {
-  // Accumulator element v is key key0 + 8(v/4) + 4hk + v%4.
-  float smax = kNegInf;
+__device__ __forceinline__ float block_max(floatx16_t& st, float m, int key0, int hk, int qabs,
+                                           float scale_log2) {
+  if (kMask) {
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    float x = st[v];
-    if (kMask) {
+    for (int v = 0; v < 16; ++v) {
       const int key = key0 + 8 * (v >> 2) + 4 * hk + (v & 3);
-      x = key <= qabs ? x : kNegInf;
-      st[v] = x;
+      st[v] = key <= qabs ? st[v] : kNegInf;
     }
-    smax = fmaxf(smax, x);
   }
-  smax = max_xor32(smax);
-  // Exact running max, so the largest weight of a column is exactly 1 before its bf16 rounding
-  // (peaked softmaxes stay accurate); the output accumulators are rescaled only on the blocks
-  // where some column's max actually grew.
-  const float m_new = fmaxf(sm.m, smax * scale_log2);
-  if (__any(m_new > sm.m)) {
-    const float alpha = m_new == sm.m ? 1.f : fast_exp2(sm.m - m_new);
-    sm.l *= alpha;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) sm.o_acc[dt][v] *= alpha;
-  }
-  sm.m = m_new;
-  const float m_use = m_new == kNegInf ? 0.f : m_new;
-  float psum = 0.f;
+  // Balanced tree (depth 3 of 3-input maxima) instead of a 16-long chain.
+  const float a0 = fmaxf(fmaxf(st[0], st[1]), st[2]), a1 = fmaxf(fmaxf(st[3], st[4]), st[5]);
+  const float a2 = fmaxf(fmaxf(st[6], st[7]), st[8]), a3 = fmaxf(fmaxf(st[9], st[10]), st[11]);
+  const float a4 = fmaxf(fmaxf(st[12], st[13]), st[14]);
+  float smax = fmaxf(fmaxf(fmaxf(a0, a1), a2), fmaxf(fmaxf(a3, a4), st[15]));
+  float other = smax;
+  swap_halves(smax, other);
+  return max_nn(m, max_nn(smax, other) * scale_log2);
+}
+
+// P^T operands of one block (exp2 of the scaled scores minus the running max, rounded to bf16)
+// and the fp32 sum of the unrounded weights over this lane's keys.
+__device__ __forceinline__ float block_exp(const floatx16_t& st, float m_use, float scale_log2,
+                                           bf16x8_t (&pf)[2]) {
+  float part[4];  // four independent partial sums instead of one 16-long chain
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     uint32_t w[4];
@@ -185,46 +217,48 @@ __device__ __forceinline__ void softmax_block(SoftmaxState& sm, floatx16_t& st, 
     for (int j = 0; j < 4; ++j) {
       const float p0 = fast_exp2(fmaf(st[8 * t + 2 * j], scale_log2, -m_use));
       const float p1 = fast_exp2(fmaf(st[8 * t + 2 * j + 1], scale_log2, -m_use));
-      psum += p0 + p1;
+      part[j] = t == 0 ? p0 + p1 : part[j] + (p0 + p1);
       w[j] = pack_bf16x2(p0, p1);
     }
     pf[t] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
   }
-  sm.l += psum;
+  return (part[0] + part[1]) + (part[2] + part[3]);
 }
 
-// O^T += V^T P^T for 32-key block mt.  k-step t: this lane's 8 keys are 32mt + 16t + 4hk + {0..3}
-// and the same + 8, read transposed from the row-major V tile (two 8-byte reads per MFMA).
-__device__ __forceinline__ void accumulate_block(SoftmaxState& sm, const bf16x8_t (&pf)[2],
-                                                 const uint8_t* v_lds, const LdsOffsets& off,
-                                                 int mt) {
+// One software-pipelined step: the online softmax of block b (scores s_cur, already computed)
+// runs while the MFMA pipe works on the scores of block b+1 (s_next, from k_lds block mt_next;
+// skipped when kScore is false) and on O^T += V^T P^T of block b-1 (p_prev, with its V^T
+// fragments v_prev read one step earlier); meanwhile block b's V^T fragments (v_lds block mt_cur)
+// are read for the next step.  The running max stays exact; the output accumulators take block
+// b's rescale at the start of the next step, after block b-1's product has landed and before
+// block b's, and only when some column's max grew.  On return p_prev and v_prev hold block b.
+template <bool kMask, bool kScore>
+__device__ __forceinline__ void pipe_step(SoftmaxState& sm, floatx16_t& s_cur, floatx16_t& s_next,
+                                          bf16x8_t (&p_prev)[2], bf16x8_t (&v_prev)[8],
+                                          const bf16x8_t (&qf)[8], const uint8_t* k_lds, int mt_next,
+                                          const uint8_t* v_lds, int mt_cur, const LdsOffsets& off,
+                                          int key0, int hk, int qabs, float scale_log2) {
+  if (__any(sm.alpha != 1.f)) {
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) {
+    for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int base = off.vbase + 4096 * dt + 64 * (32 * mt + 16 * t);
-      const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(v_lds + base));
-      const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(v_lds + base + 64 * 8));
-      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      sm.o_acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[t], sm.o_acc[dt], 0, 0, 0);
-    }
+      for (int v = 0; v < 16; ++v) sm.o_acc[dt][v] *= sm.alpha;
   }
-}
-
-// One 64-key tile as two 32-key blocks (S^T, softmax, O^T update each); the two waves sharing a
-// SIMD interleave their MFMA and VALU phases.
-template <bool kMask>
-__device__ __forceinline__ void compute_tile(SoftmaxState& sm, const bf16x8_t (&qf)[8],
-                                             const uint8_t* k_lds, const uint8_t* v_lds,
-                                             const LdsOffsets& off, int kt, int hk, int qabs,
-                                             float scale_log2) {
-  bf16x8_t p0[2], p1[2];
-  floatx16_t s0 = scores(qf, k_lds, off, 0);
-  softmax_block<kMask>(sm, s0, p0, kt * kBK, hk, qabs, scale_log2);
-  accumulate_block(sm, p0, v_lds, off, 0);
-  floatx16_t s1 = scores(qf, k_lds, off, 1);
-  softmax_block<kMask>(sm, s1, p1, kt * kBK + 32, hk, qabs, scale_log2);
-  accumulate_block(sm, p1, v_lds, off, 1);
+  bf16x8_t kf[8], vf[8];
+  if (kScore) load_k(kf, k_lds, off, mt_next);
+  const float m_new = block_max<kMask>(s_cur, sm.m, key0, hk, qabs, scale_log2);
+  if (kScore) s_next = mma_scores(kf, qf);
+  mma_pv(sm.o_acc, v_prev, p_prev);
+  load_v(vf, v_lds, off, mt_cur);
+  const float psum = block_exp(s_cur, m_new, scale_log2, p_prev);
+  sm.alpha = fast_exp2(sm.m - m_new);  // exactly 1 when the max did not move
+  sm.l = fmaf(sm.l, sm.alpha, psum);
+  sm.m = m_new;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v_prev[i] = vf[i];
+  // Keep block b's softmax in this step, beside the MFMAs it is meant to overlap.
+  asm volatile("" ::"v"(p_prev[0]), "v"(p_prev[1]), "v"(sm.l), "v"(sm.alpha));
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 __global__ __launch_bounds__(512, 1) void prefill_kernel(
@@ -232,12 +266,16 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
     const uint16_t* __restrict__ q, int chunk_len, int prefix_len,
     const int32_t* __restrict__ block_table, float scale_log2, float* __restrict__ out,
     float* __restrict__ lse, int n_qtiles) {
-  // Two stages of (K, V) tiles, 64 KiB.  Separate arrays, so the compiler can see that the DMA
-  // into one stage never aliases the reads of the other and adds no wait of its own between them.
+  // Three stages of (K, V) tiles, 96 KiB: the tile being read, the next tile (in flight, then
+  // read from the middle of the current step on) and the stage the following DMA refills.
+  // Separate arrays, so the compiler can see that the DMA into one stage never aliases the reads
+  // of another and adds no wait of its own between them.
   __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t v_lds0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t k_lds1[kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t v_lds1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t k_lds2[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t v_lds2[kTileBytes];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -259,9 +297,12 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
   const int n_plain = min((prefix_len + q0 + 1) / kBK, n_tiles);
   const TileArgs ta{k_pages, v_pages, block_table, num_pages, g, total, wave, lane, n_tiles};
 
-  // Tiles 0 and 1 in flight before anything else.
   issue_tile(ta, 0, tile_page(ta, 0), k_lds0, v_lds0);
   int next_page = tile_page(ta, 1);
+  // Stage 2's V starts as zeros: the first step multiplies it by an all-zero P^T in place of a
+  // previous block.
+  *reinterpret_cast<uint4*>(v_lds2 + 32 * tid) = make_uint4(0, 0, 0, 0);
+  *reinterpret_cast<uint4*>(v_lds2 + 32 * tid + 16) = make_uint4(0, 0, 0, 0);
 
   // Q^T fragments: k-step ks covers dims 16ks..16ks+15; this lane holds dims 16ks+8hk..+7.
   bf16x8_t qf[8];
@@ -281,33 +322,77 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int v = 0; v < 16; ++v) sm.o_acc[dt][v] = 0.f;
-  sm.m = kNegInf;
+  sm.m = kMaxFloor;
   sm.l = 0.f;
+  sm.alpha = 1.f;
 
-  // Tile kt lives in stage kt % 2.  At the top of tile kt: wait for this wave's DMAs of tile kt,
-  // barrier (everyone's DMAs of tile kt visible, everyone done with tile kt-1), start tile kt+1's
-  // DMA into the stage tile kt-1 used, compute tile kt.  Main loop: two tiles per trip with
-  // compile-time stages, none of them reaching the workgroup's first query (no causal mask).
-  // Tail: the rest, masked.
-#define MTD_PREFILL_STEP(KT, CUR_K, CUR_V, NXT_K, NXT_V, MASK)                          \
-  {                                                                                     \
-    wait_dma();                                                                         \
-    tile_barrier();                                                                     \
-    if ((KT) + 1 < n_tiles) issue_tile(ta, (KT) + 1, next_page, NXT_K, NXT_V);          \
-    next_page = tile_page(ta, (KT) + 2);                                                \
-    compute_tile<MASK>(sm, qf, CUR_K, CUR_V, off, (KT), hk, qabs, scale_log2);          \
+  wait_dma();
+  __syncthreads();
+  if (1 < n_tiles) issue_tile(ta, 1, next_page, k_lds1, v_lds1);
+  next_page = tile_page(ta, 2);
+  floatx16_t s_a, s_b;
+  bf16x8_t p_prev[2], v_prev[8];
+  load_v(v_prev, v_lds2, off, 1);  // zeros: stands in for the V^T of block -1
+  {
+    bf16x8_t kf[8];
+    load_k(kf, k_lds0, off, 0);
+    s_a = mma_scores(kf, qf);
+    const bf16x8_t zero = __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
+    p_prev[0] = zero;
+    p_prev[1] = zero;
   }
+
+  // Tile kt lives in stage kt % 3.  Step kt: first half = softmax of block 2kt beside the scores
+  // of block 2kt+1 and the O update of block 2kt-1, reading block 2kt's V^T; then wait for tile
+  // kt+1's DMA and barrier (everyone is done with tile kt-1's stage), start tile kt+2's DMA into
+  // that stage; second half = softmax of block 2kt+1 beside the scores of block 2kt+2 (next
+  // stage) and the O update of block 2kt, reading block 2kt+1's V^T.  Main loop: three steps per
+  // trip with compile-time stages, no causal mask, never the last tile.  Then the remaining
+  // steps with run-time stages (masked) and the last tile, then block 2n-1's O update.
+#define MTD_PREFILL_STEP(KT, CUR_K, CUR_V, PRV_V, NXT_K, PRV_K, MASK)                         \
+  {                                                                                           \
+    pipe_step<MASK, true>(sm, s_a, s_b, p_prev, v_prev, qf, CUR_K, 1, CUR_V, 0, off,          \
+                          (KT) * kBK, hk, qabs, scale_log2);                                  \
+    wait_dma();                                                                               \
+    tile_barrier();                                                                           \
+    if ((KT) + 2 < n_tiles) issue_tile(ta, (KT) + 2, next_page, PRV_K, PRV_V);                \
+    next_page = tile_page(ta, (KT) + 3);                                                      \
+    pipe_step<MASK, true>(sm, s_b, s_a, p_prev, v_prev, qf, NXT_K, 0, CUR_V, 1, off,          \
+                          (KT) * kBK + 32, hk, qabs, scale_log2);                             \
+  }
+  const int n_main = min(n_plain, n_tiles - 1);
   int kt = 0;
-  for (; kt + 1 < n_plain; kt += 2) {
-    MTD_PREFILL_STEP(kt, k_lds0, v_lds0, k_lds1, v_lds1, false)
-    MTD_PREFILL_STEP(kt + 1, k_lds1, v_lds1, k_lds0, v_lds0, false)
+  for (; kt + 3 <= n_main; kt += 3) {
+    MTD_PREFILL_STEP(kt, k_lds0, v_lds0, v_lds2, k_lds1, k_lds2, false)
+    MTD_PREFILL_STEP(kt + 1, k_lds1, v_lds1, v_lds0, k_lds2, k_lds0, false)
+    MTD_PREFILL_STEP(kt + 2, k_lds2, v_lds2, v_lds1, k_lds0, k_lds1, false)
   }
-  for (; kt < n_tiles; ++kt) {
-    const bool odd = kt & 1;
-    MTD_PREFILL_STEP(kt, odd ? k_lds1 : k_lds0, odd ? v_lds1 : v_lds0, odd ? k_lds0 : k_lds1,
-                     odd ? v_lds0 : v_lds1, true)
+  for (; kt < n_tiles - 1; ++kt) {
+    const int sc = kt % 3;
+    uint8_t* ck = sc == 0 ? k_lds0 : sc == 1 ? k_lds1 : k_lds2;
+    uint8_t* cv = sc == 0 ? v_lds0 : sc == 1 ? v_lds1 : v_lds2;
+    uint8_t* nk = sc == 0 ? k_lds1 : sc == 1 ? k_lds2 : k_lds0;
+    uint8_t* pk = sc == 0 ? k_lds2 : sc == 1 ? k_lds0 : k_lds1;
+    uint8_t* pv = sc == 0 ? v_lds2 : sc == 1 ? v_lds0 : v_lds1;
+    MTD_PREFILL_STEP(kt, ck, cv, pv, nk, pk, true)
   }
 #undef MTD_PREFILL_STEP
+  {
+    const int sc = kt % 3;
+    const uint8_t* ck = sc == 0 ? k_lds0 : sc == 1 ? k_lds1 : k_lds2;
+    const uint8_t* cv = sc == 0 ? v_lds0 : sc == 1 ? v_lds1 : v_lds2;
+    pipe_step<true, true>(sm, s_a, s_b, p_prev, v_prev, qf, ck, 1, cv, 0, off, kt * kBK, hk, qabs,
+                          scale_log2);
+    pipe_step<true, false>(sm, s_b, s_a, p_prev, v_prev, qf, ck, 0, cv, 1, off, kt * kBK + 32, hk,
+                           qabs, scale_log2);
+    if (__any(sm.alpha != 1.f)) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sm.o_acc[dt][v] *= sm.alpha;
+    }
+    mma_pv(sm.o_acc, v_prev, p_prev);
+  }
 
   const float l_tot = sum_xor32(sm.l);
   if (qvalid) {
