@@ -485,7 +485,183 @@ class FullDepth:
                           f"KV tokens, {t_dec:.1f} s); fp64 numpy"}
 
 
-WORKLOAD_CLASSES = {c.name: c for c in (MixedStep, Decode16, Prefill90, FullDepth)}
+class MixedStepOverlap(MixedStep):
+    """The mixed step with the decode on a second stream (default priority), so it can fill CUs the
+    prefill leaves idle: the append first, then the prefill on the library's stream and the decode
+    on the second one, joined before the next step.  Outputs are bit-identical to the sequential
+    step; per-kernel times here include the contention between the two."""
+    name = "mixed_step_overlap"
+
+    def __init__(self, dev):
+        super().__init__(dev)
+        torch = self.torch
+        self.side = torch.cuda.Stream(device=dev)
+        self.appended, self.decoded = torch.cuda.Event(), torch.cuda.Event()
+        self.timer = OverlapTimer()
+
+    def step(self, events=None):
+        mtd, torch = self.mtd, self.torch
+        main = torch.cuda.current_stream()
+        if events: events[0].record()
+        mtd.mtd_kv_append(self.k, self.v, self.k_new, self.v_new, self.cu, self.start, self.bt_all)
+        if events: events[1].record()
+        self.appended.record(main)
+        mtd.mtd_attn_prefill_chunk(self.k, self.v, self.q_a, self.prefix, self.bt_a, W.SCALE, self.o_a, self.l_a)
+        if events: events[2].record()
+        self.side.wait_event(self.appended)
+        with torch.cuda.stream(self.side):
+            if events: events[3].record()
+            mtd.mtd_attn_decode(self.k, self.v, self.q_d, self.kv_lens, self.bt_dec, self.max_len, W.SCALE,
+                                self.ws, self.o_d, self.l_d)
+            if events: events[4].record()
+            self.decoded.record()
+        main.wait_event(self.decoded)
+
+    def config(self):
+        c = super().config()
+        c["workload"] = "mixed_step_overlap: " + c["workload"].split(": ", 1)[1] + "; decode on a second stream"
+        return c
+
+    cpu_baseline = None
+
+
+class OverlapTimer(Timer):
+    """append and prefill events on the library's stream, decode events on the second stream."""
+
+    def __init__(self):
+        super().__init__(["append", "prefill", "decode"])
+
+    def step_events(self):
+        return [self.torch.cuda.Event(enable_timing=True) for _ in range(5)]
+
+    def collect(self, events):
+        self.samples["append"].append(events[0].elapsed_time(events[1]))
+        self.samples["prefill"].append(events[1].elapsed_time(events[2]))
+        self.samples["decode"].append(events[3].elapsed_time(events[4]))
+
+
+class DecodeGraph:
+    """Launch-bound decode: one request with the tiny workload's context (439 tokens and growing)
+    through 28 layers; a step is 28 x (append its new token, decode).  The same step is timed as
+    eager library calls and as one replay of a captured HIP graph (decode at concurrency 1 is where
+    graph capture pays off)."""
+    name = "decode_graph"
+    SLOTS = 8      # rotating input sets; one captured graph per set
+    LAYERS = 28
+    ROOM = 4096    # tokens the request may grow by during one timed pass
+
+    def __init__(self, dev):
+        import torch
+        import gqa_kv_cache_qwen3_amd as mtd
+        self.mtd, self.torch = mtd, torch
+        self.l0 = W.TINY.params["prompt"]
+        tables, n_pages, _ = W.place_pages([self.l0 + self.ROOM], W.TINY.tag, 1)
+        self.bt = torch.as_tensor(tables, device=dev)
+        self.k = [torch.empty((n_pages, W.HKV, W.PAGE, W.HEAD_DIM), dtype=torch.bfloat16, device=dev)
+                  for _ in range(self.LAYERS)]
+        self.v = [torch.empty_like(t) for t in self.k]
+        for l in range(self.LAYERS):
+            fill_normal_(self.k[l], W.torch_seed(W.TINY.tag, 60, l))
+            fill_normal_(self.v[l], W.torch_seed(W.TINY.tag, 61, l))
+        shape_q, shape_kv = (self.SLOTS, self.LAYERS, 1, W.HQ, W.HEAD_DIM), (self.SLOTS, self.LAYERS, 1, W.HKV, W.HEAD_DIM)
+        self.q = W.normal_bf16(shape_q, W.torch_seed(W.TINY.tag, 62), dev)
+        self.k_new = W.normal_bf16(shape_kv, W.torch_seed(W.TINY.tag, 63), dev)
+        self.v_new = W.normal_bf16(shape_kv, W.torch_seed(W.TINY.tag, 64), dev)
+        self.cu = torch.arange(2, dtype=torch.int32, device=dev)
+        self.pos = torch.zeros(1, dtype=torch.int32, device=dev)   # where this step's token goes
+        self.len = torch.zeros(1, dtype=torch.int32, device=dev)   # KV length after the append
+        self.max_len = self.l0 + self.ROOM
+        self.ws = torch.empty(mtd.decode_workspace_bytes(1, self.max_len), dtype=torch.uint8, device=dev)
+        self.o = torch.empty((self.LAYERS, 1, W.HQ, W.HEAD_DIM), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((self.LAYERS, 1, W.HQ), dtype=torch.float32, device=dev)
+        self.graphs = []
+        torch.cuda.synchronize()
+        for r in range(self.SLOTS):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self._calls(r)
+            self.graphs.append(g)
+        torch.cuda.synchronize()
+        self.samples = {"eager_ms": None, "graph_ms": None, "decode_call_ms": []}
+        self.n_steps = 0
+
+    def _calls(self, r, events=None):
+        mtd = self.mtd
+        for l in range(self.LAYERS):
+            mtd.mtd_kv_append(self.k[l], self.v[l], self.k_new[r, l], self.v_new[r, l], self.cu, self.pos, self.bt)
+            if events is not None: events[l][0].record()
+            mtd.mtd_attn_decode(self.k[l], self.v[l], self.q[r, l], self.len, self.bt, self.max_len, W.SCALE,
+                                self.ws, self.o[l], self.lse[l])
+            if events is not None: events[l][1].record()
+        self.pos.add_(1)
+        self.len.add_(1)
+
+    def _reset(self):
+        self.pos.fill_(self.l0)
+        self.len.fill_(self.l0 + 1)
+
+    def _pass(self, n, graph, events=None):
+        for s in range(n):
+            if graph:
+                self.graphs[s % self.SLOTS].replay()
+            else:
+                ev = None
+                if events is not None:
+                    ev = [[self.torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(self.LAYERS)]
+                    events.append(ev)
+                self._calls(s % self.SLOTS, ev)
+
+    def run(self, steps, warmup):
+        """Eager and graph passes of `steps` steps each, after `warmup` untimed steps of each mode.
+        Returns the graph pass's wall seconds; the eager wall time and per-call decode kernel times
+        (HIP events, from a third, eager pass) go into the results."""
+        torch = self.torch
+        if steps > self.ROOM:
+            raise SystemExit(f"--steps {steps} exceeds the {self.ROOM} tokens of room per pass")
+        walls = {}
+        for graph in (False, True):
+            self._reset()
+            self._pass(min(warmup, self.ROOM), graph)
+            self._reset()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            self._pass(steps, graph)
+            torch.cuda.synchronize()
+            walls[graph] = time.perf_counter() - t0
+        self._reset()
+        events = []
+        self._pass(steps, False, events)
+        torch.cuda.synchronize()
+        self.samples["decode_call_ms"] = [e[0].elapsed_time(e[1]) for ev in events for e in ev]
+        self.samples["eager_ms"] = walls[False] * 1e3 / steps
+        self.samples["graph_ms"] = walls[True] * 1e3 / steps
+        self.n_steps = steps
+        return walls[True]
+
+    def config(self):
+        return {"workload": "decode_graph: 1 request (439-token context growing by one token per step) through "
+                            "28 layers; step = 28 x (append 1 token, decode); eager calls vs one HIP-graph replay",
+                "layers": self.LAYERS, "batch": 1, "initial_kv_tokens": self.l0}
+
+    def results(self):
+        n = self.n_steps
+        lens = self.l0 + 1 + np.arange(n)
+        step_bytes = float(np.mean([self.LAYERS * decode_bytes([x]) for x in lens]))
+        call_ms = float(np.mean(self.samples["decode_call_ms"]))
+        call_gbs = (step_bytes / self.LAYERS) / (call_ms * 1e-3) / 1e9
+        g, e = self.samples["graph_ms"], self.samples["eager_ms"]
+        return {"decode": {"value": call_gbs, "unit": "GB/s", "frac": call_gbs / HBM_PEAK_GBS, "ms": call_ms,
+                           "bytes": step_bytes / self.LAYERS,
+                           "kernels": "decode_split_kernel + decode_merge_kernel (per layer call, eager pass)"},
+                "step": {"eager_ms": e, "graph_ms": g, "graph_speedup": e / g,
+                         "graph_step_gbs": step_bytes / (g * 1e-3) / 1e9, "launches_per_step": 3 * self.LAYERS + 2}}
+
+    def dominant(self, res):
+        return {"kernel": "decode_split_kernel+decode_merge_kernel", "bound": "hbm", "achieved": res["decode"]["value"],
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "per_launch": res["decode"]["bytes"], "ms": res["decode"]["ms"]}
+
+
+WORKLOAD_CLASSES = {c.name: c for c in (MixedStep, MixedStepOverlap, Decode16, Prefill90, FullDepth, DecodeGraph)}
 
 
 def blas_threads() -> int:
@@ -512,7 +688,8 @@ def calibrate_copy():
 
 
 # Untimed steps per workload, each about 50 ms of GPU work or more.
-WARMUP_DEFAULT = {"mixed_step": 40, "decode16": 500, "prefill90min": 3, "fulldepth_decode": 5}
+WARMUP_DEFAULT = {"mixed_step": 40, "mixed_step_overlap": 40, "decode16": 500, "prefill90min": 3,
+                  "fulldepth_decode": 5, "decode_graph": 200}
 
 
 def main():
@@ -532,7 +709,7 @@ def main():
         return
 
     if args.steps is None:
-        args.steps = 128 if args.workload == "fulldepth_decode" else 20
+        args.steps = {"fulldepth_decode": 128, "decode_graph": 500}.get(args.workload, 20)
     if args.warmup is None:
         # From idle the shader clock needs about 20 ms of sustained work to reach its steady level
         # (measured on MI355X); the default warmup covers that with margin.
@@ -550,15 +727,18 @@ def main():
 
     wl = WORKLOAD_CLASSES[args.workload](dev)
     torch.cuda.synchronize()
-    for _ in range(args.warmup):
-        wl.step()
+    if not isinstance(wl, DecodeGraph):
+        for _ in range(args.warmup):
+            wl.step()
     torch.cuda.synchronize()
     if isinstance(wl, FullDepth):
         wl.step_idx = 0  # the timed pass starts again at step 0 (appends rewrite the same slots)
 
     # timed region: exactly K steps between synchronisations; per-call events inside
     t0 = time.perf_counter()
-    if isinstance(wl, FullDepth):
+    if isinstance(wl, DecodeGraph):
+        wall = wl.run(args.steps, args.warmup)  # warm-up and the eager passes happen inside; graph pass timed
+    elif isinstance(wl, FullDepth):
         step_events = []
         for _ in range(args.steps):
             wl.step(step_events)
@@ -615,10 +795,10 @@ def main():
             "per_launch": dom["per_launch"], "source_digest": source_digest(dom["kernel"]),
         },
     }
-    for k in ("decode", "prefill", "append"):
+    for k in ("decode", "prefill", "append", "step"):
         if k in res:
             line[k] = {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in res[k].items()}
-    if not args.no_cpu_baseline and hasattr(wl, "cpu_baseline"):
+    if not args.no_cpu_baseline and getattr(wl, "cpu_baseline", None) is not None:
         line["cpu_baseline"] = wl.cpu_baseline(args.cpu_budget)
     print(json.dumps(line), flush=True)
 

@@ -8,9 +8,10 @@
 // off the memory critical path.
 //
 // decode_split: one wavefront per work item = (request b, split s, KV head g), where split s is
-//   the logical tokens [512 s, min(512 s + 512, L_b)).  Items are numbered densely: the flat split
-//   index f counts the splits of requests 0..b-1 first (ceil(L/512) each), so the grid is
-//   8 * sum_b ceil(L_b / 512) waves plus a tail of waves that find f beyond the total and exit.
+//   the logical tokens [T s, min(T s + T, L_b)) with T = split_tokens(L_b) (64 to 512 tokens, by
+//   length).  Items are numbered densely: the flat split index f counts the splits of requests
+//   0..b-1 first, so the grid is 8 * sum_b split_parts(L_b) waves plus a tail of waves that find f
+//   beyond the total and exit.
 //   Both query heads of the GQA group (2g, 2g+1) are served from the same K/V loads.  The wave
 //   writes the split's normalised partial output and its log-sum-exp.
 // decode_merge: one workgroup per (request, query head) combines that request's partials with
@@ -47,7 +48,7 @@ __device__ __forceinline__ bool locate_split(const int32_t* __restrict__ kv_lens
     const int idx = c0 + lane;
     int len = idx < batch ? kv_lens[idx] : 0;
     len = min(max(len, 0), max_kv_len);
-    const int n = (len + kSplit - 1) / kSplit;
+    const int n = split_parts(len);
     const int incl = wave_incl_scan(n, lane);
     const int chunk_total = __shfl(incl, 63, 64);
     if (f < carry + chunk_total) {
@@ -96,8 +97,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[hh][c][e] = 0.f;
 
-  const int tok0 = s * kSplit;
-  const int tok1 = min(tok0 + kSplit, len);
+  const int tok0 = s * split_tokens(len);
+  const int tok1 = min(tok0 + split_tokens(len), len);
   const int32_t* bt_row = block_tables + (size_t)b * bt_stride;
 
   for (int e0 = tok0 / kPage; e0 * kPage < tok1; ++e0) {
@@ -240,8 +241,6 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
 // w_s = exp(lse_s - LSE) go to LDS; then 16 lane groups of 16 lanes each take every 16th partial
 // (a lane covers 8 dims with two 16-byte loads), so all partial rows of the request are in flight
 // at once instead of one after another; the 16 group sums are added in LDS.
-constexpr int kMaxParts = kMaxContext / kSplit;  // partials of one request
-
 __global__ __launch_bounds__(256) void decode_merge_kernel(
     const int32_t* __restrict__ kv_lens, int batch, int max_kv_len,
     const float* __restrict__ part_o, const float* __restrict__ part_lse, float* __restrict__ out,
@@ -257,13 +256,13 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
   const int b = blockIdx.x / kQHeads;
 
   if (wave == 0) {
-    // first flat split of request b = sum over earlier requests of ceil(L / 512)
+    // first flat split of request b = sum over earlier requests of their split counts
     int first = 0, len = 0;
     for (int c0 = 0; c0 <= b; c0 += 64) {
       const int idx = c0 + lane;
       int ln = idx < batch ? kv_lens[idx] : 0;
       ln = min(max(ln, 0), max_kv_len);
-      const int n = (ln + kSplit - 1) / kSplit;
+      const int n = split_parts(ln);
       if (b < c0 + 64) {
         first += wave_sum_int(idx < b ? n : 0);
         len = __shfl(ln, b - c0, 64);
@@ -273,7 +272,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
     }
     if (lane == 0) {
       s_first = first;
-      s_n = (len + kSplit - 1) / kSplit;
+      s_n = split_parts(len);
     }
   }
   __syncthreads();
@@ -338,14 +337,14 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
 }  // namespace
 
 size_t decode_workspace_bytes(int batch, int max_kv_len) {
-  const size_t parts = (size_t)batch * (size_t)((max_kv_len + kSplit - 1) / kSplit);
+  const size_t parts = (size_t)batch * (size_t)split_parts_bound(max_kv_len);
   return parts * kQHeads * (kHeadDim + 1) * sizeof(float);
 }
 
 hipError_t launch_decode(const KvPools& kv, const uint16_t* q, const int32_t* kv_lens,
                          const int32_t* block_tables, int bt_stride, int batch, int max_kv_len,
                          float scale, void* workspace, float* out, float* lse, hipStream_t stream) {
-  const size_t parts = (size_t)batch * (size_t)((max_kv_len + kSplit - 1) / kSplit);
+  const size_t parts = (size_t)batch * (size_t)split_parts_bound(max_kv_len);
   float* part_o = static_cast<float*>(workspace);
   float* part_lse = part_o + parts * kQHeads * kHeadDim;
   const unsigned n_waves = (unsigned)(parts * kKvHeads);

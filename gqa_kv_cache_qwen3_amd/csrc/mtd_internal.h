@@ -14,9 +14,26 @@ constexpr int kGroup = kQHeads / kKvHeads;  // query heads per KV head
 constexpr int kHeadDim = 128;
 constexpr int kPage = 64;
 constexpr int kMaxContext = 131072;
-// Decode split-K partition: 512 logical tokens (8 pages).  Partition boundaries are fixed in
-// logical token space, so a request's result never depends on the batch or on page placement.
-constexpr int kSplit = 512;
+// Decode split-K partition of a request of len tokens: consecutive runs of split_tokens(len)
+// logical tokens (whole pages).  A request of up to 1024 tokens is cut into one split per page
+// (up to 16), so even a lone short request spreads over many wavefronts; longer ones use 512-token
+// splits, where the per-split costs (query load, partial write, merge) stay under 1 % of the K/V
+// bytes and a large batch streams at full rate.  The partition depends only on the request's own
+// length, in logical token space, so a request's result never depends on the batch or on page
+// placement.
+__host__ __device__ constexpr int split_tokens(int len) { return len <= 1024 ? 64 : 512; }
+__host__ __device__ constexpr int split_parts(int len) {
+  return len <= 0 ? 0 : (len + split_tokens(len) - 1) / split_tokens(len);
+}
+// Most partials one request can have (131072 tokens in 512-token splits).
+constexpr int kMaxParts = split_parts(kMaxContext);
+// Most partials any request of at most max_len tokens can have: split_parts rises within each
+// length band and drops where the split grows, so the maximum sits at a band's upper end.
+__host__ __device__ constexpr int split_parts_bound(int max_len) {
+  const int a = split_parts(max_len < 1024 ? max_len : 1024);
+  const int b = split_parts(max_len);
+  return a > b ? a : b;
+}
 
 struct KvPools {
   uint16_t* k;
@@ -35,7 +52,7 @@ hipError_t launch_prefill(const KvPools& kv, const uint16_t* q, int chunk_len, i
                           hipStream_t stream);
 
 // Workspace layout of the decode: partial O float32 [max_parts][kQHeads][kHeadDim], then partial
-// LSE float32 [max_parts][kQHeads], max_parts = batch * ceil(max_kv_len / kSplit).
+// LSE float32 [max_parts][kQHeads], max_parts = batch * split_parts_bound(max_kv_len).
 size_t decode_workspace_bytes(int batch, int max_kv_len);
 
 hipError_t launch_decode(const KvPools& kv, const uint16_t* q, const int32_t* kv_lens,

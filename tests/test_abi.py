@@ -6,6 +6,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -176,11 +177,26 @@ def test_decode_validation(lib, kw, code):
     assert decode(lib, layer(), **kw) == code
 
 
+def _split_tokens(n):
+    # the documented partition: 64-token runs up to 1024 tokens, else 512
+    return 64 if n <= 1024 else 512
+
+
+# most partials of any length 1..M, by brute force over every length
+_RUNS = np.array([0] + [-(-n // _split_tokens(n)) for n in range(1, 131073)])
+_MAX_RUNS = np.maximum.accumulate(_RUNS)
+
+
 def test_workspace_size_formula(lib):
-    # partials: batch * ceil(max_kv_len / 512) splits, each 16 heads x (128 + 1) floats
-    for batch, max_len in [(1, 1), (1, 512), (1, 513), (16, 30000), (64, 131072)]:
-        parts = batch * ((max_len + 511) // 512)
-        assert lib.mtd_attn_decode_workspace_bytes(batch, 16, max_len, 128) == parts * 16 * 129 * 4
+    # partials: batch * (most runs of any request of <= max_kv_len tokens), 16 heads x (128 + 1) floats
+    for batch, max_len in [(1, 1), (1, 64), (1, 65), (1, 439), (1, 1024), (1, 1025), (1, 2048), (2, 2049),
+                           (1, 4096), (1, 4097), (3, 6000), (1, 8192), (2, 8193), (1, 8705), (16, 30000),
+                           (31, 68000), (64, 131072)]:
+        parts = batch * int(_MAX_RUNS[max_len])
+        assert lib.mtd_attn_decode_workspace_bytes(batch, 16, max_len, 128) == parts * 16 * 129 * 4, (batch, max_len)
+    # every bound from 1 to 131072 tokens, at batch 1
+    got = np.array([lib.mtd_attn_decode_workspace_bytes(1, 16, m, 128) for m in range(1, 131073, 7)])
+    assert np.array_equal(got, _MAX_RUNS[1:131073:7] * 16 * 129 * 4)
     assert lib.mtd_attn_decode_workspace_bytes(0, 16, 100, 128) == 0
     assert lib.mtd_attn_decode_workspace_bytes(1, 16, 0, 128) == 0
     assert lib.mtd_attn_decode_workspace_bytes(1, 16, 131073, 128) == 0

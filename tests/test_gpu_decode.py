@@ -24,13 +24,32 @@ def run(batch: DecodeBatch, max_len=None, ws=None):
 
 
 def test_decode_ragged_small():
-    """Lengths around page (64) and split (512) boundaries, one token, several pages."""
+    """Lengths around page (64) and split boundaries, one token, several pages."""
     lens = [1, 2, 63, 64, 65, 127, 511, 512, 513, 1000, 1025, 1536, 2049]
     log(f"decode ragged small lens={lens}")
     batch = DecodeBatch(lens, 101)
     out, lse = run(batch)
     o_ref, l_ref = batch.reference()
     compare(out, lse, o_ref, l_ref, "decode ragged small")
+
+
+def test_decode_split_bands():
+    """Lengths on both sides of the change of split size (64 to 512 tokens) and of 512-token split
+    boundaries, in one batch."""
+    lens = [960, 1023, 1024, 1025, 1300, 1536, 1537, 2048, 2049, 3000, 4096, 4097, 4609, 9000]
+    log(f"decode split bands lens={lens}")
+    batch = DecodeBatch(lens, 104)
+    out, lse = run(batch)
+    o_ref, l_ref = batch.reference()
+    compare(out, lse, o_ref, l_ref, "decode split bands")
+    # a request's split depends on its own length only: a sub-batch (other order, other bound)
+    # gives the same bits
+    sub = [13, 0, 5, 9]
+    idx = torch.tensor(sub, device="cuda")
+    out2, lse2 = mtd.mtd_attn_decode(batch.k, batch.v, batch.q[idx].contiguous(), batch.kv_lens[idx].contiguous(),
+                                     batch.bt[idx].contiguous(), int(max(lens[i] for i in sub)), W.SCALE)
+    torch.cuda.synchronize()
+    assert torch.equal(out2, out[idx]) and torch.equal(lse2, lse[idx])
 
 
 def test_decode_max_len_above_longest():

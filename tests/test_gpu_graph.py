@@ -1,0 +1,123 @@
+"""The library's calls captured in a HIP graph (torch.cuda.CUDAGraph, on the capture stream torch
+makes current) and replayed.
+
+Every replay must reproduce the same calls made eagerly on a twin pool bit for bit, with eager
+work (the copies that stage each step's inputs) and synchronisations between replays; the last
+step is also checked against the fp64 oracle.  Capture records only kernel launches: the calls
+allocate nothing, set no memory and never synchronise, so the graph holds the same kernels the
+eager calls run."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_common import bits, compare, log, new_pool, request_pages_host
+
+pytestmark = pytest.mark.gpu
+
+mtd = pytest.importorskip("gqa_kv_cache_qwen3_amd")
+
+
+def _i32(values):
+    return torch.as_tensor(np.asarray(values, dtype=np.int32), device="cuda")
+
+
+class StepGraph:
+    """Fixed input/output buffers for `layers` x (append one token per request, decode) over one
+    block table, the graph that reads them, and an eager twin of the same pools."""
+
+    def __init__(self, lens0, steps, layers, tag):
+        self.lens0 = np.asarray(lens0, dtype=np.int64)
+        self.steps, self.layers = steps, layers
+        b = len(self.lens0)
+        self.tables, n_pages, _ = W.place_pages(self.lens0 + steps, tag, 0)
+        self.bt = torch.as_tensor(self.tables, device="cuda")
+        self.max_len = int(self.lens0.max()) + steps
+        # every slot holds N(0,1) data, so positions below lens0 act as the prompt already cached
+        self.kg = [new_pool(n_pages, "cuda", W.torch_seed(tag, 40, l)) for l in range(layers)]
+        self.vg = [new_pool(n_pages, "cuda", W.torch_seed(tag, 41, l)) for l in range(layers)]
+        self.ke = [p.clone() for p in self.kg]
+        self.ve = [p.clone() for p in self.vg]
+        self.q_all = W.normal_bf16((steps, layers, b, W.HQ, W.HEAD_DIM), W.torch_seed(tag, 42), "cuda")
+        self.k_all = W.normal_bf16((steps, layers, b, W.HKV, W.HEAD_DIM), W.torch_seed(tag, 43), "cuda")
+        self.v_all = W.normal_bf16((steps, layers, b, W.HKV, W.HEAD_DIM), W.torch_seed(tag, 44), "cuda")
+        self.cu = _i32(np.arange(b + 1))
+        self.ws = torch.empty(mtd.decode_workspace_bytes(b, self.max_len), dtype=torch.uint8, device="cuda")
+        self.ws_e = torch.empty_like(self.ws)
+        # the buffers the graph reads and writes
+        self.q_buf = torch.empty_like(self.q_all[0])
+        self.k_buf = torch.empty_like(self.k_all[0])
+        self.v_buf = torch.empty_like(self.v_all[0])
+        self.start_buf = torch.zeros(b, dtype=torch.int32, device="cuda")
+        self.len_buf = torch.zeros(b, dtype=torch.int32, device="cuda")
+        self.o_buf = torch.empty((layers, b, W.HQ, W.HEAD_DIM), dtype=torch.float32, device="cuda")
+        self.l_buf = torch.empty((layers, b, W.HQ), dtype=torch.float32, device="cuda")
+        self.graph = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(self.graph):
+            for l in range(layers):
+                mtd.mtd_kv_append(self.kg[l], self.vg[l], self.k_buf[l], self.v_buf[l], self.cu,
+                                  self.start_buf, self.bt)
+                mtd.mtd_attn_decode(self.kg[l], self.vg[l], self.q_buf[l], self.len_buf, self.bt,
+                                    self.max_len, W.SCALE, self.ws, self.o_buf[l], self.l_buf[l])
+        torch.cuda.synchronize()
+
+    def replay_step(self, s):
+        """Stage step s's inputs into the fixed buffers (eager copies), replay the graph."""
+        self.q_buf.copy_(self.q_all[s])
+        self.k_buf.copy_(self.k_all[s])
+        self.v_buf.copy_(self.v_all[s])
+        self.start_buf.copy_(_i32(self.lens0 + s))
+        self.len_buf.copy_(_i32(self.lens0 + s + 1))
+        self.graph.replay()
+
+    def eager_step(self, s):
+        start, kv_lens = _i32(self.lens0 + s), _i32(self.lens0 + s + 1)
+        outs = []
+        for l in range(self.layers):
+            mtd.mtd_kv_append(self.ke[l], self.ve[l], self.k_all[s, l], self.v_all[s, l], self.cu, start, self.bt)
+            outs.append(mtd.mtd_attn_decode(self.ke[l], self.ve[l], self.q_all[s, l], kv_lens, self.bt,
+                                            self.max_len, W.SCALE, self.ws_e))
+        return outs
+
+    def run_and_check(self, what):
+        for s in range(self.steps):
+            log(f"{what}: step {s}")
+            self.replay_step(s)
+            eager = self.eager_step(s)
+            torch.cuda.synchronize()
+            for l, (o, lse) in enumerate(eager):
+                assert torch.equal(self.o_buf[l], o), (what, s, l)
+                assert torch.equal(self.l_buf[l], lse), (what, s, l)
+        for l in range(self.layers):
+            assert torch.equal(self.kg[l], self.ke[l]) and torch.equal(self.vg[l], self.ve[l]), (what, l)
+        # the last step against the oracle, on layer 0 and the last layer
+        s = self.steps - 1
+        for l in sorted({0, self.layers - 1}):
+            qb = bits(self.q_all[s, l])
+            o_ref, l_ref = [], []
+            for r in range(len(self.lens0)):
+                n = int(self.lens0[r]) + s + 1
+                kc, vc, ident = request_pages_host(self.kg[l], self.vg[l], self.tables[r], n)
+                o, lse = oracle.decode(qb[r:r + 1], kc, vc, [n], [ident], W.SCALE)
+                o_ref.append(o[0])
+                l_ref.append(lse[0])
+            compare(self.o_buf[l], self.l_buf[l], np.stack(o_ref), np.stack(l_ref), f"{what} layer {l} last step")
+
+
+def test_graph_decode_loop_one_request():
+    """The tiny workload's decode phase: one request with a 439-token prompt, 32 steps of
+    (append its new token, decode), each step one replay of the same graph."""
+    p = W.TINY.params
+    log("graph: tiny decode loop, 1 request, 32 steps")
+    StepGraph([p["prompt"]], p["decode_steps"], 1, W.TINY.tag).run_and_check("graph tiny")
+
+
+def test_graph_multilayer_decode_step():
+    """A full-depth-style step in miniature: 4 layers x 8 requests (KV 1000-9000 tokens) per graph,
+    6 steps."""
+    lens0 = W.loguniform_lengths(8, 1000, 9000, W.FULLDEPTH.tag, 9)
+    log(f"graph: 4 layers x 8 requests, lens0={lens0.tolist()}")
+    StepGraph(lens0, 6, 4, W.FULLDEPTH.tag).run_and_check("graph 4x8")
