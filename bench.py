@@ -48,7 +48,7 @@ OUT_BYTES = W.HQ * W.HEAD_DIM * 4 + W.HQ * 4              # fp32 O + LSE per que
 # of the kernel's sources; it is reported only while the sources still match.
 TRAFFIC_TABLE = os.path.join(ROOT, "profiles", "traffic.md")
 KERNEL_SOURCES = {
-    "prefill_kernel": ["prefill.hip"],
+    "prefill_kernel+prefill_merge_kernel": ["prefill.hip"],
     "decode_split_kernel+decode_merge_kernel": ["decode.hip"],
 }
 COMMON_SOURCES = ["device_util.h", "mtd_internal.h"]
@@ -160,6 +160,8 @@ class MixedStep:
         self.kv_lens = torch.as_tensor(self.lens.astype(np.int32), device=dev)
         self.max_len = int(self.lens.max())
         self.ws = torch.empty(mtd.decode_workspace_bytes(len(self.lens), self.max_len), dtype=torch.uint8, device=dev)
+        # prefill workspace: each position tile's keys run as two halves, merged (balances the causal work)
+        self.ws_p = torch.empty(mtd.prefill_workspace_bytes(self.chunk), dtype=torch.uint8, device=dev)
         self.o_a = torch.empty((self.chunk, W.HQ, W.HEAD_DIM), dtype=torch.float32, device=dev)
         self.l_a = torch.empty((self.chunk, W.HQ), dtype=torch.float32, device=dev)
         self.o_d = torch.empty((len(self.lens), W.HQ, W.HEAD_DIM), dtype=torch.float32, device=dev)
@@ -176,7 +178,8 @@ class MixedStep:
         if events: events[0].record()
         mtd.mtd_kv_append(self.k, self.v, self.k_new, self.v_new, self.cu, self.start, self.bt_all)
         if events: events[1].record()
-        mtd.mtd_attn_prefill_chunk(self.k, self.v, self.q_a, self.prefix, self.bt_a, W.SCALE, self.o_a, self.l_a)
+        mtd.mtd_attn_prefill_chunk(self.k, self.v, self.q_a, self.prefix, self.bt_a, W.SCALE, self.o_a, self.l_a,
+                                   self.ws_p)
         if events: events[2].record()
         mtd.mtd_attn_decode(self.k, self.v, self.q_d, self.kv_lens, self.bt_dec, self.max_len, W.SCALE,
                             self.ws, self.o_d, self.l_d)
@@ -198,13 +201,13 @@ class MixedStep:
             "decode": {"value": dec_gbs, "unit": "GB/s", "frac": dec_gbs / HBM_PEAK_GBS, "ms": dec_ms,
                        "bytes": self.work["decode_bytes"], "kernels": "decode_split_kernel + decode_merge_kernel"},
             "prefill": {"value": pre_tfs, "unit": "TFLOP/s", "frac": pre_tfs / MFMA_BF16_PEAK_TFLOPS, "ms": pre_ms,
-                        "flops": self.work["prefill_flops"], "kernels": "prefill_kernel"},
+                        "flops": self.work["prefill_flops"], "kernels": "prefill_kernel + prefill_merge_kernel"},
             "append": {"ms": app_ms, "bytes": self.work["append_bytes"], "kernels": "kv_append_kernel"},
         }
 
     def dominant(self, res):
         if res["prefill"]["ms"] >= res["decode"]["ms"]:
-            return {"kernel": "prefill_kernel", "bound": "mfma", "achieved": res["prefill"]["value"],
+            return {"kernel": "prefill_kernel+prefill_merge_kernel", "bound": "mfma", "achieved": res["prefill"]["value"],
                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "per_launch": res["prefill"]["flops"],
                     "ms": res["prefill"]["ms"]}
         return {"kernel": "decode_split_kernel+decode_merge_kernel", "bound": "hbm", "achieved": res["decode"]["value"],
@@ -343,6 +346,7 @@ class Prefill90:
         fill_normal_(self.q, W.torch_seed(W.PREFILL90.tag, 3))
         self.o = torch.empty((self.chunk, W.HQ, W.HEAD_DIM), dtype=torch.float32, device=dev)
         self.l = torch.empty((self.chunk, W.HQ), dtype=torch.float32, device=dev)
+        self.ws_p = torch.empty(mtd.prefill_workspace_bytes(self.chunk), dtype=torch.uint8, device=dev)
         self.chunks = [(s, min(self.chunk, self.total - s)) for s in range(0, self.total, self.chunk)]
         self.cu = [torch.tensor([0, c], dtype=torch.int32, device=dev) for _, c in self.chunks]
         self.st = [torch.tensor([s], dtype=torch.int32, device=dev) for s, _ in self.chunks]
@@ -353,7 +357,8 @@ class Prefill90:
         mtd = self.mtd
         for i, (s, c) in enumerate(self.chunks):
             mtd.mtd_kv_append(self.k, self.v, self.k_log[s:s + c], self.v_log[s:s + c], self.cu[i], self.st[i], self.bt)
-            mtd.mtd_attn_prefill_chunk(self.k, self.v, self.q[s:s + c], s, self.bt[0], W.SCALE, self.o[:c], self.l[:c])
+            mtd.mtd_attn_prefill_chunk(self.k, self.v, self.q[s:s + c], s, self.bt[0], W.SCALE, self.o[:c], self.l[:c],
+                                       self.ws_p)
 
     def timed_step(self):
         """Per-chunk events (append and prefill separately)."""
@@ -365,7 +370,8 @@ class Prefill90:
             e[0].record()
             mtd.mtd_kv_append(self.k, self.v, self.k_log[s:s + c], self.v_log[s:s + c], self.cu[i], self.st[i], self.bt)
             e[1].record()
-            mtd.mtd_attn_prefill_chunk(self.k, self.v, self.q[s:s + c], s, self.bt[0], W.SCALE, self.o[:c], self.l[:c])
+            mtd.mtd_attn_prefill_chunk(self.k, self.v, self.q[s:s + c], s, self.bt[0], W.SCALE, self.o[:c], self.l[:c],
+                                       self.ws_p)
             e[2].record()
             evs.append(e)
         return evs
@@ -381,7 +387,7 @@ class Prefill90:
                 "append": {"ms": self.timer.mean_ms("append")}}
 
     def dominant(self, res):
-        return {"kernel": "prefill_kernel", "bound": "mfma", "achieved": res["prefill"]["value"],
+        return {"kernel": "prefill_kernel+prefill_merge_kernel", "bound": "mfma", "achieved": res["prefill"]["value"],
                 "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "per_launch": self.flops / len(self.chunks),
                 "ms": res["prefill"]["ms"] / len(self.chunks)}
 
@@ -488,8 +494,9 @@ class FullDepth:
 class MixedStepOverlap(MixedStep):
     """The mixed step with the decode on a second stream (default priority), so it can fill CUs the
     prefill leaves idle: the append first, then the prefill on the library's stream and the decode
-    on the second one, joined before the next step.  Outputs are bit-identical to the sequential
-    step; per-kernel times here include the contention between the two."""
+    on the second one, joined before the next step.  The prefill runs in one pass (no workspace):
+    its uneven causal tail is what the decode fills.  Outputs are bit-identical to the sequential
+    step with a one-pass prefill; per-kernel times here include the contention between the two."""
     name = "mixed_step_overlap"
 
     def __init__(self, dev):

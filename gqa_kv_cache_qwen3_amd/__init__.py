@@ -72,8 +72,11 @@ def lib() -> ctypes.CDLL:
         kvp = ctypes.POINTER(KvLayer)
         cdll.mtd_kv_append.argtypes = [kvp, _P, _P, _P, _P, _P, _I, _I, _I, _P]
         cdll.mtd_kv_append.restype = ctypes.c_int
-        cdll.mtd_attn_prefill_chunk.argtypes = [kvp, _P, _I, _I, _P, _I, _I, ctypes.c_float, _P, _P, _P]
+        cdll.mtd_attn_prefill_chunk.argtypes = [kvp, _P, _I, _I, _P, _I, _I, ctypes.c_float, _P,
+                                                ctypes.c_size_t, _P, _P, _P]
         cdll.mtd_attn_prefill_chunk.restype = ctypes.c_int
+        cdll.mtd_attn_prefill_workspace_bytes.argtypes = [_I, _I, _I]
+        cdll.mtd_attn_prefill_workspace_bytes.restype = ctypes.c_size_t
         cdll.mtd_attn_decode_workspace_bytes.argtypes = [_I, _I, _I, _I]
         cdll.mtd_attn_decode_workspace_bytes.restype = ctypes.c_size_t
         cdll.mtd_attn_decode.argtypes = [kvp, _P, _P, _P, _I, _I, _I, _I, ctypes.c_float, _P,
@@ -142,10 +145,16 @@ def mtd_kv_append(k_pages, v_pages, k_new, v_new, cu_new, start_pos, block_table
                                block_tables.shape[1], n_req, k_new.shape[0], _stream()))
 
 
+def prefill_workspace_bytes(chunk_len: int, num_q_heads: int = NUM_Q_HEADS, head_dim: int = HEAD_DIM) -> int:
+    return int(lib().mtd_attn_prefill_workspace_bytes(chunk_len, num_q_heads, head_dim))
+
+
 def mtd_attn_prefill_chunk(k_pages, v_pages, q, prefix_len: int, block_table, scale: float,
-                           out=None, lse=None):
+                           out=None, lse=None, workspace=None):
     """Causal attention of a chunk q ([C][Hq][D] bf16) at prefix_len over the pages.
 
+    workspace: None (one pass per position tile) or a uint8 device tensor of at least
+    prefill_workspace_bytes(C) bytes (key range of each tile in two halves, merged).
     Returns (out float32 [C][Hq][D], lse float32 [C][Hq]).
     """
     layer = kv_layer(k_pages, v_pages)
@@ -160,9 +169,14 @@ def mtd_attn_prefill_chunk(k_pages, v_pages, q, prefix_len: int, block_table, sc
     _need(lse, "lse", torch.float32, 2)
     if tuple(out.shape) != (c, hq, d) or tuple(lse.shape) != (c, hq):
         raise ValueError("out must be [C][Hq][D] and lse [C][Hq]")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, 1)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
     _check(lib().mtd_attn_prefill_chunk(ctypes.byref(layer), q.data_ptr(), c, int(prefix_len),
                                         block_table.data_ptr(), block_table.shape[0], hq,
-                                        float(scale), out.data_ptr(), lse.data_ptr(), _stream()))
+                                        float(scale), ws_ptr, ws_bytes, out.data_ptr(),
+                                        lse.data_ptr(), _stream()))
     return out, lse
 
 
@@ -205,5 +219,5 @@ def mtd_attn_decode(k_pages, v_pages, q, kv_lens, block_tables, max_kv_len: int,
 
 __all__ = [
     "MtdError", "KvLayer", "lib", "kv_layer", "mtd_kv_append", "mtd_attn_prefill_chunk",
-    "mtd_attn_decode", "decode_workspace_bytes",
+    "mtd_attn_decode", "decode_workspace_bytes", "prefill_workspace_bytes",
 ]

@@ -93,7 +93,8 @@ int mtd_kv_append(const mtd_kv_layer_t* kv, const void* k_new, const void* v_new
 
 int mtd_attn_prefill_chunk(const mtd_kv_layer_t* kv, const void* q, int32_t chunk_len,
                            int32_t prefix_len, const int32_t* block_table, int32_t block_table_len,
-                           int32_t num_q_heads, float scale, float* out, float* lse, void* stream) {
+                           int32_t num_q_heads, float scale, void* workspace, size_t workspace_bytes,
+                           float* out, float* lse, void* stream) {
   int st = check_layer(kv);
   if (st != MTD_OK) return st;
   if ((st = check_heads(num_q_heads, kv->num_kv_heads)) != MTD_OK) return st;
@@ -110,10 +111,20 @@ int mtd_attn_prefill_chunk(const mtd_kv_layer_t* kv, const void* q, int32_t chun
   if (block_table_len < pages)
     return fail(MTD_ERR_CAPACITY, "block_table_len %d < %lld pages needed", block_table_len,
                 (long long)pages);
+  if (workspace != nullptr && workspace_bytes < mtd::prefill_workspace_bytes(chunk_len))
+    return fail(MTD_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes,
+                mtd::prefill_workspace_bytes(chunk_len));
   return hip_status(mtd::launch_prefill(pools(kv), static_cast<const uint16_t*>(q), chunk_len,
-                                        prefix_len, block_table, scale, out, lse,
+                                        prefix_len, block_table, scale, workspace, out, lse,
                                         static_cast<hipStream_t>(stream)),
                     "prefill launch");
+}
+
+size_t mtd_attn_prefill_workspace_bytes(int32_t chunk_len, int32_t num_q_heads, int32_t head_dim) {
+  if (chunk_len <= 0 || chunk_len > MTD_MAX_CONTEXT || num_q_heads != mtd::kQHeads ||
+      head_dim != mtd::kHeadDim)
+    return 0;
+  return mtd::prefill_workspace_bytes(chunk_len);
 }
 
 size_t mtd_attn_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t max_kv_len,

@@ -47,9 +47,13 @@ hipError_t launch_kv_append(const KvPools& kv, const uint16_t* k_new, const uint
                             const int32_t* block_tables, int bt_stride, int n_req, int n_new,
                             hipStream_t stream);
 
+// Optional prefill workspace: partial O float32 [chunk_len][kQHeads][kHeadDim], then partial LSE
+// float32 [chunk_len][kQHeads] (the second halves of split tiles).  workspace == nullptr: no split.
+size_t prefill_workspace_bytes(int chunk_len);
+
 hipError_t launch_prefill(const KvPools& kv, const uint16_t* q, int chunk_len, int prefix_len,
-                          const int32_t* block_table, float scale, float* out, float* lse,
-                          hipStream_t stream);
+                          const int32_t* block_table, float scale, void* workspace, float* out,
+                          float* lse, hipStream_t stream);
 
 // Workspace layout of the decode: partial O float32 [max_parts][kQHeads][kHeadDim], then partial
 // LSE float32 [max_parts][kQHeads], max_parts = batch * split_parts_bound(max_kv_len).

@@ -37,6 +37,8 @@
 // Causal masking is applied only on tiles that reach past the workgroup's first position.  Keys
 // past the request's last token (tail of the last page) are loaded from the page's first row
 // instead of their slots, so V stays finite where their weight is exactly zero.
+#include <atomic>
+
 #include "device_util.h"
 #include "mtd_internal.h"
 
@@ -265,7 +267,8 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
     const uint16_t* __restrict__ k_pages, const uint16_t* __restrict__ v_pages, int num_pages,
     const uint16_t* __restrict__ q, int chunk_len, int prefix_len,
     const int32_t* __restrict__ block_table, float scale_log2, float* __restrict__ out,
-    float* __restrict__ lse, int n_qtiles) {
+    float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse, int n_qtiles,
+    int split) {
   // Three stages of (K, V) tiles, 96 KiB: the tile being read, the next tile (in flight, then
   // read from the middle of the current step on) and the stage the following DMA refills.
   // Separate arrays, so the compiler can see that the DMA into one stage never aliases the reads
@@ -283,7 +286,12 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
   const int n = lane & 31;   // query column of this lane
   const int hk = lane >> 5;  // which half of each 32-key block this lane holds
   const int g = blockIdx.x % kKvHeads;
-  const int qt = n_qtiles - 1 - (int)(blockIdx.x / kKvHeads);
+  // Work item: position tile qt of KV head g, longest first.  When split, each item is two
+  // workgroups, one per half of its key tiles (the dispatcher then pairs long and short halves on
+  // the CUs), and the second half's partial result goes to part_o / part_lse.
+  const int rank = (int)(blockIdx.x / kKvHeads);
+  const int qt = n_qtiles - 1 - (split ? rank >> 1 : rank);
+  const int half = split ? rank & 1 : 0;
   const int q0 = qt * kBQ;
   const int qpos = q0 + 16 * wave + (n & 15);
   const int head = kGroup * g + (n >> 4);
@@ -292,13 +300,18 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
   const int total = prefix_len + chunk_len;
 
   const int kv_end = min(prefix_len + q0 + kBQ, total);
-  const int n_tiles = (kv_end + kBK - 1) / kBK;
+  const int n_item = (kv_end + kBK - 1) / kBK;
+  // This workgroup's key tiles [t0, t1): all of them, or one half when the item is split.
+  const bool cut = split && n_item >= 2;
+  const int t0 = cut && half ? n_item / 2 : 0;
+  const int t1 = cut && !half ? n_item / 2 : n_item;
+  if (half && !cut) return;  // the second half of an item too short to split
   // Tiles whose keys all precede the workgroup's first query need no causal mask.
-  const int n_plain = min((prefix_len + q0 + 1) / kBK, n_tiles);
-  const TileArgs ta{k_pages, v_pages, block_table, num_pages, g, total, wave, lane, n_tiles};
+  const int n_plain = min((prefix_len + q0 + 1) / kBK, t1);
+  const TileArgs ta{k_pages, v_pages, block_table, num_pages, g, total, wave, lane, t1};
 
-  issue_tile(ta, 0, tile_page(ta, 0), k_lds0, v_lds0);
-  int next_page = tile_page(ta, 1);
+  issue_tile(ta, t0, tile_page(ta, t0), k_lds0, v_lds0);
+  int next_page = tile_page(ta, t0 + 1);
   // Stage 2's V starts as zeros: the first step multiplies it by an all-zero P^T in place of a
   // previous block.
   *reinterpret_cast<uint4*>(v_lds2 + 32 * tid) = make_uint4(0, 0, 0, 0);
@@ -328,8 +341,8 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
 
   wait_dma();
   __syncthreads();
-  if (1 < n_tiles) issue_tile(ta, 1, next_page, k_lds1, v_lds1);
-  next_page = tile_page(ta, 2);
+  if (t0 + 1 < t1) issue_tile(ta, t0 + 1, next_page, k_lds1, v_lds1);
+  next_page = tile_page(ta, t0 + 2);
   floatx16_t s_a, s_b;
   bf16x8_t p_prev[2], v_prev[8];
   load_v(v_prev, v_lds2, off, 1);  // zeros: stands in for the V^T of block -1
@@ -342,7 +355,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
     p_prev[1] = zero;
   }
 
-  // Tile kt lives in stage kt % 3.  Step kt: first half = softmax of block 2kt beside the scores
+  // Tile kt lives in stage (kt - t0) % 3.  Step kt: first half = softmax of block 2kt beside the scores
   // of block 2kt+1 and the O update of block 2kt-1, reading block 2kt's V^T; then wait for tile
   // kt+1's DMA and barrier (everyone is done with tile kt-1's stage), start tile kt+2's DMA into
   // that stage; second half = softmax of block 2kt+1 beside the scores of block 2kt+2 (next
@@ -355,20 +368,20 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
                           (KT) * kBK, hk, qabs, scale_log2);                                  \
     wait_dma();                                                                               \
     tile_barrier();                                                                           \
-    if ((KT) + 2 < n_tiles) issue_tile(ta, (KT) + 2, next_page, PRV_K, PRV_V);                \
+    if ((KT) + 2 < t1) issue_tile(ta, (KT) + 2, next_page, PRV_K, PRV_V);                     \
     next_page = tile_page(ta, (KT) + 3);                                                      \
     pipe_step<MASK, true>(sm, s_b, s_a, p_prev, v_prev, qf, NXT_K, 0, CUR_V, 1, off,          \
                           (KT) * kBK + 32, hk, qabs, scale_log2);                             \
   }
-  const int n_main = min(n_plain, n_tiles - 1);
-  int kt = 0;
+  const int n_main = min(n_plain, t1 - 1);
+  int kt = t0;
   for (; kt + 3 <= n_main; kt += 3) {
     MTD_PREFILL_STEP(kt, k_lds0, v_lds0, v_lds2, k_lds1, k_lds2, false)
     MTD_PREFILL_STEP(kt + 1, k_lds1, v_lds1, v_lds0, k_lds2, k_lds0, false)
     MTD_PREFILL_STEP(kt + 2, k_lds2, v_lds2, v_lds1, k_lds0, k_lds1, false)
   }
-  for (; kt < n_tiles - 1; ++kt) {
-    const int sc = kt % 3;
+  for (; kt < t1 - 1; ++kt) {
+    const int sc = (kt - t0) % 3;
     uint8_t* ck = sc == 0 ? k_lds0 : sc == 1 ? k_lds1 : k_lds2;
     uint8_t* cv = sc == 0 ? v_lds0 : sc == 1 ? v_lds1 : v_lds2;
     uint8_t* nk = sc == 0 ? k_lds1 : sc == 1 ? k_lds2 : k_lds0;
@@ -378,7 +391,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
   }
 #undef MTD_PREFILL_STEP
   {
-    const int sc = kt % 3;
+    const int sc = (kt - t0) % 3;
     const uint8_t* ck = sc == 0 ? k_lds0 : sc == 1 ? k_lds1 : k_lds2;
     const uint8_t* cv = sc == 0 ? v_lds0 : sc == 1 ? v_lds1 : v_lds2;
     pipe_step<true, true>(sm, s_a, s_b, p_prev, v_prev, qf, ck, 1, cv, 0, off, kt * kBK, hk, qabs,
@@ -394,10 +407,14 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
     mma_pv(sm.o_acc, v_prev, p_prev);
   }
 
+  // A second half can hold no key a row may see (early rows of a short item): its partial is then
+  // O = 0 with LSE = -inf, which the merge weighs by exactly zero.
   const float l_tot = sum_xor32(sm.l);
   if (qvalid) {
-    const float inv = 1.f / l_tot;
-    float* orow = out + ((size_t)qpos * kQHeads + head) * kHeadDim;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    float* const o_dst = half ? part_o : out;
+    float* const l_dst = half ? part_lse : lse;
+    float* orow = o_dst + ((size_t)qpos * kQHeads + head) * kHeadDim;
     // Accumulator element v of tile dt is dim 32dt + 8(v/4) + 4hk + v%4.
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
@@ -406,19 +423,79 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
         *reinterpret_cast<float4*>(orow + 32 * dt + 8 * a + 4 * hk) =
             make_float4(sm.o_acc[dt][4 * a] * inv, sm.o_acc[dt][4 * a + 1] * inv,
                         sm.o_acc[dt][4 * a + 2] * inv, sm.o_acc[dt][4 * a + 3] * inv);
-    if (hk == 0) lse[(size_t)qpos * kQHeads + head] = (sm.m + log2f(l_tot)) * kLn2;
+    if (hk == 0) l_dst[(size_t)qpos * kQHeads + head] = l_tot > 0.f ? (sm.m + log2f(l_tot)) * kLn2 : kNegInf;
   }
+}
+
+// Combines the two halves of every split item: out/lse hold the first half's normalised partial,
+// part_o/part_lse the second's.  One wavefront per (position, head) row; each lane takes 2 dims.
+// Both LSEs are read before lane 0 overwrites lse, in program order within the wave.
+__global__ __launch_bounds__(256) void prefill_merge_kernel(float* __restrict__ out, float* __restrict__ lse,
+                                                            const float* __restrict__ part_o,
+                                                            const float* __restrict__ part_lse,
+                                                            int chunk_len, int prefix_len) {
+  const int row = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);  // (position, head)
+  const int lane = threadIdx.x & 63;
+  if (row >= chunk_len * kQHeads) return;
+  const int qpos = row / kQHeads;
+  const int q0 = (qpos / kBQ) * kBQ;
+  const int kv_end = min(prefix_len + q0 + kBQ, prefix_len + chunk_len);
+  if ((kv_end + kBK - 1) / kBK < 2) return;  // item was not split: out/lse are final
+  const float l0 = lse[row], l1 = part_lse[row];
+  const float mx = fmaxf(l0, l1);
+  const float w0 = __expf(l0 - mx), w1 = __expf(l1 - mx);
+  const float inv = 1.f / (w0 + w1);
+  float2* o = reinterpret_cast<float2*>(out + (size_t)row * kHeadDim) + lane;
+  const float2 a = *o;
+  const float2 b = reinterpret_cast<const float2*>(part_o + (size_t)row * kHeadDim)[lane];
+  *o = make_float2((w0 * a.x + w1 * b.x) * inv, (w0 * a.y + w1 * b.y) * inv);
+  if (lane == 0) lse[row] = mx + __logf(w0 + w1);
 }
 
 }  // namespace
 
+// Compute units of the calling thread's current device, queried once per device.
+int device_cus() {
+  static std::atomic<int> cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+size_t prefill_workspace_bytes(int chunk_len) {
+  return (size_t)chunk_len * kQHeads * (kHeadDim + 1) * sizeof(float);
+}
+
 hipError_t launch_prefill(const KvPools& kv, const uint16_t* q, int chunk_len, int prefix_len,
-                          const int32_t* block_table, float scale, float* out, float* lse,
-                          hipStream_t stream) {
+                          const int32_t* block_table, float scale, void* workspace, float* out,
+                          float* lse, hipStream_t stream) {
   const int n_qtiles = (chunk_len + kBQ - 1) / kBQ;
-  prefill_kernel<<<dim3(n_qtiles * kKvHeads), dim3(64 * kWaves), 0, stream>>>(
+  // Splitting pays where one pass would leave CUs idle: when there are fewer (tile, KV head)
+  // items than CUs (chunks shorter than 32 tiles on a 256-CU part), and where the causal work per
+  // tile is very uneven (the last tile of a chunk sees prefix + chunk keys, the first only
+  // prefix).  It has costs: the merge pass, and K/V read twice from HBM because the second-round
+  // halves start at staggered times and miss the L2 reuse of workgroups that sweep the same tiles
+  // together.  With a prefix above twice the chunk the spread is under 20 % and the clock the
+  // early-idle CUs free absorbs most of it (measured: +18 % at a 0 prefix, +4 % at 4096, +0.4 % at
+  // 32,768, -1 % at 61,440 for 4096-token chunks), so such chunks run in one pass.
+  const int split = workspace != nullptr &&
+                    (prefix_len <= 2 * chunk_len || n_qtiles * kKvHeads < device_cus());
+  float* part_o = static_cast<float*>(workspace);
+  float* part_lse = split ? part_o + (size_t)chunk_len * kQHeads * kHeadDim : nullptr;
+  prefill_kernel<<<dim3(n_qtiles * kKvHeads * (split ? 2 : 1)), dim3(64 * kWaves), 0, stream>>>(
       kv.k, kv.v, kv.num_pages, q, chunk_len, prefix_len, block_table, scale * kLog2e, out, lse,
-      n_qtiles);
+      part_o, part_lse, n_qtiles, split);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || !split) return err;
+  const int rows = chunk_len * kQHeads;
+  prefill_merge_kernel<<<dim3((rows + 3) / 4), dim3(256), 0, stream>>>(out, lse, part_o, part_lse,
+                                                                      chunk_len, prefix_len);
   return hipGetLastError();
 }
 

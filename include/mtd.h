@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define MTD_ABI_VERSION 1
+#define MTD_ABI_VERSION 2
 
 /* Status codes. */
 #define MTD_OK               0
@@ -120,12 +120,29 @@ int mtd_kv_append(const mtd_kv_layer_t* kv, const void* k_new, const void* v_new
  *   block_table_len host: capacity of block_table in entries; must be at least
  *                   ceil((prefix_len + chunk_len) / page_size), else MTD_ERR_CAPACITY
  *   num_q_heads     16;  scale > 0 and finite (1/sqrt(head_dim) for the Qwen3 decoder)
+ *   workspace       NULL, or device scratch of at least mtd_attn_prefill_workspace_bytes(chunk_len,
+ *                   num_q_heads, head_dim) bytes (else MTD_ERR_WORKSPACE), owned by the caller,
+ *                   contents ignored on entry and unspecified on return.  With a workspace, the
+ *                   keys of each (128-position tile, KV head) are processed in two halves whose
+ *                   partial results are merged by log-sum-exp whenever one pass would leave
+ *                   compute units idle: when there are fewer such items than compute units, or
+ *                   when prefix_len <= 2 * chunk_len (uneven causal work).  Otherwise, and
+ *                   without a workspace, each tile is one pass.  Both give correct results; their
+ *                   bits differ.  Calls on different streams need different workspaces.
  *   out             float32 [chunk_len][num_q_heads][head_dim], written
  *   lse             float32 [chunk_len][num_q_heads], written: natural-log sum of exp(s_j)
  */
 int mtd_attn_prefill_chunk(const mtd_kv_layer_t* kv, const void* q, int32_t chunk_len,
                            int32_t prefix_len, const int32_t* block_table, int32_t block_table_len,
-                           int32_t num_q_heads, float scale, float* out, float* lse, void* stream);
+                           int32_t num_q_heads, float scale, void* workspace, size_t workspace_bytes,
+                           float* out, float* lse, void* stream);
+
+/*
+ * mtd_attn_prefill_workspace_bytes - size of the optional mtd_attn_prefill_chunk workspace:
+ * chunk_len * num_q_heads * (head_dim + 1) * 4 bytes (the second halves' partial outputs and
+ * log-sum-exps).  Returns 0 for arguments mtd_attn_prefill_chunk would reject.
+ */
+size_t mtd_attn_prefill_workspace_bytes(int32_t chunk_len, int32_t num_q_heads, int32_t head_dim);
 
 /*
  * mtd_attn_decode_workspace_bytes - device workspace mtd_attn_decode needs for a batch whose

@@ -30,9 +30,9 @@ def declared_functions():
 
 def test_header_declares_the_three_calls():
     names = declared_functions()
-    for n in ("mtd_kv_append", "mtd_attn_prefill_chunk", "mtd_attn_decode",
-              "mtd_attn_decode_workspace_bytes", "mtd_status_string", "mtd_last_error",
-              "mtd_abi_version"):
+    for n in ("mtd_kv_append", "mtd_attn_prefill_chunk", "mtd_attn_prefill_workspace_bytes",
+              "mtd_attn_decode", "mtd_attn_decode_workspace_bytes", "mtd_status_string",
+              "mtd_last_error", "mtd_abi_version"):
         assert n in names
 
 
@@ -78,11 +78,12 @@ def append(lib, kv, **kw):
 
 
 def prefill(lib, kv, **kw):
-    a = dict(q=FAKE, chunk=10, prefix=0, bt=FAKE, bt_len=4, hq=16, scale=0.088, out=FAKE, lse=FAKE)
+    a = dict(q=FAKE, chunk=10, prefix=0, bt=FAKE, bt_len=4, hq=16, scale=0.088, ws=None, ws_bytes=0,
+             out=FAKE, lse=FAKE)
     a.update(kw)
     return lib.mtd_attn_prefill_chunk(ctypes.byref(kv) if kv is not None else None, a["q"],
                                       a["chunk"], a["prefix"], a["bt"], a["bt_len"], a["hq"],
-                                      a["scale"], a["out"], a["lse"], None)
+                                      a["scale"], a["ws"], a["ws_bytes"], a["out"], a["lse"], None)
 
 
 def decode(lib, kv, **kw):
@@ -153,6 +154,9 @@ def test_append_empty_is_noop(lib):
     (dict(prefix=-1), mtd.MTD_ERR_INVALID_ARG),
     (dict(prefix=131072 - 9, chunk=10, bt_len=2048), mtd.MTD_ERR_CAPACITY),
     (dict(prefix=200, chunk=57, bt_len=4), mtd.MTD_ERR_CAPACITY),   # 257 tokens need 5 pages
+    (dict(ws=FAKE, ws_bytes=0), mtd.MTD_ERR_WORKSPACE),
+    (dict(ws=FAKE, ws_bytes=10 * 16 * 129 * 4 - 1), mtd.MTD_ERR_WORKSPACE),
+    (dict(ws=FAKE, ws_bytes=10 * 16 * 129 * 4, hq=12), mtd.MTD_ERR_UNSUPPORTED),
 ])
 def test_prefill_validation(lib, kw, code):
     assert prefill(lib, layer(), **kw) == code
@@ -175,6 +179,16 @@ def test_prefill_validation(lib, kw, code):
 ])
 def test_decode_validation(lib, kw, code):
     assert decode(lib, layer(), **kw) == code
+
+
+def test_prefill_workspace_size_formula(lib):
+    # the second halves' partial O and LSE: chunk_len rows of 16 heads x (128 + 1) floats
+    for c in (1, 2, 127, 128, 129, 4096, 131072):
+        assert lib.mtd_attn_prefill_workspace_bytes(c, 16, 128) == c * 16 * 129 * 4
+    assert lib.mtd_attn_prefill_workspace_bytes(0, 16, 128) == 0
+    assert lib.mtd_attn_prefill_workspace_bytes(131073, 16, 128) == 0
+    assert lib.mtd_attn_prefill_workspace_bytes(10, 8, 128) == 0
+    assert lib.mtd_attn_prefill_workspace_bytes(10, 16, 64) == 0
 
 
 def _split_tokens(n):

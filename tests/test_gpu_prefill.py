@@ -1,6 +1,8 @@
 """mtd_attn_prefill_chunk on the GPU against the fp64 oracle: one-shot and chunked prefill over
 pages written by mtd_kv_append, at small ragged shapes in full and at the 90-minute and
-mixed-step sizes on sampled rows; plus chunked == one-shot and decode == 1-row prefill."""
+mixed-step sizes on sampled rows; plus chunked == one-shot and decode == 1-row prefill.  The
+checks run both without a workspace (one pass per position tile) and with one (each tile's keys
+in two halves, merged by log-sum-exp, wherever one pass would leave compute units idle)."""
 
 import numpy as np
 import pytest
@@ -18,8 +20,9 @@ mtd = pytest.importorskip("gqa_kv_cache_qwen3_amd")
 class Request:
     """One request's paged KV, filled through mtd_kv_append (the path under test)."""
 
-    def __init__(self, total: int, tag: int, lowrank: bool = False, spare: int = 2):
+    def __init__(self, total: int, tag: int, lowrank: bool = False, spare: int = 2, split: bool = False):
         self.total = total
+        self.split = split
         tables, self.num_pages, self.spare = W.place_pages([total], tag, 0, spare=spare)
         self.table_np = tables[0]
         self.table = torch.as_tensor(self.table_np, device="cuda")
@@ -46,8 +49,11 @@ class Request:
 
     def prefill(self, prefix: int, chunk: int):
         self.append_to(prefix + chunk)
+        ws = None
+        if self.split:
+            ws = torch.empty(mtd.prefill_workspace_bytes(chunk), dtype=torch.uint8, device="cuda")
         out, lse = mtd.mtd_attn_prefill_chunk(self.k, self.v, self.q_log[prefix:prefix + chunk].contiguous(),
-                                              prefix, self.table, W.SCALE)
+                                              prefix, self.table, W.SCALE, workspace=ws)
         torch.cuda.synchronize()
         return out, lse
 
@@ -63,14 +69,18 @@ class Request:
         return oracle.attention(oracle.bf16_to_f64(q[rows]), k, v, prefix + rows, W.SCALE)
 
 
-@pytest.mark.parametrize("prefix,chunk", [(0, 1), (0, 64), (0, 65), (5, 1), (63, 2), (100, 37),
-                                          (64, 64), (1000, 300), (0, 439), (4096, 4096)])
-def test_prefill_small_full_compare(prefix, chunk):
-    log(f"prefill prefix={prefix} chunk={chunk}")
-    req = Request(prefix + chunk, 200 + prefix + 7 * chunk)
+SPLIT = pytest.mark.parametrize("split", [False, True], ids=["one-pass", "split"])
+
+
+@SPLIT
+@pytest.mark.parametrize("prefix,chunk", [(0, 1), (0, 64), (0, 65), (5, 1), (63, 2), (50, 37), (100, 37),
+                                          (64, 64), (500, 300), (1000, 300), (0, 439), (4096, 4096)])
+def test_prefill_small_full_compare(prefix, chunk, split):
+    log(f"prefill prefix={prefix} chunk={chunk} split={split}")
+    req = Request(prefix + chunk, 200 + prefix + 7 * chunk, split=split)
     out, lse = req.prefill(prefix, chunk)
     o_ref, l_ref = req.reference(prefix, chunk)
-    compare(out, lse, o_ref, l_ref, f"prefill P={prefix} C={chunk}")
+    compare(out, lse, o_ref, l_ref, f"prefill P={prefix} C={chunk}{' split' if split else ''}")
 
 
 def test_tiny_one_shot_then_decode_steps():
@@ -95,9 +105,10 @@ def test_tiny_one_shot_then_decode_steps():
         compare(o, l, o_ref, l_ref, f"tiny decode step {s}")
 
 
-def test_gpu_chunked_matches_gpu_one_shot():
+@SPLIT
+def test_gpu_chunked_matches_gpu_one_shot(split):
     """The tiny prompt as chunks of 128 + 128 + 128 + 55 against one 439-token call."""
-    req = Request(439, 301)
+    req = Request(439, 301, split=split)
     one_o, one_l = req.prefill(0, 439)
     parts_o, parts_l = [], []
     for start, c in [(0, 128), (128, 128), (256, 128), (384, 55)]:
@@ -128,12 +139,13 @@ def sample_rows(chunk: int, tag: int, n: int = 40) -> np.ndarray:
     return np.array(sorted({r for r in fixed + rnd if 0 <= r < chunk}))
 
 
-def test_prefill_90_minutes_chunked_sampled():
+@SPLIT
+def test_prefill_90_minutes_chunked_sampled(split):
     """67,500 tokens in 17 chunks of 4096 (last 1,964), K with a rank-4 per-head component so the
     softmax is peaked; every chunk is checked on sampled rows against the oracle."""
     p = W.PREFILL90.params
     total, chunk = p["total"], p["chunk"]
-    req = Request(total, W.PREFILL90.tag, lowrank=True)
+    req = Request(total, W.PREFILL90.tag, lowrank=True, split=split)
     req.append_to(total)
     torch.cuda.synchronize()
     kc, vc, ident = request_pages_host(req.k, req.v, req.table_np, total)
@@ -142,32 +154,34 @@ def test_prefill_90_minutes_chunked_sampled():
     qb = bits(req.q_log)
     for ci, start in enumerate(range(0, total, chunk)):
         c = min(chunk, total - start)
-        log(f"prefill90 chunk {ci} prefix={start} len={c}")
+        log(f"prefill90 chunk {ci} prefix={start} len={c} split={split}")
         out, lse = req.prefill(start, c)
         rows = sample_rows(c, ci)
         o_ref, l_ref = oracle.attention(oracle.bf16_to_f64(qb[start + rows]), k, v, start + rows, W.SCALE)
-        compare(out[rows], lse[rows], o_ref, l_ref, f"prefill90 chunk {ci}")
+        compare(out[rows], lse[rows], o_ref, l_ref, f"prefill90 chunk {ci}{' split' if split else ''}")
 
 
-def test_mixed_step_prefill_part_sampled():
+@SPLIT
+def test_mixed_step_prefill_part_sampled(split):
     """The mixed step's chunk: 4096 tokens of request A at prefix 32,768."""
     p = W.MIXED.params
     prefix, chunk = p["prefix"], p["chunk"]
-    req = Request(prefix + chunk, W.MIXED.tag)
-    log("mixed prefill part")
+    req = Request(prefix + chunk, W.MIXED.tag, split=split)
+    log(f"mixed prefill part split={split}")
     out, lse = req.prefill(prefix, chunk)
     rows = sample_rows(chunk, 99, 64)
     o_ref, l_ref = req.reference(prefix, chunk, rows)
-    compare(out[rows], lse[rows], o_ref, l_ref, "mixed prefill part")
+    compare(out[rows], lse[rows], o_ref, l_ref, f"mixed prefill part{' split' if split else ''}")
 
 
-def test_prefill_deterministic_and_placement_invariant():
-    a = Request(5000, 303)
+@SPLIT
+def test_prefill_deterministic_and_placement_invariant(split):
+    a = Request(5000, 303, split=split)
     o1, l1 = a.prefill(1000, 4000)
     o2, l2 = a.prefill(1000, 4000)
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     # same logical data, different page placement
-    b = Request(5000, 303)
+    b = Request(5000, 303, split=split)
     tables, _, _ = W.place_pages([5000], 304, 0, spare=2)
     b.table_np = tables[0]
     b.table = torch.as_tensor(b.table_np, device="cuda")
