@@ -83,3 +83,15 @@ def test_append_one_token_per_request_batch():
         tables[b, lens[b] // W.PAGE] = perm[b]
     kp, vp = new_pool(65, "cuda"), new_pool(65, "cuda")
     check_append(kp, vp, np.ones(64, dtype=np.int64), lens, tables, 800)
+
+
+def test_append_many_requests():
+    """150 requests of 0 to 3 tokens each: the owning request of a token is found by binary search
+    over cu_new, across more than two wavefronts' worth of requests."""
+    rng = W.rng(6, 1)
+    counts = rng.integers(0, 4, size=150)
+    starts = rng.integers(0, 5000, size=150)
+    final = np.maximum(starts + counts, 1)
+    tables, n_pages, _ = W.place_pages(final, 78, 0)
+    kp, vp = new_pool(n_pages, "cuda"), new_pool(n_pages, "cuda")
+    check_append(kp, vp, counts, starts, tables, 900)

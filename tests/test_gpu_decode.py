@@ -52,6 +52,23 @@ def test_decode_split_bands():
     assert torch.equal(out2, out[idx]) and torch.equal(lse2, lse[idx])
 
 
+def test_decode_batch_beyond_one_wavefront_scan():
+    """130 requests: the split and merge kernels locate a request's splits by scanning kv_lens 64
+    requests at a time, so batches above 64 cross that boundary twice."""
+    lens = W.loguniform_lengths(130, 1, 3000, 2, 77)
+    log(f"decode batch 130, lens sum {int(lens.sum())}")
+    batch = DecodeBatch(lens, 105)
+    out, lse = run(batch)
+    o_ref, l_ref = batch.reference()
+    compare(out, lse, o_ref, l_ref, "decode batch 130")
+    sub = [129, 64, 63, 0, 100]
+    idx = torch.tensor(sub, device="cuda")
+    out2, lse2 = mtd.mtd_attn_decode(batch.k, batch.v, batch.q[idx].contiguous(), batch.kv_lens[idx].contiguous(),
+                                     batch.bt[idx].contiguous(), batch.max_len, W.SCALE)
+    torch.cuda.synchronize()
+    assert torch.equal(out2, out[idx]) and torch.equal(lse2, lse[idx])
+
+
 def test_decode_max_len_above_longest():
     """A loose host bound (max_kv_len > every kv_len) gives the same bits as the tight one."""
     batch = DecodeBatch([700, 5, 3000], 102)

@@ -175,6 +175,21 @@ def test_mixed_step_prefill_part_sampled(split):
 
 
 @SPLIT
+@pytest.mark.parametrize("chunk", [4096, 1000])
+def test_prefill_at_the_context_cap(chunk, split):
+    """The last chunk of a 131,072-token context (the 128K cap): a full 4096-token chunk and a
+    1000-token one (fewer tiles than CUs, so the workspace path splits it), sampled rows."""
+    total = W.CONTEXT_CAP
+    prefix = total - chunk
+    req = Request(total, 310 + chunk, split=split)
+    log(f"prefill at the cap: prefix={prefix} chunk={chunk} split={split}")
+    out, lse = req.prefill(prefix, chunk)
+    rows = sample_rows(chunk, 311, 24)
+    o_ref, l_ref = req.reference(prefix, chunk, rows)
+    compare(out[rows], lse[rows], o_ref, l_ref, f"prefill cap C={chunk}{' split' if split else ''}")
+
+
+@SPLIT
 def test_prefill_deterministic_and_placement_invariant(split):
     a = Request(5000, 303, split=split)
     o1, l1 = a.prefill(1000, 4000)
