@@ -8,7 +8,7 @@
 // off the memory critical path.
 //
 // decode_split: one wavefront per work item = (request b, split s, KV head g), where split s is
-//   the logical tokens [T s, min(T s + T, L_b)) with T = split_tokens(L_b) (64 to 512 tokens, by
+//   the logical tokens [T s, min(T s + T, L_b)) with T = split_tokens(L_b) (64 or 512 tokens, by
 //   length).  Items are numbered densely: the flat split index f counts the splits of requests
 //   0..b-1 first, so the grid is 8 * sum_b split_parts(L_b) waves plus a tail of waves that find f
 //   beyond the total and exit.

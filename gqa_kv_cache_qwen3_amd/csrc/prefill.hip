@@ -10,7 +10,9 @@
 // head and serves both query heads of its GQA group, so every K/V tile staged in LDS feeds 256
 // query rows.  Wave w takes positions 16w .. 16w+15 for both heads: 32 query columns.  Workgroup
 // id = 8 * (position tile, longest first) + KV head, so the dispatcher's round-robin over the 8
-// XCDs keeps all tiles of one KV head on one XCD and its L2 serves the K/V re-reads.
+// XCDs keeps all tiles of one KV head on one XCD and its L2 serves the K/V re-reads.  With a
+// workspace, an item can instead run as two workgroups over the two halves of its key tiles,
+// merged afterwards by prefill_merge_kernel (see launch_prefill for when that pays).
 //
 // K/V staging.  A 64-key tile is one page of the KV head: 16 KiB of K and 16 KiB of V, each
 // brought into LDS by 16-byte direct-to-LDS loads (global_load_lds_dwordx4, no registers, no
