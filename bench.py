@@ -54,11 +54,19 @@ KERNEL_SOURCES = {
 COMMON_SOURCES = ["device_util.h", "mtd_internal.h"]
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and blank space, so that comment edits keep the digest."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_digest(kernel: str) -> str:
     h = hashlib.sha256()
     for name in KERNEL_SOURCES.get(kernel, []) + COMMON_SOURCES:
-        with open(os.path.join(ROOT, "gqa_kv_cache_qwen3_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "gqa_kv_cache_qwen3_amd", "csrc", name)) as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
