@@ -1,4 +1,5 @@
-"""fp64 CPU oracle for paged causal grouped-query attention (test infrastructure only).
+"""fp64 CPU oracle for paged causal grouped-query attention and the projections around it
+(test infrastructure only).
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s ``cpu_baseline`` leg
 may import this package.  It shares no code with the HIP library.
@@ -14,3 +15,4 @@ from .attention import (  # noqa: F401
     page_of,
     prefill_chunk,
 )
+from .projection import o_proj, qkv_proj, round_to_bf16_bits  # noqa: F401
