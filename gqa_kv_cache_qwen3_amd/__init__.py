@@ -11,6 +11,8 @@ Names match the C entry points:
     mtd_attn_prefill_chunk(k_pages, v_pages, q, prefix_len, block_table, scale, out=None, lse=None)
     mtd_attn_decode(k_pages, v_pages, q, kv_lens, block_tables, max_kv_len, scale,
                     workspace=None, out=None, lse=None)
+    mtd_qkv_proj(x, w_qkv, q=None, k_new=None, v_new=None)
+    mtd_o_proj(attn, w_o, out=None)
 """
 
 from __future__ import annotations
@@ -35,6 +37,7 @@ NUM_Q_HEADS = 16
 NUM_KV_HEADS = 8
 HEAD_DIM = 128
 PAGE_SIZE = 64
+HIDDEN = 1024
 
 
 class MtdError(RuntimeError):
@@ -82,6 +85,10 @@ def lib() -> ctypes.CDLL:
         cdll.mtd_attn_decode.argtypes = [kvp, _P, _P, _P, _I, _I, _I, _I, ctypes.c_float, _P,
                                          ctypes.c_size_t, _P, _P, _P]
         cdll.mtd_attn_decode.restype = ctypes.c_int
+        cdll.mtd_qkv_proj.argtypes = [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P]
+        cdll.mtd_qkv_proj.restype = ctypes.c_int
+        cdll.mtd_o_proj.argtypes = [_P, _P, _I, _I, _I, _I, _P, _P]
+        cdll.mtd_o_proj.restype = ctypes.c_int
         cdll.mtd_status_string.argtypes = [ctypes.c_int]
         cdll.mtd_status_string.restype = ctypes.c_char_p
         cdll.mtd_last_error.argtypes = []
@@ -217,7 +224,53 @@ def mtd_attn_decode(k_pages, v_pages, q, kv_lens, block_tables, max_kv_len: int,
     return out, lse
 
 
+def _out(t, name, shape, dtype, like):
+    if t is None:
+        t = torch.empty(shape, dtype=dtype, device=like.device)
+    _need(t, name, dtype, len(shape))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be {list(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def mtd_qkv_proj(x, w_qkv, q=None, k_new=None, v_new=None):
+    """q, k, v of n_tok tokens from their hidden states x (bf16 [n_tok][1024]) and the stacked
+    weights w_qkv (bf16 [(16 + 8 + 8) * 128][1024], rows Wq, Wk, Wv).
+
+    Returns (q bf16 [n_tok][16][128], k_new bf16 [n_tok][8][128], v_new bf16 [n_tok][8][128]).
+    """
+    _need(x, "x", torch.bfloat16, 2)
+    _need(w_qkv, "w_qkv", torch.bfloat16, 2)
+    n_tok, hidden = x.shape
+    n_feat = (NUM_Q_HEADS + 2 * NUM_KV_HEADS) * HEAD_DIM
+    if tuple(w_qkv.shape) != (n_feat, hidden):
+        raise ValueError(f"w_qkv must be [{n_feat}][{hidden}], got {tuple(w_qkv.shape)}")
+    q = _out(q, "q", (n_tok, NUM_Q_HEADS, HEAD_DIM), torch.bfloat16, x)
+    k_new = _out(k_new, "k_new", (n_tok, NUM_KV_HEADS, HEAD_DIM), torch.bfloat16, x)
+    v_new = _out(v_new, "v_new", (n_tok, NUM_KV_HEADS, HEAD_DIM), torch.bfloat16, x)
+    _check(lib().mtd_qkv_proj(x.data_ptr(), w_qkv.data_ptr(), n_tok, hidden, NUM_Q_HEADS,
+                              NUM_KV_HEADS, HEAD_DIM, q.data_ptr(), k_new.data_ptr(),
+                              v_new.data_ptr(), _stream()))
+    return q, k_new, v_new
+
+
+def mtd_o_proj(attn, w_o, out=None):
+    """Hidden states from the attention output attn (float32 [n_tok][16][128], rounded to bf16
+    on the way in) and w_o (bf16 [1024][16 * 128]).  Returns out bf16 [n_tok][1024]."""
+    _need(attn, "attn", torch.float32, 3)
+    _need(w_o, "w_o", torch.bfloat16, 2)
+    n_tok, hq, d = attn.shape
+    hidden = w_o.shape[0]
+    if w_o.shape[1] != hq * d:
+        raise ValueError(f"w_o must be [hidden][{hq * d}], got {tuple(w_o.shape)}")
+    out = _out(out, "out", (n_tok, hidden), torch.bfloat16, attn)
+    _check(lib().mtd_o_proj(attn.data_ptr(), w_o.data_ptr(), n_tok, hq, d, hidden, out.data_ptr(),
+                            _stream()))
+    return out
+
+
 __all__ = [
     "MtdError", "KvLayer", "lib", "kv_layer", "mtd_kv_append", "mtd_attn_prefill_chunk",
-    "mtd_attn_decode", "decode_workspace_bytes", "prefill_workspace_bytes",
+    "mtd_attn_decode", "decode_workspace_bytes", "prefill_workspace_bytes", "mtd_qkv_proj",
+    "mtd_o_proj",
 ]

@@ -62,6 +62,24 @@ int check_scale(float scale) {
   return MTD_OK;
 }
 
+// The projections' shape arguments.
+int check_proj_shape(int32_t n_tok, int32_t hidden, int32_t num_q_heads, int32_t num_kv_heads,
+                     int32_t head_dim) {
+  if (n_tok < 0) return fail(MTD_ERR_INVALID_ARG, "n_tok = %d", n_tok);
+  if (hidden <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0)
+    return fail(MTD_ERR_INVALID_ARG, "hidden %d, num_q_heads %d, num_kv_heads %d, head_dim %d",
+                hidden, num_q_heads, num_kv_heads, head_dim);
+  if (hidden != mtd::kHidden || num_q_heads != mtd::kQHeads || num_kv_heads != mtd::kKvHeads ||
+      head_dim != mtd::kHeadDim)
+    return fail(MTD_ERR_UNSUPPORTED,
+                "hidden %d, heads %d/%d, head_dim %d (supported: %d, %d/%d, %d)", hidden,
+                num_q_heads, num_kv_heads, head_dim, mtd::kHidden, mtd::kQHeads, mtd::kKvHeads,
+                mtd::kHeadDim);
+  return MTD_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
 mtd::KvPools pools(const mtd_kv_layer_t* kv) {
   return mtd::KvPools{static_cast<uint16_t*>(kv->k_pages), static_cast<uint16_t*>(kv->v_pages),
                       kv->num_pages};
@@ -159,6 +177,36 @@ int mtd_attn_decode(const mtd_kv_layer_t* kv, const void* q, const int32_t* kv_l
                                        block_tables, bt_stride, batch, max_kv_len, scale,
                                        workspace, out, lse, static_cast<hipStream_t>(stream)),
                     "decode launch");
+}
+
+int mtd_qkv_proj(const void* x, const void* w_qkv, int32_t n_tok, int32_t hidden,
+                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, void* q, void* k_new,
+                 void* v_new, void* stream) {
+  int st = check_proj_shape(n_tok, hidden, num_q_heads, num_kv_heads, head_dim);
+  if (st != MTD_OK) return st;
+  if (x == nullptr || w_qkv == nullptr || q == nullptr || k_new == nullptr || v_new == nullptr)
+    return fail(MTD_ERR_INVALID_ARG, "x / w_qkv / q / k_new / v_new is NULL");
+  if (!aligned16(x) || !aligned16(w_qkv) || !aligned16(q) || !aligned16(k_new) || !aligned16(v_new))
+    return fail(MTD_ERR_INVALID_ARG, "x / w_qkv / q / k_new / v_new not 16-byte aligned");
+  return hip_status(mtd::launch_qkv_proj(static_cast<const uint16_t*>(x),
+                                         static_cast<const uint16_t*>(w_qkv), n_tok,
+                                         static_cast<uint16_t*>(q), static_cast<uint16_t*>(k_new),
+                                         static_cast<uint16_t*>(v_new),
+                                         static_cast<hipStream_t>(stream)),
+                    "qkv projection launch");
+}
+
+int mtd_o_proj(const float* attn, const void* w_o, int32_t n_tok, int32_t num_q_heads,
+               int32_t head_dim, int32_t hidden, void* out, void* stream) {
+  int st = check_proj_shape(n_tok, hidden, num_q_heads, mtd::kKvHeads, head_dim);
+  if (st != MTD_OK) return st;
+  if (attn == nullptr || w_o == nullptr || out == nullptr)
+    return fail(MTD_ERR_INVALID_ARG, "attn / w_o / out is NULL");
+  if (!aligned16(attn) || !aligned16(w_o) || !aligned16(out))
+    return fail(MTD_ERR_INVALID_ARG, "attn / w_o / out not 16-byte aligned");
+  return hip_status(mtd::launch_o_proj(attn, static_cast<const uint16_t*>(w_o), n_tok,
+                                       static_cast<uint16_t*>(out), static_cast<hipStream_t>(stream)),
+                    "output projection launch");
 }
 
 const char* mtd_status_string(int status) {

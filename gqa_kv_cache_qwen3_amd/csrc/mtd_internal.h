@@ -14,6 +14,7 @@ constexpr int kGroup = kQHeads / kKvHeads;  // query heads per KV head
 constexpr int kHeadDim = 128;
 constexpr int kPage = 64;
 constexpr int kMaxContext = 131072;
+constexpr int kHidden = 1024;  // decoder hidden size (input of the QKV map, output of o_proj)
 // Decode split-K partition of a request of len tokens: consecutive runs of split_tokens(len)
 // logical tokens (whole pages).  A request of up to 1024 tokens is cut into one split per page
 // (up to 16), so even a lone short request spreads over many wavefronts; longer ones use 512-token
@@ -62,5 +63,15 @@ size_t decode_workspace_bytes(int batch, int max_kv_len);
 hipError_t launch_decode(const KvPools& kv, const uint16_t* q, const int32_t* kv_lens,
                          const int32_t* block_tables, int bt_stride, int batch, int max_kv_len,
                          float scale, void* workspace, float* out, float* lse, hipStream_t stream);
+
+// The projections around the attention (n_tok >= 0; pointers 16-byte aligned):
+//   x bf16 [n_tok][kHidden], w_qkv bf16 [(kQHeads + 2 kKvHeads) kHeadDim][kHidden]
+//     -> q bf16 [n_tok][kQHeads][kHeadDim], k, v bf16 [n_tok][kKvHeads][kHeadDim];
+//   attn float32 [n_tok][kQHeads][kHeadDim], w_o bf16 [kHidden][kQHeads kHeadDim]
+//     -> out bf16 [n_tok][kHidden].
+hipError_t launch_qkv_proj(const uint16_t* x, const uint16_t* w_qkv, int n_tok, uint16_t* q,
+                           uint16_t* k, uint16_t* v, hipStream_t stream);
+hipError_t launch_o_proj(const float* attn, const uint16_t* w_o, int n_tok, uint16_t* out,
+                         hipStream_t stream);
 
 }  // namespace mtd

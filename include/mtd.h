@@ -17,6 +17,11 @@
  *                           batch of requests ("Optimizing ASR Models ...", section ASR Model
  *                           Primer, Autoregressive Decode, and section Batched Inference)
  *
+ * and two linear maps sit on either side of them in every decoder layer:
+ *
+ *   mtd_qkv_proj            hidden states -> q, k, v of new tokens
+ *   mtd_o_proj              attention output -> hidden states
+ *
  * Everything computed is exact softmax attention:
  *     s_j = scale * <q, k_j>  for visible keys j;  LSE = ln sum_j exp(s_j);  O = sum_j exp(s_j - LSE) v_j
  * Query head h reads KV head h / (num_q_heads / num_kv_heads).
@@ -55,7 +60,7 @@
 extern "C" {
 #endif
 
-#define MTD_ABI_VERSION 2
+#define MTD_ABI_VERSION 3
 
 /* Status codes. */
 #define MTD_OK               0
@@ -183,6 +188,46 @@ int mtd_attn_decode(const mtd_kv_layer_t* kv, const void* q, const int32_t* kv_l
                     const int32_t* block_tables, int32_t bt_stride, int32_t batch,
                     int32_t max_kv_len, int32_t num_q_heads, float scale, void* workspace,
                     size_t workspace_bytes, float* out, float* lse, void* stream);
+
+/*
+ * mtd_qkv_proj - the QKV projection of new tokens: q = Wq x, k = Wk x, v = Wv x.
+ *
+ * Each decoder layer maps the hidden states (size 1024) of the tokens it processes to their
+ * queries and their new keys and values ("Optimizing ASR Models ...", section ASR Model Primer,
+ * component table: Qwen3, hidden 1024, GQA 16/8; cookbook section Model Architecture).  No bias.
+ * The outputs have the layouts mtd_kv_append and the attention calls take.
+ *
+ *   x               bf16 [n_tok][hidden]
+ *   w_qkv           bf16 [(num_q_heads + 2 num_kv_heads) * head_dim][hidden], the rows of Wq,
+ *                   then Wk, then Wv ([out][in] layout: row n makes output feature n)
+ *   n_tok           >= 0 (0 enqueues nothing);  hidden 1024;  num_q_heads 16;  num_kv_heads 8;
+ *                   head_dim 128
+ *   q               bf16 [n_tok][num_q_heads][head_dim], written: features 0 .. 2047
+ *   k_new, v_new    bf16 [n_tok][num_kv_heads][head_dim], written: features 2048 .. 3071 and
+ *                   3072 .. 4095
+ * Feature f of a part is (head f / head_dim, dim f % head_dim).  Products are summed in float32
+ * from bf16 operands and each result is rounded to bf16 (nearest, ties to even).  Every pointer
+ * must be 16-byte aligned (else MTD_ERR_INVALID_ARG).  The result of a token does not depend on
+ * n_tok or on the other tokens.
+ */
+int mtd_qkv_proj(const void* x, const void* w_qkv, int32_t n_tok, int32_t hidden,
+                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, void* q, void* k_new,
+                 void* v_new, void* stream);
+
+/*
+ * mtd_o_proj - the output projection of attention outputs: y = Wo o.
+ *
+ *   attn            float32 [n_tok][num_q_heads][head_dim], the attention output O (as written by
+ *                   mtd_attn_prefill_chunk / mtd_attn_decode); rounded to bf16 (nearest, ties to
+ *                   even), the decoder's activation type, before the product
+ *   w_o             bf16 [hidden][num_q_heads * head_dim] ([out][in] layout; input feature
+ *                   h * head_dim + d is head h, dim d)
+ *   n_tok           >= 0 (0 enqueues nothing);  num_q_heads 16;  head_dim 128;  hidden 1024
+ *   out             bf16 [n_tok][hidden], written (float32 sums rounded to bf16)
+ * Every pointer must be 16-byte aligned (else MTD_ERR_INVALID_ARG).
+ */
+int mtd_o_proj(const float* attn, const void* w_o, int32_t n_tok, int32_t num_q_heads,
+               int32_t head_dim, int32_t hidden, void* out, void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* mtd_status_string(int status);

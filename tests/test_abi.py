@@ -32,7 +32,7 @@ def test_header_declares_the_three_calls():
     names = declared_functions()
     for n in ("mtd_kv_append", "mtd_attn_prefill_chunk", "mtd_attn_prefill_workspace_bytes",
               "mtd_attn_decode", "mtd_attn_decode_workspace_bytes", "mtd_status_string",
-              "mtd_last_error", "mtd_abi_version"):
+              "mtd_last_error", "mtd_abi_version", "mtd_qkv_proj", "mtd_o_proj"):
         assert n in names
 
 
@@ -224,3 +224,62 @@ def test_binding_rejects_cpu_tensors():
         mtd.kv_layer(cpu, cpu)
     with pytest.raises(TypeError):
         mtd.kv_layer(cpu.float(), cpu.float())
+
+
+def qkv(lib, **kw):
+    a = dict(x=FAKE, w=FAKE, n_tok=5, hidden=1024, hq=16, hkv=8, d=128, q=FAKE, k=FAKE, v=FAKE)
+    a.update(kw)
+    return lib.mtd_qkv_proj(a["x"], a["w"], a["n_tok"], a["hidden"], a["hq"], a["hkv"], a["d"],
+                            a["q"], a["k"], a["v"], None)
+
+
+def oproj(lib, **kw):
+    a = dict(attn=FAKE, w=FAKE, n_tok=5, hq=16, d=128, hidden=1024, out=FAKE)
+    a.update(kw)
+    return lib.mtd_o_proj(a["attn"], a["w"], a["n_tok"], a["hq"], a["d"], a["hidden"], a["out"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_tok=-1), mtd.MTD_ERR_INVALID_ARG),
+    (dict(hidden=0), mtd.MTD_ERR_INVALID_ARG),
+    (dict(hidden=2048), mtd.MTD_ERR_UNSUPPORTED),
+    (dict(hq=32), mtd.MTD_ERR_UNSUPPORTED),
+    (dict(d=64), mtd.MTD_ERR_UNSUPPORTED),
+    (dict(x=None), mtd.MTD_ERR_INVALID_ARG),
+    (dict(w=None), mtd.MTD_ERR_INVALID_ARG),
+    (dict(q=None), mtd.MTD_ERR_INVALID_ARG),
+    (dict(k=None), mtd.MTD_ERR_INVALID_ARG),
+    (dict(v=None), mtd.MTD_ERR_INVALID_ARG),
+    (dict(x=FAKE + 8), mtd.MTD_ERR_INVALID_ARG),
+    (dict(w=FAKE + 2), mtd.MTD_ERR_INVALID_ARG),
+    (dict(v=FAKE + 4), mtd.MTD_ERR_INVALID_ARG),
+])
+def test_qkv_proj_validation(lib, kw, code):
+    assert qkv(lib, **kw) == code
+    assert lib.mtd_last_error().decode() != ""
+
+
+def test_qkv_proj_kv_heads_checked(lib):
+    assert qkv(lib, hkv=4) == mtd.MTD_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_tok=-3), mtd.MTD_ERR_INVALID_ARG),
+    (dict(hidden=512), mtd.MTD_ERR_UNSUPPORTED),
+    (dict(hq=8), mtd.MTD_ERR_UNSUPPORTED),
+    (dict(d=0), mtd.MTD_ERR_INVALID_ARG),
+    (dict(attn=None), mtd.MTD_ERR_INVALID_ARG),
+    (dict(w=None), mtd.MTD_ERR_INVALID_ARG),
+    (dict(out=None), mtd.MTD_ERR_INVALID_ARG),
+    (dict(attn=FAKE + 4), mtd.MTD_ERR_INVALID_ARG),
+    (dict(out=FAKE + 2), mtd.MTD_ERR_INVALID_ARG),
+])
+def test_o_proj_validation(lib, kw, code):
+    assert oproj(lib, **kw) == code
+    assert lib.mtd_last_error().decode() != ""
+
+
+def test_projections_of_no_tokens_enqueue_nothing(lib):
+    """n_tok = 0 is valid and returns before any HIP call (so it runs without a GPU)."""
+    assert qkv(lib, n_tok=0) == mtd.MTD_OK
+    assert oproj(lib, n_tok=0) == mtd.MTD_OK

@@ -26,6 +26,7 @@ import numpy as np
 HQ = 16          # query heads
 HKV = 8          # key/value heads
 HEAD_DIM = 128
+HIDDEN = 1024    # decoder hidden size (input of the QKV projection, output of o_proj)
 PAGE = 64        # tokens per page
 SCALE = 1.0 / math.sqrt(HEAD_DIM)
 CHUNK = 4096     # prefill chunk length
@@ -88,6 +89,24 @@ def normal_bf16(shape, seed: int, device="cpu"):
     gen = torch.Generator(device=device)
     gen.manual_seed(seed)
     return torch.randn(*shape, generator=gen, device=device, dtype=torch.float32).to(torch.bfloat16)
+
+
+def normal_bf16_std(shape, std: float, seed: int, device="cpu"):
+    """fp32 N(0, std^2) cast to bf16 with round-to-nearest-even (random projection weights use
+    std = 1/sqrt(fan_in), so outputs keep the inputs' scale)."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    return (torch.randn(*shape, generator=gen, device=device, dtype=torch.float32) * std).to(torch.bfloat16)
+
+
+def projection_weights(seed: int, device="cpu"):
+    """Random bf16 weights of one layer's projections: W_qkv [(16 + 8 + 8) * 128][1024] (rows Wq,
+    Wk, Wv) and W_o [1024][16 * 128], both in the [out][in] layout."""
+    n_qkv = (HQ + 2 * HKV) * HEAD_DIM
+    w_qkv = normal_bf16_std((n_qkv, HIDDEN), 1.0 / math.sqrt(HIDDEN), seed, device)
+    w_o = normal_bf16_std((HIDDEN, HQ * HEAD_DIM), 1.0 / math.sqrt(HQ * HEAD_DIM), seed + 1, device)
+    return w_qkv, w_o
 
 
 def lowrank_keys(n_tokens: int, seed: int, device="cpu", rank: int = 4, weight: float = 2.0):
