@@ -18,8 +18,13 @@
 // 64 quarter (w / 2, w % 2) as 2 x 2 blocks of v_mfma_f32_32x32x16_bf16 with fp32 accumulators.
 // K advances 64 at a time through two LDS stages: right after the barrier that publishes stage
 // s, the loads of the next 64-wide slice into stage s^1 are issued, so they travel while stage s
-// is multiplied.  Two workgroups fit per CU (64 KiB of LDS each), so the matrix pipe of a SIMD
-// always has a second wave to switch to at a barrier.
+// is multiplied.  The stages are separate arrays picked at compile time (the loop is unrolled by
+// two), which lets the compiler see that the reads of one stage never wait on the loads into the
+// other.  Two workgroups fit per CU (64 KiB of LDS each).  At 128 x 128 the tile does 64 flops
+// per staged byte, so the kernel is bound by the L2 -> LDS traffic well before the matrix pipe.
+// Calls with at most 64 tokens use proj_skinny_kernel instead, which spreads K over the waves.
+// Both kernels add the products in one order (fixed K slices, see kKSlice), so a token's result
+// is the same whatever the token count and whichever kernel runs.
 //
 // Staging.  A 128 x 64 bf16 slice is two column groups of 64 bytes (k 32j .. 32j+31) of 128 rows;
 // the 16-byte slot of (row r, chunk c) is 512 (c/4) + 4 r + ((c%4) ^ ((r/4)%4)).  bf16 slices
@@ -29,10 +34,11 @@
 // the same layout.  MFMA operands are ds_read_b128 of one row's 16-byte chunk: A rows for the A
 // operand and W rows for the B operand, both free of bank conflicts under the XOR swizzle.
 //
-// Placement.  Workgroup i runs on XCD i % 8.  The tiles are numbered so that each XCD takes one
-// contiguous eighth of them, either whole rows of tiles (every XCD then reads W whole and an
-// eighth of A) or whole columns (an eighth of W, all of A); the host picks the split that reads
-// fewer bytes, so the replicated operand is the smaller one and stays in the XCD's L2.
+// Placement.  Workgroup i runs on XCD i % 8.  Each XCD owns an eighth of the tile rows (every
+// XCD then reads W whole and an eighth of A) or of the tile columns (an eighth of W, all of A);
+// the host picks the split whose replicated operand is the smaller.  Within an XCD the owned
+// index varies fastest, so the workgroups in flight together touch few tiles of the replicated
+// operand and each is brought into the XCD's L2 once rather than once per owned row.
 #include "device_util.h"
 #include "mtd_internal.h"
 
@@ -44,6 +50,12 @@ constexpr int kTN = 128;    // tile columns (output features)
 constexpr int kTK = 64;     // K per stage
 constexpr int kThreads = 256;
 constexpr int kSliceBytes = kTM * kTK * 2;  // 16 KiB per operand per stage
+// Summation order, the same in both kernels: K is cut into slices of kKSlice; each slice's
+// products are accumulated by one chain of MFMAs starting from zero, and the slice sums are then
+// added in slice order to a running total that starts from zero.  So a token's outputs never
+// depend on how many tokens share the call or which kernel serves it.
+constexpr int kKSlice = 128;
+constexpr int kSkinnyRows = 64;  // calls with at most this many tokens use proj_skinny_kernel
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef const __attribute__((address_space(1))) void global_cvoid_t;
@@ -108,18 +120,33 @@ __global__ __launch_bounds__(kThreads, 2) void proj_gemm_kernel(const void* __re
                                                                 int rows, const uint16_t* __restrict__ w,
                                                                 int k_dim, int n_tm, int n_tn,
                                                                 int rows_major, OutMap out) {
-  __shared__ __attribute__((aligned(1024))) uint8_t s_a[2][kSliceBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t s_w[2][kSliceBytes];
+  // One array per stage: with the stage known at compile time, the compiler can see that the
+  // loads into one stage never touch the LDS being read from the other, and does not wait for them.
+  __shared__ __attribute__((aligned(1024))) uint8_t s_a0[kSliceBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_a1[kSliceBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_w0[kSliceBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_w1[kSliceBytes];
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
 
-  // Tile of this workgroup: XCD blockIdx.x % 8 takes a contiguous eighth of the tile list.
-  const int total = n_tm * n_tn;
+  // Tile of this workgroup.  XCD x = blockIdx.x % 8 owns an eighth of the rows of tiles (or of
+  // the columns); inside it the owned index varies fastest, so the workgroups running at once
+  // share a few tiles of the replicated operand and each of those is fetched into the XCD's L2
+  // once.
   const int id = blockIdx.x;
-  const int t = (total % 8 == 0) ? (id % 8) * (total / 8) + id / 8 : id;
-  const int tm = rows_major ? t / n_tn : t % n_tm;
-  const int tn = rows_major ? t % n_tn : t / n_tm;
+  const int x = id % 8, local = id / 8;
+  int tm, tn;
+  if (rows_major && n_tm % 8 == 0) {
+    tm = x * (n_tm / 8) + local % (n_tm / 8);
+    tn = local / (n_tm / 8);
+  } else if (!rows_major && n_tn % 8 == 0) {
+    tn = x * (n_tn / 8) + local % (n_tn / 8);
+    tm = local / (n_tn / 8);
+  } else {
+    tm = id / n_tn;
+    tn = id % n_tn;
+  }
   const int row0 = tm * kTM;
   const int col0 = tn * kTN;
   const int rows_valid = min(kTM, rows - row0);
@@ -135,39 +162,36 @@ __global__ __launch_bounds__(kThreads, 2) void proj_gemm_kernel(const void* __re
     wbase[e] = 64 * (64 * wn + n) + sw;
   }
 
-  floatx16_t acc[2][2];
+  floatx16_t acc[2][2], sum[2][2];  // the current K slice; the slices before it
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = sum[i][j][v] = 0.f;
 
-  const int nk = k_dim / kTK;
+  const int nk = k_dim / kTK;  // even (k_dim is a multiple of kKSlice)
   F32Slice fa;
-  auto issue = [&](int kt, int st) {
-    dma_slice(w, k_dim, col0, kTN, kt * kTK, s_w[st], wave, lane);
+  auto issue = [&](int kt, uint8_t* a_dst, uint8_t* w_dst) {
+    dma_slice(w, k_dim, col0, kTN, kt * kTK, w_dst, wave, lane);
     if constexpr (kAF32)
       load_f32_slice(fa, static_cast<const float*>(a_ptr), lda, row0, rows_valid, kt * kTK, wave, lane);
     else
-      dma_slice(static_cast<const uint16_t*>(a_ptr), lda, row0, rows_valid, kt * kTK, s_a[st], wave, lane);
+      dma_slice(static_cast<const uint16_t*>(a_ptr), lda, row0, rows_valid, kt * kTK, a_dst, wave, lane);
   };
-
-  issue(0, 0);
-  if constexpr (kAF32) store_f32_slice(fa, s_a[0], wave, lane);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int st = kt & 1;
-    __syncthreads();  // stage st complete for every wave; stage st^1 no longer read
-    if (kt + 1 < nk) issue(kt + 1, st ^ 1);
+  // K step kt: stage (cur_a, cur_w) holds slice kt; slice kt+1 goes to (nxt_a, nxt_w).
+  auto step = [&](int kt, const uint8_t* cur_a, const uint8_t* cur_w, uint8_t* nxt_a, uint8_t* nxt_w) {
+    __syncthreads();  // the current stage complete for every wave; the other no longer read
+    if (kt + 1 < nk) issue(kt + 1, nxt_a, nxt_w);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       bf16x8_t af[2], wf[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         af[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(
-                                                 s_a[st] + abase[ks & 1] + 8192 * (ks >> 1) + 2048 * i));
+                                                 cur_a + abase[ks & 1] + 8192 * (ks >> 1) + 2048 * i));
         wf[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(
-                                                 s_w[st] + wbase[ks & 1] + 8192 * (ks >> 1) + 2048 * i));
+                                                 cur_w + wbase[ks & 1] + 8192 * (ks >> 1) + 2048 * i));
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
@@ -176,7 +200,25 @@ __global__ __launch_bounds__(kThreads, 2) void proj_gemm_kernel(const void* __re
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], wf[j], acc[i][j], 0, 0, 0);
     }
     if constexpr (kAF32)
-      if (kt + 1 < nk) store_f32_slice(fa, s_a[st ^ 1], wave, lane);
+      if (kt + 1 < nk) store_f32_slice(fa, nxt_a, wave, lane);
+    if ((kt + 1) % (kKSlice / kTK) == 0) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            sum[i][j][v] += acc[i][j][v];
+            acc[i][j][v] = 0.f;
+          }
+    }
+  };
+
+  issue(0, s_a0, s_w0);
+  if constexpr (kAF32) store_f32_slice(fa, s_a0, wave, lane);
+  for (int kt = 0; kt < nk; kt += 2) {
+    step(kt, s_a0, s_w0, s_a1, s_w1);
+    step(kt + 1, s_a1, s_w1, s_a0, s_w0);
   }
 
   // Epilogue: accumulator element v of block (i, j) is C[row0 + 64wm + 32i + 8(v/4) + 4hk + v%4]
@@ -193,9 +235,75 @@ __global__ __launch_bounds__(kThreads, 2) void proj_gemm_kernel(const void* __re
       if (r < rows_valid) {
         uint16_t* drow = dst + (size_t)(row0 + r) * ld + cbase;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) drow[32 * j] = (uint16_t)pack_bf16x2(acc[i][j][v], 0.f);
+        for (int j = 0; j < 2; ++j) drow[32 * j] = (uint16_t)pack_bf16x2(sum[i][j][v], 0.f);
       }
     }
+}
+
+// Few tokens (at most 64): the weights dominate the bytes, so the grid is spread over K instead
+// of tokens.  Workgroup (column block x, row block y) = 32 columns of W against 32 tokens; its
+// wave s takes K slice s (k_dim / kKSlice waves), loads the slice's MFMA fragments straight from
+// global memory and runs the slice's MFMA chain; the slice sums meet in LDS and are added in
+// slice order.
+template <bool kAF32>
+__global__ __launch_bounds__(1024) void proj_skinny_kernel(const void* __restrict__ a_ptr, int lda,
+                                                           int rows, const uint16_t* __restrict__ w,
+                                                           int k_dim, OutMap out) {
+  constexpr int kMaxSlices = 16;
+  __shared__ float s_part[kMaxSlices][16][64];  // [slice][accumulator element][lane]
+  const int tid = threadIdx.x;
+  const int slice = tid >> 6;
+  const int lane = tid & 63;
+  const int n_slices = blockDim.x >> 6;
+  const int n = lane & 31, hk = lane >> 5;
+  const int col0 = 32 * blockIdx.x;
+  const int row0 = 32 * blockIdx.y;
+  const int k0 = slice * kKSlice + 8 * hk;
+
+  const uint16_t* wrow = w + (size_t)(col0 + n) * k_dim + k0;
+  const int r = min(row0 + n, rows - 1);
+  bf16x8_t wf[kKSlice / 16], af[kKSlice / 16];
+#pragma unroll
+  for (int ks = 0; ks < kKSlice / 16; ++ks)
+    wf[ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(wrow + 16 * ks));
+  if constexpr (kAF32) {
+    const float* arow = static_cast<const float*>(a_ptr) + (size_t)r * lda + k0;
+#pragma unroll
+    for (int ks = 0; ks < kKSlice / 16; ++ks) {
+      const float4 lo = *reinterpret_cast<const float4*>(arow + 16 * ks);
+      const float4 hi = *reinterpret_cast<const float4*>(arow + 16 * ks + 4);
+      const uint4 packed = make_uint4(pack_bf16x2(lo.x, lo.y), pack_bf16x2(lo.z, lo.w),
+                                      pack_bf16x2(hi.x, hi.y), pack_bf16x2(hi.z, hi.w));
+      af[ks] = __builtin_bit_cast(bf16x8_t, packed);
+    }
+  } else {
+    const uint16_t* arow = static_cast<const uint16_t*>(a_ptr) + (size_t)r * lda + k0;
+#pragma unroll
+    for (int ks = 0; ks < kKSlice / 16; ++ks)
+      af[ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(arow + 16 * ks));
+  }
+  floatx16_t acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < kKSlice / 16; ++ks)
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks], wf[ks], acc, 0, 0, 0);
+#pragma unroll
+  for (int v = 0; v < 16; ++v) s_part[slice][v][lane] = acc[v];
+  __syncthreads();
+
+  // Element e = (accumulator element v, lane l): C[row0 + 8(v/4) + 4(l/32) + v%4][col0 + l%32].
+  const int reg = (col0 >= out.lo[2]) ? 2 : (col0 >= out.lo[1]) ? 1 : 0;
+  uint16_t* dst = out.dst[reg];
+  const int ld = out.ld[reg];
+  for (int e = tid; e < 16 * 64; e += blockDim.x) {
+    const int v = e >> 6, l = e & 63;
+    const int rr = row0 + 8 * (v >> 2) + 4 * (l >> 5) + (v & 3);
+    if (rr >= rows) continue;
+    float total = 0.f;
+    for (int sl = 0; sl < n_slices; ++sl) total += s_part[sl][v][l];
+    dst[(size_t)rr * ld + col0 - out.lo[reg] + (l & 31)] = (uint16_t)pack_bf16x2(total, 0.f);
+  }
 }
 
 // The operand split (see Placement) that reads fewer bytes.
@@ -220,6 +328,11 @@ hipError_t launch_qkv_proj(const uint16_t* x, const uint16_t* w_qkv, int n_tok, 
   om.lo[0] = 0;
   om.lo[1] = kQHeads * kHeadDim;
   om.lo[2] = (kQHeads + kKvHeads) * kHeadDim;
+  if (n_tok <= kSkinnyRows) {
+    proj_skinny_kernel<false><<<dim3(kN / 32, (n_tok + 31) / 32), dim3(64 * (kHidden / kKSlice)), 0, stream>>>(
+        x, kHidden, n_tok, w_qkv, kHidden, om);
+    return hipGetLastError();
+  }
   const int rows_major = rows_major_split(n_tok, kHidden * 2, (size_t)kN * kHidden * 2);
   proj_gemm_kernel<false><<<dim3(n_tm * n_tn), dim3(kThreads), 0, stream>>>(
       x, kHidden, n_tok, w_qkv, kHidden, n_tm, n_tn, rows_major, om);
@@ -237,6 +350,11 @@ hipError_t launch_o_proj(const float* attn, const uint16_t* w_o, int n_tok, uint
     om.dst[r] = out;
     om.ld[r] = kHidden;
     om.lo[r] = 0;
+  }
+  if (n_tok <= kSkinnyRows) {
+    proj_skinny_kernel<true><<<dim3(kHidden / 32, (n_tok + 31) / 32), dim3(64 * (kK / kKSlice)), 0, stream>>>(
+        attn, kK, n_tok, w_o, kK, om);
+    return hipGetLastError();
   }
   const int rows_major = rows_major_split(n_tok, kK * 4, (size_t)kHidden * kK * 2);
   proj_gemm_kernel<true><<<dim3(n_tm * n_tn), dim3(kThreads), 0, stream>>>(

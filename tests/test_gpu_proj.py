@@ -50,7 +50,7 @@ def _weights(dev):
     return W.projection_weights(W.torch_seed(TAG, 0), dev)
 
 
-@pytest.mark.parametrize("n_tok", [1, 37, 128, 300, 439])
+@pytest.mark.parametrize("n_tok", [1, 37, 64, 65, 128, 300, 439])
 def test_qkv_proj_matches_oracle(n_tok):
     log(f"qkv projection n_tok={n_tok}")
     w_qkv, _ = _weights("cuda")
@@ -67,7 +67,7 @@ def test_qkv_proj_matches_oracle(n_tok):
     _check("v", v, v_ref, bound[:, nq + nkv:].reshape(v_ref.shape))
 
 
-@pytest.mark.parametrize("n_tok", [1, 37, 64, 300, 439])
+@pytest.mark.parametrize("n_tok", [1, 37, 64, 65, 300, 439])
 def test_o_proj_matches_oracle(n_tok):
     log(f"output projection n_tok={n_tok}")
     _, w_o = _weights("cuda")
@@ -108,14 +108,16 @@ def test_projections_full_chunk():
 
 def test_token_results_do_not_depend_on_the_batch():
     """Rows of a 300-token call equal, bit for bit, the same tokens projected alone or in a
-    different-sized call (each output element is one lane's fixed-order sum)."""
+    different-sized call, whichever kernel serves the call (at most 64 tokens: K split over the
+    waves; more: 128 x 128 tiles): both sum each 128-wide K slice with one MFMA chain from zero
+    and add the slice sums in order."""
     log("projections: batch invariance")
     w_qkv, w_o = _weights("cuda")
     x = W.normal_bf16((300, W.HIDDEN), W.torch_seed(TAG, 5), "cuda")
     attn = W.normal_bf16((300, W.HQ, W.HEAD_DIM), W.torch_seed(TAG, 6), "cuda").float()
     full = mtd.mtd_qkv_proj(x, w_qkv)
     y_full = mtd.mtd_o_proj(attn, w_o)
-    for lo, hi in [(0, 37), (128, 129), (250, 300)]:
+    for lo, hi in [(0, 37), (128, 129), (0, 64), (0, 65), (200, 300)]:
         part = mtd.mtd_qkv_proj(x[lo:hi].contiguous(), w_qkv)
         y_part = mtd.mtd_o_proj(attn[lo:hi].contiguous(), w_o)
         for a, b in zip(full, part):
