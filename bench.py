@@ -9,7 +9,9 @@ shared pool of 64-token pages.  Per step:
     mtd_attn_prefill_chunk  A's chunk over its 36,864 keys
     mtd_attn_decode         31 requests (split-K + merge)
 Other workloads (--workload): decode16 (16 requests, L in [27000, 30000]), prefill90min (17 chunks
-of a 67,500-token request), fulldepth_decode (28 layers x 64 requests, 128K cap).
+of a 67,500-token request), fulldepth_decode (28 layers x 64 requests, 128K cap), and the same
+steps as whole attention blocks with the QKV and output projections around the attention
+(mixed_block, fulldepth_block), besides mixed_step_overlap and decode_graph.
 
 Prints one JSON line.  `value` is decode-attention HBM throughput (algorithmic bytes / time) and
 `prefill` carries the chunked-prefill TFLOP/s; `roofline` is for the kernel that takes the most
@@ -499,6 +501,148 @@ class FullDepth:
                           f"KV tokens, {t_dec:.1f} s); fp64 numpy"}
 
 
+def proj_work(n_tok: int):
+    """Algorithmic flops and HBM bytes of one QKV projection and one output projection call:
+    weights once, activations in and out once (bf16, the float32 attention output for o_proj)."""
+    n_qkv, n_o = (W.HQ + 2 * W.HKV) * W.HEAD_DIM, W.HQ * W.HEAD_DIM
+    qkv = {"flops": 2.0 * n_tok * W.HIDDEN * n_qkv, "bytes": 2 * (n_qkv * W.HIDDEN + n_tok * W.HIDDEN + n_tok * n_qkv)}
+    o = {"flops": 2.0 * n_tok * n_o * W.HIDDEN, "bytes": 2 * W.HIDDEN * n_o + 4 * n_tok * n_o + 2 * n_tok * W.HIDDEN}
+    return qkv, o
+
+
+def proj_results(samples_qkv, samples_o, n_tok, calls_per_sample=1):
+    qkv_w, o_w = proj_work(n_tok)
+    out = {}
+    for name, samples, wk in (("qkv_proj", samples_qkv, qkv_w), ("o_proj", samples_o, o_w)):
+        ms = float(np.sum(samples)) / (len(samples) * calls_per_sample)
+        tfs = wk["flops"] / (ms * 1e-3) / 1e12
+        gbs = wk["bytes"] / (ms * 1e-3) / 1e9
+        out[name] = {"ms": ms, "tokens": n_tok, "tflops": tfs, "mfma_frac": tfs / MFMA_BF16_PEAK_TFLOPS,
+                     "gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS, "flops": wk["flops"], "bytes": wk["bytes"]}
+    return out
+
+
+class MixedBlock(MixedStep):
+    """The mixed scheduler step as a whole attention block: the QKV projection of all 4127 new tokens
+    (the chunk's 4096 and one per decode request) feeds the append, the prefill and the decode, and
+    the output projection maps all their attention outputs back to hidden size."""
+    name = "mixed_block"
+
+    def __init__(self, dev):
+        super().__init__(dev)
+        torch, mtd = self.torch, self.mtd
+        n_new = self.chunk + len(self.lens)
+        self.w_qkv, self.w_o = W.projection_weights(W.torch_seed(W.MIXED.tag, 7), dev)
+        self.x = W.normal_bf16((n_new, W.HIDDEN), W.torch_seed(W.MIXED.tag, 8), dev)
+        self.q_all = torch.empty((n_new, W.HQ, W.HEAD_DIM), dtype=torch.bfloat16, device=dev)
+        self.q_a, self.q_d = self.q_all[:self.chunk], self.q_all[self.chunk:]
+        self.o_all = torch.empty((n_new, W.HQ, W.HEAD_DIM), dtype=torch.float32, device=dev)
+        self.o_a, self.o_d = self.o_all[:self.chunk], self.o_all[self.chunk:]
+        self.y = torch.empty((n_new, W.HIDDEN), dtype=torch.bfloat16, device=dev)
+        self.n_new = n_new
+        self.timer = Timer(["qkv_proj", "append", "prefill", "decode", "o_proj"])
+
+    def step(self, events=None):
+        mtd = self.mtd
+        if events: events[0].record()
+        mtd.mtd_qkv_proj(self.x, self.w_qkv, self.q_all, self.k_new, self.v_new)
+        if events: events[1].record()
+        mtd.mtd_kv_append(self.k, self.v, self.k_new, self.v_new, self.cu, self.start, self.bt_all)
+        if events: events[2].record()
+        mtd.mtd_attn_prefill_chunk(self.k, self.v, self.q_a, self.prefix, self.bt_a, W.SCALE, self.o_a, self.l_a,
+                                   self.ws_p)
+        if events: events[3].record()
+        mtd.mtd_attn_decode(self.k, self.v, self.q_d, self.kv_lens, self.bt_dec, self.max_len, W.SCALE,
+                            self.ws, self.o_d, self.l_d)
+        if events: events[4].record()
+        mtd.mtd_o_proj(self.o_all, self.w_o, self.y)
+        if events: events[5].record()
+
+    def config(self):
+        c = super().config()
+        c["workload"] = ("mixed_block: the mixed step as an attention block: QKV projection of the 4127 new "
+                         "tokens (hidden 1024 -> 16+8+8 heads x 128, random bf16 weights) -> append -> "
+                         "prefill chunk 4096 at prefix 32768 + decode of 31 requests -> output projection")
+        c["hidden"] = W.HIDDEN
+        return c
+
+    def results(self):
+        res = super().results()
+        res["proj"] = proj_results(self.timer.samples["qkv_proj"], self.timer.samples["o_proj"], self.n_new)
+        return res
+
+    cpu_baseline = None
+
+
+class FullDepthBlock(FullDepth):
+    """Full-depth decode with the projections around each layer's attention: per step and layer,
+    the QKV projection of the 64 requests' hidden states, the append of the new K/V, decode
+    attention, and the output projection whose result is the next layer's input."""
+    name = "fulldepth_block"
+
+    def __init__(self, dev):
+        import torch
+        p = W.FULLDEPTH.params
+        # the weights first, so that the pools are sized to the memory that is left
+        self.w = [W.projection_weights(W.torch_seed(W.FULLDEPTH.tag, 50, l), dev) for l in range(p["layers"])]
+        super().__init__(dev)
+        b = len(self.lens0)
+        self.x0 = [W.normal_bf16((b, W.HIDDEN), W.torch_seed(W.FULLDEPTH.tag, 51, s), dev) for s in range(4)]
+        self.x = torch.empty((b, W.HIDDEN), dtype=torch.bfloat16, device=dev)
+        self.q = torch.empty((b, W.HQ, W.HEAD_DIM), dtype=torch.bfloat16, device=dev)
+        self.kn = torch.empty((b, W.HKV, W.HEAD_DIM), dtype=torch.bfloat16, device=dev)
+        self.vn = torch.empty_like(self.kn)
+        self.timer = Timer(["qkv_proj", "append", "decode", "o_proj"])
+
+    def step(self, events=None):
+        mtd, inp = self.mtd, self.inp
+        s = self.step_idx % self.steps
+        self.step_idx += 1
+        evs = []
+        x = self.x0[s % len(self.x0)]
+        for layer in range(self.layers):
+            kp, vp = inp["k_pools"][layer], inp["v_pools"][layer]
+            w_qkv, w_o = self.w[layer]
+            e = [self.torch.cuda.Event(enable_timing=True) for _ in range(5)] if events is not None else None
+            if e: e[0].record()
+            mtd.mtd_qkv_proj(x, w_qkv, self.q, self.kn, self.vn)
+            if e: e[1].record()
+            mtd.mtd_kv_append(kp, vp, self.kn, self.vn, self.cu, self.start[s], self.bt)
+            if e: e[2].record()
+            mtd.mtd_attn_decode(kp, vp, self.q, self.kv_lens[s], self.bt, self.max_len, W.SCALE,
+                                self.ws, self.o, self.l)
+            if e: e[3].record()
+            mtd.mtd_o_proj(self.o, w_o, self.x)
+            if e: e[4].record()
+            if e: evs.append(e)
+            x = self.x
+        if events is not None:
+            events.append(evs)
+            self.timed_bytes += self.bytes_per_step[s]
+
+    def collect(self, step_events):
+        for evs in step_events:
+            for i, n in enumerate(("qkv_proj", "append", "decode", "o_proj")):
+                self.timer.samples[n].append(sum(e[i].elapsed_time(e[i + 1]) for e in evs))
+
+    def config(self):
+        c = super().config()
+        c["workload"] = ("fulldepth_block: 28 layers x 64 requests, initial KV lengths log-uniform in "
+                         "[4000, 131072-128], all layers resident; per step and layer: QKV projection of the "
+                         "64 hidden states (random bf16 weights) -> append -> decode -> output projection "
+                         "(the next layer's input)")
+        c["hidden"] = W.HIDDEN
+        return c
+
+    def results(self):
+        res = super().results()
+        res["proj"] = proj_results(self.timer.samples["qkv_proj"], self.timer.samples["o_proj"], len(self.lens0),
+                                   calls_per_sample=self.layers)
+        calls = len(self.timer.samples["decode"]) * self.layers
+        res["step"] = {"layer_ms": sum(float(np.sum(self.timer.samples[n])) for n in self.timer.names) / calls}
+        return res
+
+
 class MixedStepOverlap(MixedStep):
     """The mixed step with the decode on a second stream (default priority), so it can fill CUs the
     prefill leaves idle: the append first, then the prefill on the library's stream and the decode
@@ -676,7 +820,8 @@ class DecodeGraph:
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "per_launch": res["decode"]["bytes"], "ms": res["decode"]["ms"]}
 
 
-WORKLOAD_CLASSES = {c.name: c for c in (MixedStep, MixedStepOverlap, Decode16, Prefill90, FullDepth, DecodeGraph)}
+WORKLOAD_CLASSES = {c.name: c for c in (MixedStep, MixedStepOverlap, MixedBlock, Decode16, Prefill90, FullDepth,
+                                         FullDepthBlock, DecodeGraph)}
 
 
 def blas_threads() -> int:
@@ -703,8 +848,8 @@ def calibrate_copy():
 
 
 # Untimed steps per workload, each about 50 ms of GPU work or more.
-WARMUP_DEFAULT = {"mixed_step": 40, "mixed_step_overlap": 40, "decode16": 500, "prefill90min": 3,
-                  "fulldepth_decode": 5, "decode_graph": 200}
+WARMUP_DEFAULT = {"mixed_step": 40, "mixed_step_overlap": 40, "mixed_block": 40, "decode16": 500,
+                  "prefill90min": 3, "fulldepth_decode": 5, "fulldepth_block": 5, "decode_graph": 200}
 
 
 def main():
@@ -724,7 +869,7 @@ def main():
         return
 
     if args.steps is None:
-        args.steps = {"fulldepth_decode": 128, "decode_graph": 500}.get(args.workload, 20)
+        args.steps = {"fulldepth_decode": 128, "fulldepth_block": 128, "decode_graph": 500}.get(args.workload, 20)
     if args.warmup is None:
         # From idle the shader clock needs about 20 ms of sustained work to reach its steady level
         # (measured on MI355X); the default warmup covers that with margin.
@@ -813,6 +958,9 @@ def main():
     for k in ("decode", "prefill", "append", "step"):
         if k in res:
             line[k] = {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in res[k].items()}
+    if "proj" in res:
+        line["proj"] = {name: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in d.items()}
+                        for name, d in res["proj"].items()}
     if not args.no_cpu_baseline and getattr(wl, "cpu_baseline", None) is not None:
         line["cpu_baseline"] = wl.cpu_baseline(args.cpu_budget)
     print(json.dumps(line), flush=True)

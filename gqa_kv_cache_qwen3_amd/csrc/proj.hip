@@ -130,23 +130,26 @@ __global__ __launch_bounds__(kThreads, 2) void proj_gemm_kernel(const void* __re
   const int wave = tid >> 6;
   const int lane = tid & 63;
 
-  // Tile of this workgroup.  XCD x = blockIdx.x % 8 owns an eighth of the rows of tiles (or of
-  // the columns); inside it the owned index varies fastest, so the workgroups running at once
-  // share a few tiles of the replicated operand and each of those is fetched into the XCD's L2
-  // once.
+  // Tile of this workgroup.  XCD x = blockIdx.x % 8 owns the tile rows x, x + 8, x + 16, ... (or
+  // an eighth of the tile columns); inside it the owned index varies fastest, so the workgroups
+  // running at once share a few tiles of the replicated operand and each of those is fetched into
+  // the XCD's L2 once.  With rows owned, the grid is padded to whole groups of 8 rows and the
+  // workgroups of missing rows exit at once.
   const int id = blockIdx.x;
   const int x = id % 8, local = id / 8;
   int tm, tn;
-  if (rows_major && n_tm % 8 == 0) {
-    tm = x * (n_tm / 8) + local % (n_tm / 8);
-    tn = local / (n_tm / 8);
-  } else if (!rows_major && n_tn % 8 == 0) {
+  if (rows_major) {
+    const int m_per = (n_tm + 7) / 8;
+    tm = x + 8 * (local % m_per);
+    tn = local / m_per;
+  } else if (n_tn % 8 == 0) {
     tn = x * (n_tn / 8) + local % (n_tn / 8);
     tm = local / (n_tn / 8);
   } else {
     tm = id / n_tn;
     tn = id % n_tn;
   }
+  if (tm >= n_tm || tn >= n_tn) return;  // whole workgroup, before any barrier
   const int row0 = tm * kTM;
   const int col0 = tn * kTN;
   const int rows_valid = min(kTM, rows - row0);
@@ -306,6 +309,11 @@ __global__ __launch_bounds__(1024) void proj_skinny_kernel(const void* __restric
   }
 }
 
+// Workgroups launched for n_tm x n_tn tiles (rows owned by XCD: padded to whole groups of 8 rows).
+int grid_tiles(int n_tm, int n_tn, int rows_major) {
+  return rows_major ? 8 * ((n_tm + 7) / 8) * n_tn : n_tm * n_tn;
+}
+
 // The operand split (see Placement) that reads fewer bytes.
 int rows_major_split(int rows, size_t a_row_bytes, size_t w_bytes) {
   return (size_t)rows * a_row_bytes >= w_bytes;
@@ -334,7 +342,7 @@ hipError_t launch_qkv_proj(const uint16_t* x, const uint16_t* w_qkv, int n_tok, 
     return hipGetLastError();
   }
   const int rows_major = rows_major_split(n_tok, kHidden * 2, (size_t)kN * kHidden * 2);
-  proj_gemm_kernel<false><<<dim3(n_tm * n_tn), dim3(kThreads), 0, stream>>>(
+  proj_gemm_kernel<false><<<dim3(grid_tiles(n_tm, n_tn, rows_major)), dim3(kThreads), 0, stream>>>(
       x, kHidden, n_tok, w_qkv, kHidden, n_tm, n_tn, rows_major, om);
   return hipGetLastError();
 }
@@ -357,7 +365,7 @@ hipError_t launch_o_proj(const float* attn, const uint16_t* w_o, int n_tok, uint
     return hipGetLastError();
   }
   const int rows_major = rows_major_split(n_tok, kK * 4, (size_t)kHidden * kK * 2);
-  proj_gemm_kernel<true><<<dim3(n_tm * n_tn), dim3(kThreads), 0, stream>>>(
+  proj_gemm_kernel<true><<<dim3(grid_tiles(n_tm, n_tn, rows_major)), dim3(kThreads), 0, stream>>>(
       attn, kK, n_tok, w_o, kK, n_tm, n_tn, rows_major, om);
   return hipGetLastError();
 }

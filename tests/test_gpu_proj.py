@@ -83,8 +83,10 @@ def test_o_proj_matches_oracle(n_tok):
 
 
 def test_projections_full_chunk():
-    """A whole 4096-token prefill chunk through both maps (every tile of both grids)."""
-    n_tok = W.CHUNK
+    """The mixed step's new tokens through both maps: a whole 4096-token prefill chunk plus 31
+    decode tokens (4127 rows: every tile of both grids, a ragged last row of tiles and a row
+    count that does not split evenly over the 8 XCDs)."""
+    n_tok = W.CHUNK + W.MIXED.params["batch"]
     log(f"projections, full chunk n_tok={n_tok}")
     w_qkv, w_o = _weights("cuda")
     x = W.normal_bf16((n_tok, W.HIDDEN), W.torch_seed(TAG, 3), "cuda")
