@@ -244,55 +244,106 @@ __global__ __launch_bounds__(kThreads, 2) void proj_gemm_kernel(const void* __re
 }
 
 // Few tokens (at most 64): the weights dominate the bytes, so the grid is spread over K instead
-// of tokens.  Workgroup (column block x, row block y) = 32 columns of W against 32 tokens; its
-// wave s takes K slice s (k_dim / kKSlice waves), loads the slice's MFMA fragments straight from
-// global memory and runs the slice's MFMA chain; the slice sums meet in LDS and are added in
-// slice order.
+// of tokens.  Workgroup (column block x, row block y) = 32 columns of W against 32 tokens, 8
+// waves; wave w takes the K slices w * q .. w * q + q - 1 (q = k_dim / kKSlice / 8: 1 for QKV,
+// 2 for o_proj).  For each slice the wave stages its 32 x 128 pieces of A and W in its own 16 KiB
+// of LDS with coalesced loads (each direct-to-LDS instruction fetches 8 rows x 128 contiguous
+// bytes; the float32 A comes through registers, 512 contiguous bytes per row, and is rounded to
+// bf16 on the way), then runs the slice's MFMA chain from ds_read_b128 fragments.  The slice sums
+// meet in LDS and are added in slice order.
+//
+// Per-wave staging of a 32-row x 128-column bf16 piece: two column groups of 128 bytes (8 chunks of
+// 16 bytes); the slot of (row r, chunk c) is 256 (c/8) + 8 r + ((c%8) ^ ((r/2)%4)), which keeps
+// the 8 lanes of each ds_read_b128 phase on distinct banks.
+constexpr int kSkinnyWaves = 8;
+constexpr int kSkinnyStage = 16384;  // per wave: the A piece, then the W piece
+
+__device__ __forceinline__ int slot32_bytes(int r, int c) {
+  return 16 * (256 * (c >> 3) + 8 * r + ((c & 7) ^ ((r >> 1) & 3)));
+}
+
+// Direct-to-LDS copy of rows row0 .. row0+31 (at or past rows_valid: the last valid row), columns
+// k0 .. k0+127 of a bf16 matrix: instruction i fills slots 64 i .. 64 i + 63 = column group i / 4,
+// rows 8 (i % 4) + lane / 8.
+__device__ __forceinline__ void dma_piece32(const uint16_t* __restrict__ m, int ld, int row0,
+                                            int rows_valid, int k0, uint8_t* lds, int lane) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = 8 * (i & 3) + (lane >> 3);
+    const int c = 8 * (i >> 2) + ((lane & 7) ^ ((r >> 1) & 3));
+    const int rs = r < rows_valid ? r : rows_valid - 1;
+    __builtin_amdgcn_global_load_lds((global_cvoid_t*)(m + (size_t)(row0 + rs) * ld + k0 + 8 * c),
+                                     (lds_void_t*)(lds + i * 1024), 16, 0, 0);
+  }
+}
+
+// The float32 piece through registers: load j covers row 2j + lane/32, floats 4 (lane%32) .. +3.
+__device__ __forceinline__ void stage_f32_piece32(const float* __restrict__ a, int ld, int row0,
+                                                  int rows_valid, int k0, uint8_t* lds, int lane) {
+  float4 v[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int r = 2 * j + (lane >> 5);
+    const int rs = r < rows_valid ? r : rows_valid - 1;
+    v[j] = *reinterpret_cast<const float4*>(a + (size_t)(row0 + rs) * ld + k0 + 4 * (lane & 31));
+  }
+  const int f = lane & 31;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int r = 2 * j + (lane >> 5);
+    *reinterpret_cast<uint2*>(lds + slot32_bytes(r, f >> 1) + 8 * (f & 1)) =
+        make_uint2(pack_bf16x2(v[j].x, v[j].y), pack_bf16x2(v[j].z, v[j].w));
+  }
+}
+
 template <bool kAF32>
-__global__ __launch_bounds__(1024) void proj_skinny_kernel(const void* __restrict__ a_ptr, int lda,
-                                                           int rows, const uint16_t* __restrict__ w,
-                                                           int k_dim, OutMap out) {
-  constexpr int kMaxSlices = 16;
-  __shared__ float s_part[kMaxSlices][16][64];  // [slice][accumulator element][lane]
+__global__ __launch_bounds__(64 * kSkinnyWaves) void proj_skinny_kernel(
+    const void* __restrict__ a_ptr, int lda, int rows, const uint16_t* __restrict__ w, int k_dim,
+    OutMap out) {
+  constexpr int kMaxPerWave = 2;
+  __shared__ __attribute__((aligned(1024))) uint8_t s_mem[kSkinnyWaves * kSkinnyStage];
   const int tid = threadIdx.x;
-  const int slice = tid >> 6;
+  const int wave = tid >> 6;
   const int lane = tid & 63;
-  const int n_slices = blockDim.x >> 6;
+  const int n_slices = k_dim / kKSlice;
+  const int per_wave = n_slices / kSkinnyWaves;
   const int n = lane & 31, hk = lane >> 5;
   const int col0 = 32 * blockIdx.x;
   const int row0 = 32 * blockIdx.y;
-  const int k0 = slice * kKSlice + 8 * hk;
+  const int rows_valid = min(32, rows - row0);
+  uint8_t* a_lds = s_mem + wave * kSkinnyStage;
+  uint8_t* w_lds = a_lds + kSkinnyStage / 2;
 
-  const uint16_t* wrow = w + (size_t)(col0 + n) * k_dim + k0;
-  const int r = min(row0 + n, rows - 1);
-  bf16x8_t wf[kKSlice / 16], af[kKSlice / 16];
+  floatx16_t acc[kMaxPerWave];
 #pragma unroll
-  for (int ks = 0; ks < kKSlice / 16; ++ks)
-    wf[ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(wrow + 16 * ks));
-  if constexpr (kAF32) {
-    const float* arow = static_cast<const float*>(a_ptr) + (size_t)r * lda + k0;
+  for (int t = 0; t < kMaxPerWave; ++t) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[t][v] = 0.f;
+    if (t >= per_wave) continue;
+    const int k0 = (wave * per_wave + t) * kKSlice;
+    dma_piece32(w, k_dim, col0, 32, k0, w_lds, lane);
+    if constexpr (kAF32)
+      stage_f32_piece32(static_cast<const float*>(a_ptr), lda, row0, rows_valid, k0, a_lds, lane);
+    else
+      dma_piece32(static_cast<const uint16_t*>(a_ptr), lda, row0, rows_valid, k0, a_lds, lane);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's pieces are in its LDS
 #pragma unroll
     for (int ks = 0; ks < kKSlice / 16; ++ks) {
-      const float4 lo = *reinterpret_cast<const float4*>(arow + 16 * ks);
-      const float4 hi = *reinterpret_cast<const float4*>(arow + 16 * ks + 4);
-      const uint4 packed = make_uint4(pack_bf16x2(lo.x, lo.y), pack_bf16x2(lo.z, lo.w),
-                                      pack_bf16x2(hi.x, hi.y), pack_bf16x2(hi.z, hi.w));
-      af[ks] = __builtin_bit_cast(bf16x8_t, packed);
+      const int off = slot32_bytes(n, 2 * ks + hk);
+      const bf16x8_t af = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(a_lds + off));
+      const bf16x8_t wf = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(w_lds + off));
+      acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, wf, acc[t], 0, 0, 0);
     }
-  } else {
-    const uint16_t* arow = static_cast<const uint16_t*>(a_ptr) + (size_t)r * lda + k0;
-#pragma unroll
-    for (int ks = 0; ks < kKSlice / 16; ++ks)
-      af[ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(arow + 16 * ks));
   }
-  floatx16_t acc;
+  __syncthreads();  // every wave is done with its pieces; the LDS now holds the slice sums
+  float* s_part = reinterpret_cast<float*>(s_mem);  // [slice][accumulator element][lane]
 #pragma unroll
-  for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+  for (int t = 0; t < kMaxPerWave; ++t) {
+    if (t >= per_wave) continue;
+    const int slice = wave * per_wave + t;
 #pragma unroll
-  for (int ks = 0; ks < kKSlice / 16; ++ks)
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks], wf[ks], acc, 0, 0, 0);
-#pragma unroll
-  for (int v = 0; v < 16; ++v) s_part[slice][v][lane] = acc[v];
+    for (int v = 0; v < 16; ++v) s_part[(slice * 16 + v) * 64 + lane] = acc[t][v];
+  }
   __syncthreads();
 
   // Element e = (accumulator element v, lane l): C[row0 + 8(v/4) + 4(l/32) + v%4][col0 + l%32].
@@ -301,11 +352,11 @@ __global__ __launch_bounds__(1024) void proj_skinny_kernel(const void* __restric
   const int ld = out.ld[reg];
   for (int e = tid; e < 16 * 64; e += blockDim.x) {
     const int v = e >> 6, l = e & 63;
-    const int rr = row0 + 8 * (v >> 2) + 4 * (l >> 5) + (v & 3);
-    if (rr >= rows) continue;
+    const int rr = 8 * (v >> 2) + 4 * (l >> 5) + (v & 3);
+    if (rr >= rows_valid) continue;
     float total = 0.f;
-    for (int sl = 0; sl < n_slices; ++sl) total += s_part[sl][v][l];
-    dst[(size_t)rr * ld + col0 - out.lo[reg] + (l & 31)] = (uint16_t)pack_bf16x2(total, 0.f);
+    for (int sl = 0; sl < n_slices; ++sl) total += s_part[(sl * 16 + v) * 64 + l];
+    dst[(size_t)(row0 + rr) * ld + col0 - out.lo[reg] + (l & 31)] = (uint16_t)pack_bf16x2(total, 0.f);
   }
 }
 
@@ -337,7 +388,7 @@ hipError_t launch_qkv_proj(const uint16_t* x, const uint16_t* w_qkv, int n_tok, 
   om.lo[1] = kQHeads * kHeadDim;
   om.lo[2] = (kQHeads + kKvHeads) * kHeadDim;
   if (n_tok <= kSkinnyRows) {
-    proj_skinny_kernel<false><<<dim3(kN / 32, (n_tok + 31) / 32), dim3(64 * (kHidden / kKSlice)), 0, stream>>>(
+    proj_skinny_kernel<false><<<dim3(kN / 32, (n_tok + 31) / 32), dim3(64 * kSkinnyWaves), 0, stream>>>(
         x, kHidden, n_tok, w_qkv, kHidden, om);
     return hipGetLastError();
   }
@@ -360,7 +411,7 @@ hipError_t launch_o_proj(const float* attn, const uint16_t* w_o, int n_tok, uint
     om.lo[r] = 0;
   }
   if (n_tok <= kSkinnyRows) {
-    proj_skinny_kernel<true><<<dim3(kHidden / 32, (n_tok + 31) / 32), dim3(64 * (kK / kKSlice)), 0, stream>>>(
+    proj_skinny_kernel<true><<<dim3(kHidden / 32, (n_tok + 31) / 32), dim3(64 * kSkinnyWaves), 0, stream>>>(
         attn, kK, n_tok, w_o, kK, om);
     return hipGetLastError();
   }
