@@ -11,7 +11,7 @@ shared pool of 64-token pages.  Per step:
 Other workloads (--workload): decode16 (16 requests, L in [27000, 30000]), prefill90min (17 chunks
 of a 67,500-token request), fulldepth_decode (28 layers x 64 requests, 128K cap), and the same
 steps as whole attention blocks with the QKV and output projections around the attention
-(mixed_block, fulldepth_block), besides mixed_step_overlap and decode_graph.
+(mixed_block, fulldepth_block, decode_graph_block), besides mixed_step_overlap and decode_graph.
 
 Prints one JSON line.  `value` is decode-attention HBM throughput (algorithmic bytes / time) and
 `prefill` carries the chunked-prefill TFLOP/s; `roofline` is for the kernel that takes the most
@@ -820,8 +820,54 @@ class DecodeGraph:
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "per_launch": res["decode"]["bytes"], "ms": res["decode"]["ms"]}
 
 
+class DecodeGraphBlock(DecodeGraph):
+    """decode_graph with the projections: per layer the QKV projection of the request's hidden state,
+    the append of its new K/V, decode attention and the output projection, whose result is the next
+    layer's input; eager calls against one HIP-graph replay per step."""
+    name = "decode_graph_block"
+
+    def __init__(self, dev):
+        import torch
+        self.w = [W.projection_weights(W.torch_seed(W.TINY.tag, 70, l), dev) for l in range(self.LAYERS)]
+        self.x0 = W.normal_bf16((self.SLOTS, 1, W.HIDDEN), W.torch_seed(W.TINY.tag, 71), dev)
+        self.qb = torch.empty((1, W.HQ, W.HEAD_DIM), dtype=torch.bfloat16, device=dev)
+        self.kb = torch.empty((1, W.HKV, W.HEAD_DIM), dtype=torch.bfloat16, device=dev)
+        self.vb = torch.empty_like(self.kb)
+        self.xb = torch.empty((1, W.HIDDEN), dtype=torch.bfloat16, device=dev)
+        super().__init__(dev)
+
+    def _calls(self, r, events=None):
+        mtd = self.mtd
+        x = self.x0[r]
+        for l in range(self.LAYERS):
+            w_qkv, w_o = self.w[l]
+            mtd.mtd_qkv_proj(x, w_qkv, self.qb, self.kb, self.vb)
+            mtd.mtd_kv_append(self.k[l], self.v[l], self.kb, self.vb, self.cu, self.pos, self.bt)
+            if events is not None: events[l][0].record()
+            mtd.mtd_attn_decode(self.k[l], self.v[l], self.qb, self.len, self.bt, self.max_len, W.SCALE,
+                                self.ws, self.o[l], self.lse[l])
+            if events is not None: events[l][1].record()
+            mtd.mtd_o_proj(self.o[l], w_o, self.xb)
+            x = self.xb
+        self.pos.add_(1)
+        self.len.add_(1)
+
+    def config(self):
+        c = super().config()
+        c["workload"] = ("decode_graph_block: 1 request (439-token context growing by one token per step) through "
+                         "28 attention blocks; step = 28 x (QKV projection, append, decode, output projection; "
+                         "random bf16 weights); eager calls vs one HIP-graph replay")
+        c["hidden"] = W.HIDDEN
+        return c
+
+    def results(self):
+        res = super().results()
+        res["step"]["launches_per_step"] = 5 * self.LAYERS + 2
+        return res
+
+
 WORKLOAD_CLASSES = {c.name: c for c in (MixedStep, MixedStepOverlap, MixedBlock, Decode16, Prefill90, FullDepth,
-                                         FullDepthBlock, DecodeGraph)}
+                                         FullDepthBlock, DecodeGraph, DecodeGraphBlock)}
 
 
 def blas_threads() -> int:
@@ -849,7 +895,8 @@ def calibrate_copy():
 
 # Untimed steps per workload, each about 50 ms of GPU work or more.
 WARMUP_DEFAULT = {"mixed_step": 40, "mixed_step_overlap": 40, "mixed_block": 40, "decode16": 500,
-                  "prefill90min": 3, "fulldepth_decode": 5, "fulldepth_block": 5, "decode_graph": 200}
+                  "prefill90min": 3, "fulldepth_decode": 5, "fulldepth_block": 5, "decode_graph": 200,
+                  "decode_graph_block": 200}
 
 
 def main():
@@ -869,7 +916,8 @@ def main():
         return
 
     if args.steps is None:
-        args.steps = {"fulldepth_decode": 128, "fulldepth_block": 128, "decode_graph": 500}.get(args.workload, 20)
+        args.steps = {"fulldepth_decode": 128, "fulldepth_block": 128, "decode_graph": 500,
+                      "decode_graph_block": 500}.get(args.workload, 20)
     if args.warmup is None:
         # From idle the shader clock needs about 20 ms of sustained work to reach its steady level
         # (measured on MI355X); the default warmup covers that with margin.

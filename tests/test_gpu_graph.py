@@ -121,3 +121,62 @@ def test_graph_multilayer_decode_step():
     lens0 = W.loguniform_lengths(8, 1000, 9000, W.FULLDEPTH.tag, 9)
     log(f"graph: 4 layers x 8 requests, lens0={lens0.tolist()}")
     StepGraph(lens0, 6, 4, W.FULLDEPTH.tag).run_and_check("graph 4x8")
+
+
+def test_graph_attention_block_step():
+    """Whole attention blocks in one graph: 3 layers x (QKV projection -> append -> decode -> output
+    projection, whose result feeds the next layer) for 5 requests, 4 steps; every replay bit-identical
+    to the same calls made eagerly on twin pools."""
+    lens0 = W.loguniform_lengths(5, 100, 3000, W.FULLDEPTH.tag, 11)
+    layers, steps, b = 3, 4, len(lens0)
+    log(f"graph: attention blocks, {layers} layers x {b} requests, lens0={lens0.tolist()}")
+    tables, n_pages, _ = W.place_pages(lens0 + steps, W.FULLDEPTH.tag, 12)
+    bt = torch.as_tensor(tables, device="cuda")
+    max_len = int(lens0.max()) + steps
+    tag = W.FULLDEPTH.tag
+    kg = [new_pool(n_pages, "cuda", W.torch_seed(tag, 80, l)) for l in range(layers)]
+    vg = [new_pool(n_pages, "cuda", W.torch_seed(tag, 81, l)) for l in range(layers)]
+    ke, ve = [p.clone() for p in kg], [p.clone() for p in vg]
+    weights = [W.projection_weights(W.torch_seed(tag, 82, l), "cuda") for l in range(layers)]
+    x_all = W.normal_bf16((steps, b, W.HIDDEN), W.torch_seed(tag, 83), "cuda")
+    cu = _i32(np.arange(b + 1))
+    ws_g = torch.empty(mtd.decode_workspace_bytes(b, max_len), dtype=torch.uint8, device="cuda")
+    ws_e = torch.empty_like(ws_g)
+    x_buf = torch.empty((b, W.HIDDEN), dtype=torch.bfloat16, device="cuda")
+    start_buf = torch.zeros(b, dtype=torch.int32, device="cuda")
+    len_buf = torch.zeros(b, dtype=torch.int32, device="cuda")
+    q_b = torch.empty((b, W.HQ, W.HEAD_DIM), dtype=torch.bfloat16, device="cuda")
+    k_b = torch.empty((b, W.HKV, W.HEAD_DIM), dtype=torch.bfloat16, device="cuda")
+    v_b = torch.empty_like(k_b)
+    o_b = torch.empty((b, W.HQ, W.HEAD_DIM), dtype=torch.float32, device="cuda")
+    l_b = torch.empty((b, W.HQ), dtype=torch.float32, device="cuda")
+    y_g = torch.empty((layers, b, W.HIDDEN), dtype=torch.bfloat16, device="cuda")
+
+    def block_calls(kp, vp, x, start, kv_lens, ws, y_out, o, lse, q, k, v):
+        for l in range(layers):
+            w_qkv, w_o = weights[l]
+            mtd.mtd_qkv_proj(x, w_qkv, q, k, v)
+            mtd.mtd_kv_append(kp[l], vp[l], k, v, cu, start, bt)
+            mtd.mtd_attn_decode(kp[l], vp[l], q, kv_lens, bt, max_len, W.SCALE, ws, o, lse)
+            mtd.mtd_o_proj(o, w_o, y_out[l])
+            x = y_out[l]
+
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        block_calls(kg, vg, x_buf, start_buf, len_buf, ws_g, y_g, o_b, l_b, q_b, k_b, v_b)
+    torch.cuda.synchronize()
+    for s in range(steps):
+        log(f"graph blocks: step {s}")
+        x_buf.copy_(x_all[s])
+        start_buf.copy_(_i32(lens0 + s))
+        len_buf.copy_(_i32(lens0 + s + 1))
+        graph.replay()
+        y_e = torch.empty_like(y_g)
+        block_calls(ke, ve, x_all[s], _i32(lens0 + s), _i32(lens0 + s + 1), ws_e, y_e,
+                    torch.empty_like(o_b), torch.empty_like(l_b), torch.empty_like(q_b),
+                    torch.empty_like(k_b), torch.empty_like(v_b))
+        torch.cuda.synchronize()
+        assert torch.equal(y_g, y_e), s
+    for l in range(layers):
+        assert torch.equal(kg[l], ke[l]) and torch.equal(vg[l], ve[l]), l
