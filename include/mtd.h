@@ -31,7 +31,8 @@
  * ---------------------------------------------------------------------------------------------
  * Memory.  Every pointer argument is a DEVICE pointer (memory of the GPU that is current on the
  *   calling thread) unless the comment says "host".  The caller owns all memory; the library
- *   allocates none and keeps no state other than a per-thread error string.
+ *   allocates none and keeps no state other than a per-thread error string and, per device, the
+ *   compute-unit count it reads once to size launches.
  * Streams.  `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue work on it,
  *   in order, and never synchronise the host.
  * bf16.  bfloat16 values are 2-byte IEEE-754 binary32 upper halves.
