@@ -34,8 +34,8 @@
 // the same layout.  MFMA operands are ds_read_b128 of one row's 16-byte chunk: A rows for the A
 // operand and W rows for the B operand, both free of bank conflicts under the XOR swizzle.
 //
-// Placement.  Workgroup i runs on XCD i % 8.  Each XCD owns an eighth of the tile rows (every
-// XCD then reads W whole and an eighth of A) or of the tile columns (an eighth of W, all of A);
+// Placement.  Workgroup i runs on XCD i % 8.  Each XCD owns every eighth tile row (every XCD
+// then reads W whole and an eighth of A) or an eighth of the tile columns (an eighth of W, all of A);
 // the host picks the split whose replicated operand is the smaller.  Within an XCD the owned
 // index varies fastest, so the workgroups in flight together touch few tiles of the replicated
 // operand and each is brought into the XCD's L2 once rather than once per owned row.
