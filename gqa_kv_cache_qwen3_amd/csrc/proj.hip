@@ -20,8 +20,8 @@
 // s, the loads of the next 64-wide slice into stage s^1 are issued, so they travel while stage s
 // is multiplied.  The stages are separate arrays picked at compile time (the loop is unrolled by
 // two), which lets the compiler see that the reads of one stage never wait on the loads into the
-// other.  Two workgroups fit per CU (64 KiB of LDS each).  At 128 x 128 the tile does 64 flops
-// per staged byte, so the kernel is bound by the L2 -> LDS traffic well before the matrix pipe.
+// other.  Two workgroups fit per CU (64 KiB of LDS each); the tile does 64 flops per staged
+// byte (a 256-row tile, with a quarter fewer staged bytes per flop, measured no faster).
 // Calls with at most 64 tokens use proj_skinny_kernel instead, which spreads K over the waves.
 // Both kernels add the products in one order (fixed K slices, see kKSlice), so a token's result
 // is the same whatever the token count and whichever kernel runs.
