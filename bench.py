@@ -52,6 +52,8 @@ TRAFFIC_TABLE = os.path.join(ROOT, "profiles", "traffic.md")
 KERNEL_SOURCES = {
     "prefill_kernel+prefill_merge_kernel": ["prefill.hip"],
     "decode_split_kernel+decode_merge_kernel": ["decode.hip"],
+    "proj_gemm_kernel<bf16 A>": ["proj.hip"],
+    "proj_gemm_kernel<f32 A>": ["proj.hip"],
 }
 COMMON_SOURCES = ["device_util.h", "mtd_internal.h"]
 
@@ -510,15 +512,18 @@ def proj_work(n_tok: int):
     return qkv, o
 
 
-def proj_results(samples_qkv, samples_o, n_tok, calls_per_sample=1):
+def proj_results(samples_qkv, samples_o, n_tok, calls_per_sample=1, workload=None):
     qkv_w, o_w = proj_work(n_tok)
     out = {}
+    kernels = {"qkv_proj": "proj_gemm_kernel<bf16 A>", "o_proj": "proj_gemm_kernel<f32 A>"}
     for name, samples, wk in (("qkv_proj", samples_qkv, qkv_w), ("o_proj", samples_o, o_w)):
         ms = float(np.sum(samples)) / (len(samples) * calls_per_sample)
         tfs = wk["flops"] / (ms * 1e-3) / 1e12
         gbs = wk["bytes"] / (ms * 1e-3) / 1e9
         out[name] = {"ms": ms, "tokens": n_tok, "tflops": tfs, "mfma_frac": tfs / MFMA_BF16_PEAK_TFLOPS,
                      "gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS, "flops": wk["flops"], "bytes": wk["bytes"]}
+        if workload is not None:
+            out[name]["traffic"] = recorded_traffic(kernels[name], workload)
     return out
 
 
@@ -568,7 +573,8 @@ class MixedBlock(MixedStep):
 
     def results(self):
         res = super().results()
-        res["proj"] = proj_results(self.timer.samples["qkv_proj"], self.timer.samples["o_proj"], self.n_new)
+        res["proj"] = proj_results(self.timer.samples["qkv_proj"], self.timer.samples["o_proj"], self.n_new,
+                                   workload=self.name)
         return res
 
     cpu_baseline = None
