@@ -11,7 +11,8 @@ shared pool of 64-token pages.  Per step:
 Other workloads (--workload): decode16 (16 requests, L in [27000, 30000]), prefill90min (17 chunks
 of a 67,500-token request), fulldepth_decode (28 layers x 64 requests, 128K cap), and the same
 steps as whole attention blocks with the QKV and output projections around the attention
-(mixed_block, fulldepth_block, decode_graph_block), besides mixed_step_overlap and decode_graph.
+(mixed_block, fulldepth_block, decode_graph_block), besides mixed_step_overlap, decode_graph and
+decode16_seqsplit (one GPU's share of decode16 split by sequence over 8 GPUs, with the merge).
 
 Prints one JSON line.  `value` is decode-attention HBM throughput (algorithmic bytes / time) and
 `prefill` carries the chunked-prefill TFLOP/s; `roofline` is for the kernel that takes the most
@@ -336,6 +337,71 @@ class Decode16:
     def dominant(self, res):
         return {"kernel": "decode_split_kernel+decode_merge_kernel", "bound": "hbm", "achieved": res["decode"]["value"],
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "per_launch": self.bytes, "ms": res["decode"]["ms"]}
+
+
+class Decode16SeqSplit:
+    """One GPU's share of decode16 with each request's KV split by sequence over 8 GPUs: this GPU
+    holds the first eighth of every request's tokens (whole pages), decodes them (the library's
+    decode over a block table that starts at the shard's first page), and merges the 8 gathered
+    (O, LSE) partials with mtd_attn_merge.  The gather itself (8 x 16 heads x 129 floats per
+    request) is the one step a single GPU cannot show; the other shards are the same kernels."""
+    name = "decode16_seqsplit"
+    GPUS = 8
+
+    def __init__(self, dev):
+        import torch
+        import gqa_kv_cache_qwen3_amd as mtd
+        self.mtd, self.torch = mtd, torch
+        p = W.DECODE16.params
+        self.lens = W.uniform_lengths(p["batch"], p["lo"], p["hi"], W.DECODE16.tag, 0)
+        # shard 0 of each request: its first ceil(L / 8) tokens, rounded up to whole pages
+        per_gpu = -(-self.lens // self.GPUS)
+        self.shard = np.minimum(-(-per_gpu // W.PAGE) * W.PAGE, self.lens)
+        tables, n_pages, _ = W.place_pages(self.shard, W.DECODE16.tag, 3)
+        b = len(self.lens)
+        self.k = torch.empty((n_pages, W.HKV, W.PAGE, W.HEAD_DIM), dtype=torch.bfloat16, device=dev)
+        self.v = torch.empty_like(self.k)
+        fill_normal_(self.k, W.torch_seed(W.DECODE16.tag, 31))
+        fill_normal_(self.v, W.torch_seed(W.DECODE16.tag, 32))
+        self.bt = torch.as_tensor(tables, device=dev)
+        self.q = W.normal_bf16((b, W.HQ, W.HEAD_DIM), W.torch_seed(W.DECODE16.tag, 33), dev)
+        self.kv_lens = torch.as_tensor(self.shard.astype(np.int32), device=dev)
+        self.max_len = int(self.shard.max())
+        self.ws = torch.empty(mtd.decode_workspace_bytes(b, self.max_len), dtype=torch.uint8, device=dev)
+        # the gathered partials: this GPU's in slot 0, the other shards' as seeded stand-ins
+        self.o_parts = torch.randn((self.GPUS, b, W.HQ, W.HEAD_DIM), device=dev) * 0.1
+        self.l_parts = torch.randn((self.GPUS, b, W.HQ), device=dev) + 8.0
+        self.out = torch.empty((b, W.HQ, W.HEAD_DIM), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((b, W.HQ), dtype=torch.float32, device=dev)
+        self.timer = Timer(["decode", "merge"])
+        self.work = {"decode_bytes": decode_bytes(self.shard)}
+
+    def step(self, events=None):
+        mtd = self.mtd
+        if events: events[0].record()
+        mtd.mtd_attn_decode(self.k, self.v, self.q, self.kv_lens, self.bt, self.max_len, W.SCALE, self.ws,
+                            self.o_parts[0], self.l_parts[0])
+        if events: events[1].record()
+        mtd.mtd_attn_merge(self.o_parts, self.l_parts, self.out, self.lse)
+        if events: events[2].record()
+
+    def config(self):
+        return {"workload": "decode16_seqsplit: one GPU's share of decode16 with each request's KV split by "
+                            "sequence over 8 GPUs (the first eighth of each request's tokens), then the merge of "
+                            "the 8 gathered partials", "gpus_in_split": self.GPUS, "batch": len(self.lens),
+                "shard_kv_tokens": int(self.shard.sum()), "request_kv_tokens": int(self.lens.sum())}
+
+    def results(self):
+        dec_ms, mrg_ms = self.timer.mean_ms("decode"), self.timer.mean_ms("merge")
+        gbs = self.work["decode_bytes"] / (dec_ms * 1e-3) / 1e9
+        return {"decode": {"value": gbs, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "ms": dec_ms,
+                           "bytes": self.work["decode_bytes"], "kernels": "decode_split_kernel + decode_merge_kernel (shard)"},
+                "step": {"shard_decode_ms": dec_ms, "merge_ms": mrg_ms, "per_gpu_ms": dec_ms + mrg_ms,
+                         "gathered_bytes_per_request": self.GPUS * W.HQ * (W.HEAD_DIM + 1) * 4}}
+
+    def dominant(self, res):
+        return {"kernel": "decode_split_kernel+decode_merge_kernel", "bound": "hbm", "achieved": res["decode"]["value"],
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "per_launch": res["decode"]["bytes"], "ms": res["decode"]["ms"]}
 
 
 class Prefill90:
@@ -872,8 +938,8 @@ class DecodeGraphBlock(DecodeGraph):
         return res
 
 
-WORKLOAD_CLASSES = {c.name: c for c in (MixedStep, MixedStepOverlap, MixedBlock, Decode16, Prefill90, FullDepth,
-                                         FullDepthBlock, DecodeGraph, DecodeGraphBlock)}
+WORKLOAD_CLASSES = {c.name: c for c in (MixedStep, MixedStepOverlap, MixedBlock, Decode16, Decode16SeqSplit, Prefill90,
+                                         FullDepth, FullDepthBlock, DecodeGraph, DecodeGraphBlock)}
 
 
 def blas_threads() -> int:
@@ -902,7 +968,7 @@ def calibrate_copy():
 # Untimed steps per workload, each about 50 ms of GPU work or more.
 WARMUP_DEFAULT = {"mixed_step": 40, "mixed_step_overlap": 40, "mixed_block": 40, "decode16": 500,
                   "prefill90min": 3, "fulldepth_decode": 5, "fulldepth_block": 5, "decode_graph": 200,
-                  "decode_graph_block": 200}
+                  "decode_graph_block": 200, "decode16_seqsplit": 2000}
 
 
 def main():

@@ -13,6 +13,7 @@ Names match the C entry points:
                     workspace=None, out=None, lse=None)
     mtd_qkv_proj(x, w_qkv, q=None, k_new=None, v_new=None)
     mtd_o_proj(attn, w_o, out=None)
+    mtd_attn_merge(o_parts, lse_parts, out=None, lse=None)
 """
 
 from __future__ import annotations
@@ -32,6 +33,7 @@ MTD_ERR_CAPACITY = -3
 MTD_ERR_WORKSPACE = -4
 MTD_ERR_HIP = -5
 MTD_MAX_CONTEXT = 131072
+MTD_MAX_MERGE_PARTS = 1024
 
 NUM_Q_HEADS = 16
 NUM_KV_HEADS = 8
@@ -89,6 +91,8 @@ def lib() -> ctypes.CDLL:
         cdll.mtd_qkv_proj.restype = ctypes.c_int
         cdll.mtd_o_proj.argtypes = [_P, _P, _I, _I, _I, _I, _P, _P]
         cdll.mtd_o_proj.restype = ctypes.c_int
+        cdll.mtd_attn_merge.argtypes = [_P, _P, _I, _I, _I, _P, _P, _P]
+        cdll.mtd_attn_merge.restype = ctypes.c_int
         cdll.mtd_status_string.argtypes = [ctypes.c_int]
         cdll.mtd_status_string.restype = ctypes.c_char_p
         cdll.mtd_last_error.argtypes = []
@@ -269,8 +273,25 @@ def mtd_o_proj(attn, w_o, out=None):
     return out
 
 
+def mtd_attn_merge(o_parts, lse_parts, out=None, lse=None):
+    """Combine attention results over disjoint key sets: o_parts float32 [S][..., D] and
+    lse_parts float32 [S][...] (natural log; -inf = no keys) -> (out [..., D], lse [...])."""
+    _need(o_parts, "o_parts", torch.float32)
+    _need(lse_parts, "lse_parts", torch.float32)
+    if o_parts.dim() < 2 or tuple(o_parts.shape[:-1]) != tuple(lse_parts.shape):
+        raise ValueError("o_parts must be [S][..., D] with lse_parts [S][...]")
+    n_parts, d = o_parts.shape[0], o_parts.shape[-1]
+    rows_shape = tuple(lse_parts.shape[1:])
+    n_rows = lse_parts[0].numel() if n_parts else 0
+    out = _out(out, "out", rows_shape + (d,), torch.float32, o_parts)
+    lse = _out(lse, "lse", rows_shape, torch.float32, o_parts)
+    _check(lib().mtd_attn_merge(o_parts.data_ptr(), lse_parts.data_ptr(), n_parts, n_rows, d,
+                                out.data_ptr(), lse.data_ptr(), _stream()))
+    return out, lse
+
+
 __all__ = [
     "MtdError", "KvLayer", "lib", "kv_layer", "mtd_kv_append", "mtd_attn_prefill_chunk",
     "mtd_attn_decode", "decode_workspace_bytes", "prefill_workspace_bytes", "mtd_qkv_proj",
-    "mtd_o_proj",
+    "mtd_o_proj", "mtd_attn_merge",
 ]

@@ -22,7 +22,7 @@ LIB_NAME = "libmtd.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["mtd_api.cpp", "kv_append.hip", "decode.hip", "prefill.hip", "proj.hip"]
+SOURCES = ["mtd_api.cpp", "kv_append.hip", "decode.hip", "prefill.hip", "proj.hip", "merge.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 COMMON_FLAGS = [

@@ -209,6 +209,22 @@ int mtd_o_proj(const float* attn, const void* w_o, int32_t n_tok, int32_t num_q_
                     "output projection launch");
 }
 
+int mtd_attn_merge(const float* o_parts, const float* lse_parts, int32_t n_parts, int32_t n_rows,
+                   int32_t head_dim, float* out, float* lse, void* stream) {
+  if (n_parts <= 0 || n_parts > MTD_MAX_MERGE_PARTS)
+    return fail(MTD_ERR_INVALID_ARG, "n_parts = %d (1 .. %d)", n_parts, MTD_MAX_MERGE_PARTS);
+  if (n_rows < 0) return fail(MTD_ERR_INVALID_ARG, "n_rows = %d", n_rows);
+  if (head_dim != mtd::kHeadDim)
+    return fail(MTD_ERR_UNSUPPORTED, "head_dim %d (supported: %d)", head_dim, mtd::kHeadDim);
+  if (o_parts == nullptr || lse_parts == nullptr || out == nullptr || lse == nullptr)
+    return fail(MTD_ERR_INVALID_ARG, "o_parts / lse_parts / out / lse is NULL");
+  if (!aligned16(o_parts) || !aligned16(out))
+    return fail(MTD_ERR_INVALID_ARG, "o_parts / out not 16-byte aligned");
+  return hip_status(mtd::launch_attn_merge(o_parts, lse_parts, n_parts, n_rows, out, lse,
+                                           static_cast<hipStream_t>(stream)),
+                    "merge launch");
+}
+
 const char* mtd_status_string(int status) {
   switch (status) {
     case MTD_OK: return "ok";

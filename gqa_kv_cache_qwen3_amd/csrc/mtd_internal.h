@@ -74,4 +74,10 @@ hipError_t launch_qkv_proj(const uint16_t* x, const uint16_t* w_qkv, int n_tok, 
 hipError_t launch_o_proj(const float* attn, const uint16_t* w_o, int n_tok, uint16_t* out,
                          hipStream_t stream);
 
+// LSE combination of attention results over disjoint key sets: o_parts float32
+// [n_parts][n_rows][kHeadDim], lse_parts float32 [n_parts][n_rows] -> out [n_rows][kHeadDim],
+// lse [n_rows] (n_parts >= 1, n_rows >= 0).
+hipError_t launch_attn_merge(const float* o_parts, const float* lse_parts, int n_parts, int n_rows,
+                             float* out, float* lse, hipStream_t stream);
+
 }  // namespace mtd

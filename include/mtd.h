@@ -22,6 +22,9 @@
  *   mtd_qkv_proj            hidden states -> q, k, v of new tokens
  *   mtd_o_proj              attention output -> hidden states
  *
+ * and mtd_attn_merge combines attention results computed over disjoint key ranges (a request's KV
+ * split by sequence).
+ *
  * Everything computed is exact softmax attention:
  *     s_j = scale * <q, k_j>  for visible keys j;  LSE = ln sum_j exp(s_j);  O = sum_j exp(s_j - LSE) v_j
  * Query head h reads KV head h / (num_q_heads / num_kv_heads).
@@ -61,7 +64,7 @@
 extern "C" {
 #endif
 
-#define MTD_ABI_VERSION 3
+#define MTD_ABI_VERSION 4
 
 /* Status codes. */
 #define MTD_OK               0
@@ -229,6 +232,29 @@ int mtd_qkv_proj(const void* x, const void* w_qkv, int32_t n_tok, int32_t hidden
  */
 int mtd_o_proj(const float* attn, const void* w_o, int32_t n_tok, int32_t num_q_heads,
                int32_t head_dim, int32_t hidden, void* out, void* stream);
+
+/* Most parts mtd_attn_merge combines in one call. */
+#define MTD_MAX_MERGE_PARTS 1024
+
+/*
+ * mtd_attn_merge - combine attention results over disjoint key sets (log-sum-exp merge).
+ *
+ * The step after the gather when a request's KV is split by sequence over several GPUs: each GPU
+ * runs mtd_attn_decode over its own page range (a block table starting at the range's first page
+ * and kv_lens counting the range's tokens) and so produces that range's O and LSE; this call
+ * combines the gathered partials into the result over all keys (the pages list multi-GPU support
+ * for KV caches that outgrow one GPU as ongoing work: "Optimizing ASR Models ...", section What's
+ * Next).  It is exact up to rounding: LSE = ln sum_k exp(lse_k), O = sum_k exp(lse_k - LSE) o_k.
+ *
+ *   o_parts     float32 [n_parts][n_rows][head_dim], part k's outputs (rows = tokens x heads)
+ *   lse_parts   float32 [n_parts][n_rows], part k's natural-log LSE; -inf = no keys (zero weight)
+ *   n_parts     1 .. MTD_MAX_MERGE_PARTS;  n_rows >= 0 (0 enqueues nothing);  head_dim 128
+ *   out         float32 [n_rows][head_dim], written;  lse  float32 [n_rows], written
+ * A row whose parts all have LSE = -inf gets O = 0 and LSE = -inf.  o_parts and out must be
+ * 16-byte aligned (else MTD_ERR_INVALID_ARG).
+ */
+int mtd_attn_merge(const float* o_parts, const float* lse_parts, int32_t n_parts, int32_t n_rows,
+                   int32_t head_dim, float* out, float* lse, void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* mtd_status_string(int status);

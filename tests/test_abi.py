@@ -32,7 +32,7 @@ def test_header_declares_the_three_calls():
     names = declared_functions()
     for n in ("mtd_kv_append", "mtd_attn_prefill_chunk", "mtd_attn_prefill_workspace_bytes",
               "mtd_attn_decode", "mtd_attn_decode_workspace_bytes", "mtd_status_string",
-              "mtd_last_error", "mtd_abi_version", "mtd_qkv_proj", "mtd_o_proj"):
+              "mtd_last_error", "mtd_abi_version", "mtd_qkv_proj", "mtd_o_proj", "mtd_attn_merge"):
         assert n in names
 
 
@@ -283,3 +283,31 @@ def test_projections_of_no_tokens_enqueue_nothing(lib):
     """n_tok = 0 is valid and returns before any HIP call (so it runs without a GPU)."""
     assert qkv(lib, n_tok=0) == mtd.MTD_OK
     assert oproj(lib, n_tok=0) == mtd.MTD_OK
+
+
+def merge(lib, **kw):
+    a = dict(o=FAKE, l=FAKE, n_parts=3, n_rows=10, d=128, out=FAKE, lse=FAKE)
+    a.update(kw)
+    return lib.mtd_attn_merge(a["o"], a["l"], a["n_parts"], a["n_rows"], a["d"], a["out"], a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_parts=0), mtd.MTD_ERR_INVALID_ARG),
+    (dict(n_parts=mtd.MTD_MAX_MERGE_PARTS + 1), mtd.MTD_ERR_INVALID_ARG),
+    (dict(n_rows=-1), mtd.MTD_ERR_INVALID_ARG),
+    (dict(d=64), mtd.MTD_ERR_UNSUPPORTED),
+    (dict(o=None), mtd.MTD_ERR_INVALID_ARG),
+    (dict(l=None), mtd.MTD_ERR_INVALID_ARG),
+    (dict(out=None), mtd.MTD_ERR_INVALID_ARG),
+    (dict(lse=None), mtd.MTD_ERR_INVALID_ARG),
+    (dict(o=FAKE + 4), mtd.MTD_ERR_INVALID_ARG),
+    (dict(out=FAKE + 8), mtd.MTD_ERR_INVALID_ARG),
+])
+def test_merge_validation(lib, kw, code):
+    assert merge(lib, **kw) == code
+    assert lib.mtd_last_error().decode() != ""
+
+
+def test_merge_of_no_rows_enqueues_nothing(lib):
+    assert merge(lib, n_rows=0) == mtd.MTD_OK
+    assert merge(lib, n_rows=0, n_parts=mtd.MTD_MAX_MERGE_PARTS) == mtd.MTD_OK

@@ -1,0 +1,81 @@
+"""Sequence-split decode on one GPU: what each GPU of a sequence split would compute, and the merge.
+
+A request's KV split by sequence over S GPUs: GPU k holds the pages of tokens [c_k, c_{k+1}) and
+runs mtd_attn_decode over them (a block table starting at page c_k / 64, kv_len = its token count),
+giving that range's (O, LSE); after the gather, mtd_attn_merge combines the S partials.  Here the
+S shards run one after another on one GPU.  The merged result must match the oracle over the whole
+request within the attention gates; its distance to the unsplit library decode (which cuts the
+request into other splits, and rounds P to bf16 against each split's own maximum) is logged and
+held to the same gates.  mtd_attn_merge alone is checked against the oracle's
+lse_merge, including parts and rows with no keys.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_common import DecodeBatch, compare, log
+
+pytestmark = pytest.mark.gpu
+
+mtd = pytest.importorskip("gqa_kv_cache_qwen3_amd")
+
+
+def test_merge_matches_oracle():
+    rs = np.random.default_rng(W.torch_seed(9, 1))
+    for n_parts, rows in [(1, 3), (2, 80), (3, 37), (8, 160)]:
+        log(f"merge: {n_parts} parts x {rows} rows")
+        o = rs.standard_normal((n_parts, rows, W.HEAD_DIM)).astype(np.float32)
+        l = (rs.standard_normal((n_parts, rows)) * 4).astype(np.float32)
+        if n_parts > 1:
+            l[0, ::3] = -np.inf          # some parts hold no keys
+        l[:, rows - 1] = -np.inf         # and one row has no keys at all
+        out, lse = mtd.mtd_attn_merge(torch.from_numpy(o).cuda(), torch.from_numpy(l).cuda())
+        torch.cuda.synchronize()
+        out, lse = out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+        assert np.all(out[rows - 1] == 0) and lse[rows - 1] == -np.inf
+        o_ref, l_ref = oracle.lse_merge(o[:, : rows - 1], l[:, : rows - 1])
+        assert np.abs(out[: rows - 1] - o_ref).max() <= 1e-5 * max(1.0, np.abs(o_ref).max())
+        assert np.abs(lse[: rows - 1] - l_ref).max() <= 1e-5 * max(1.0, np.abs(l_ref).max())
+
+
+def _shard_decode(batch, cuts):
+    """Decode every shard [cuts[k], cuts[k+1]) of every request; (O, LSE) partials [S][B][H][D]."""
+    b = len(batch.lens)
+    s = len(cuts) - 1
+    o_parts = torch.zeros((s, b, W.HQ, W.HEAD_DIM), dtype=torch.float32, device="cuda")
+    l_parts = torch.full((s, b, W.HQ), float("-inf"), dtype=torch.float32, device="cuda")
+    for k in range(s):
+        lo, hi = cuts[k], cuts[k + 1]
+        n = np.clip(np.minimum(batch.lens, hi) - lo, 0, None)
+        have = np.nonzero(n > 0)[0]
+        if len(have) == 0:
+            continue
+        idx = torch.as_tensor(have, device="cuda")
+        pages = (int(n.max()) + W.PAGE - 1) // W.PAGE
+        bt = batch.bt[idx][:, lo // W.PAGE: lo // W.PAGE + pages].contiguous()
+        lens = torch.as_tensor(n[have].astype(np.int32), device="cuda")
+        o, l = mtd.mtd_attn_decode(batch.k, batch.v, batch.q[idx].contiguous(), lens, bt, int(n.max()), W.SCALE)
+        o_parts[k, idx] = o
+        l_parts[k, idx] = l
+    return o_parts, l_parts
+
+
+@pytest.mark.parametrize("cuts", [[0, 1024, 1 << 17], [0, 512, 4096, 8192, 1 << 17], [0, 9984, 20032, 1 << 17]],
+                         ids=["2-way", "4-way", "3-way uneven"])
+def test_sequence_split_decode_matches_whole(cuts):
+    lens = [3000, 28500, 700, 9000, 20033, 64]
+    batch = DecodeBatch(lens, 104)
+    log(f"sequence-split decode: cuts={cuts} lens={lens}")
+    o_parts, l_parts = _shard_decode(batch, cuts)
+    out, lse = mtd.mtd_attn_merge(o_parts, l_parts)
+    whole_o, whole_l = mtd.mtd_attn_decode(batch.k, batch.v, batch.q, batch.kv_lens, batch.bt, batch.max_len, W.SCALE)
+    torch.cuda.synchronize()
+    d_o = (out - whole_o).abs().max().item()
+    d_l = (lse - whole_l).abs().max().item()
+    log(f"  against the unsplit decode: max |dO| {d_o:.3g}, max |dLSE| {d_l:.3g}")
+    assert d_o <= 1e-2 and d_l <= 1e-3
+    o_ref, l_ref = batch.reference()
+    compare(out, lse, o_ref, l_ref, f"sequence split {cuts}")
