@@ -39,6 +39,8 @@
 // Causal masking is applied only on tiles that reach past the workgroup's first position.  Keys
 // past the request's last token (tail of the last page) are loaded from the page's first row
 // instead of their slots, so V stays finite where their weight is exactly zero.
+// No score is ever NaN, so this file is compiled with -fno-honor-nans: the maxima then compile to
+// bare v_max3_f32 trees without NaN-quieting copies of their operands.
 #include <atomic>
 
 #include "device_util.h"
@@ -57,24 +59,33 @@ constexpr float kMaxFloor = -1e30f;  // initial running max: below any real scal
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4_t lds_short4_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
-typedef const __attribute__((address_space(1))) void global_cvoid_t;
+// Word 3 of a raw buffer resource descriptor on gfx9-family parts (32-bit data format, no
+// swizzle, no index stride).
+constexpr int kBufferWord3 = 0x00020000;
 
 // Direct-to-LDS load of one K or V tile, 2 instructions per wave.  Instruction inst fills slots
 // 64 inst .. 64 inst + 63 = column group inst/4, rows 16 (inst%4) .. +15; lane l writes slot
 // 64 inst + l and so fetches row 16 (inst%4) + l/4, chunk 4 (inst/4) + ((l%4) ^ g(row)), where
 // g = (row/4)%4 for K (kSwizzle) and 0 for V.  Rows >= nvalid fetch row 0 instead.
-template <bool kSwizzle>
-__device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ blk, uint8_t* lds, int wave,
-                                         int lane, int nvalid) {
+// The loads are buffer loads: the page's base address goes into a resource descriptor built by
+// the scalar unit, and each lane supplies a 32-bit byte offset within the 16 KiB block, so a
+// full tile costs no vector ALU work at all.
+__device__ __forceinline__ uint32_t dma_offset(int wave, int j, int lane, bool swizzle, int nvalid) {
+  const int inst = 2 * wave + j;
+  const int r = 16 * (inst & 3) + (lane >> 2);
+  const int c = 4 * (inst >> 2) + ((lane & 3) ^ (swizzle ? ((r >> 2) & 3) : 0));
+  const int rs = r < nvalid ? r : 0;
+  return (uint32_t)(rs * kHeadDim + c * 8) * 2u;
+}
+
+__device__ __forceinline__ void dma_tile(const uint16_t* blk, uint8_t* lds, int wave,
+                                         const uint32_t (&off)[2]) {
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(blk), (short)0, kTileBytes, kBufferWord3);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int inst = 2 * wave + j;
-    const int r = 16 * (inst & 3) + (lane >> 2);
-    const int c = 4 * (inst >> 2) + ((lane & 3) ^ (kSwizzle ? ((r >> 2) & 3) : 0));
-    const int rs = r < nvalid ? r : 0;
-    __builtin_amdgcn_global_load_lds((global_cvoid_t*)(blk + rs * kHeadDim + c * 8),
-                                     (lds_void_t*)(lds + inst * 1024), 16, 0, 0);
-  }
+  for (int j = 0; j < 2; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(lds + (2 * wave + j) * 1024), 16, off[j], 0,
+                                             0, 0);
 }
 
 // s_waitcnt vmcnt(0) (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8; the
@@ -98,6 +109,7 @@ struct TileArgs {
   const uint16_t* v_pages;
   const int32_t* block_table;
   int num_pages, g, total, wave, lane, n_tiles;
+  uint32_t k_off[2], v_off[2];  // this lane's byte offsets in a full K / V block
 };
 
 // Page id of tile kt (loaded one tile ahead of its DMA so the scalar load is never waited on).
@@ -109,9 +121,18 @@ __device__ __forceinline__ void issue_tile(const TileArgs& a, int kt, int page, 
                                            uint8_t* v_lds) {
   if (page < 0 || page >= a.num_pages) page = 0;  // out-of-pool ids: defined reads, unspecified result
   const size_t blk = ((size_t)page * kKvHeads + a.g) * (kPage * kHeadDim);
-  const int nvalid = min(kBK, a.total - kt * kBK);
-  dma_tile<true>(a.k_pages + blk, k_lds, a.wave, a.lane, nvalid);
-  dma_tile<false>(a.v_pages + blk, v_lds, a.wave, a.lane, nvalid);
+  const int nvalid = a.total - kt * kBK;
+  if (nvalid >= kBK) {
+    dma_tile(a.k_pages + blk, k_lds, a.wave, a.k_off);
+    dma_tile(a.v_pages + blk, v_lds, a.wave, a.v_off);
+  } else {  // the request's last, partly filled page
+    const uint32_t k_off[2] = {dma_offset(a.wave, 0, a.lane, true, nvalid),
+                               dma_offset(a.wave, 1, a.lane, true, nvalid)};
+    const uint32_t v_off[2] = {dma_offset(a.wave, 0, a.lane, false, nvalid),
+                               dma_offset(a.wave, 1, a.lane, false, nvalid)};
+    dma_tile(a.k_pages + blk, k_lds, a.wave, k_off);
+    dma_tile(a.v_pages + blk, v_lds, a.wave, v_off);
+  }
 }
 
 struct SoftmaxState {
@@ -164,11 +185,6 @@ __device__ __forceinline__ void load_v(bf16x8_t (&vf)[8], const uint8_t* v_lds, 
     }
 }
 
-// max(a, b) for values that are never NaN, as one v_med3_f32 with no operand canonicalisation.
-__device__ __forceinline__ float max_nn(float a, float b) {
-  return __builtin_amdgcn_fmed3f(a, b, __builtin_huge_valf());
-}
-
 // S^T block = K Q^T for this wave's 32 query columns.
 __device__ __forceinline__ floatx16_t mma_scores(const bf16x8_t (&kf)[8], const bf16x8_t (&qf)[8]) {
   floatx16_t st;
@@ -206,7 +222,7 @@ __device__ __forceinline__ float block_max(floatx16_t& st, float m, int key0, in
   float smax = fmaxf(fmaxf(fmaxf(a0, a1), a2), fmaxf(fmaxf(a3, a4), st[15]));
   float other = smax;
   swap_halves(smax, other);
-  return max_nn(m, max_nn(smax, other) * scale_log2);
+  return fmaxf(m, fmaxf(smax, other) * scale_log2);
 }
 
 // P^T operands of one block (exp2 of the scaled scores minus the running max, rounded to bf16)
@@ -283,7 +299,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
   __shared__ __attribute__((aligned(1024))) uint8_t v_lds2[kTileBytes];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS bases in scalar registers
   const int lane = tid & 63;
   const int n = lane & 31;   // query column of this lane
   const int hk = lane >> 5;  // which half of each 32-key block this lane holds
@@ -310,7 +326,17 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
   if (half && !cut) return;  // the second half of an item too short to split
   // Tiles whose keys all precede the workgroup's first query need no causal mask.
   const int n_plain = min((prefix_len + q0 + 1) / kBK, t1);
-  const TileArgs ta{k_pages, v_pages, block_table, num_pages, g, total, wave, lane, t1};
+  const TileArgs ta{k_pages,
+                    v_pages,
+                    block_table,
+                    num_pages,
+                    g,
+                    total,
+                    wave,
+                    lane,
+                    t1,
+                    {dma_offset(wave, 0, lane, true, kBK), dma_offset(wave, 1, lane, true, kBK)},
+                    {dma_offset(wave, 0, lane, false, kBK), dma_offset(wave, 1, lane, false, kBK)}};
 
   issue_tile(ta, t0, tile_page(ta, t0), k_lds0, v_lds0);
   int next_page = tile_page(ta, t0 + 1);
