@@ -173,7 +173,7 @@ class MixedStep:
         self.kv_lens = torch.as_tensor(self.lens.astype(np.int32), device=dev)
         self.max_len = int(self.lens.max())
         self.ws = torch.empty(mtd.decode_workspace_bytes(len(self.lens), self.max_len), dtype=torch.uint8, device=dev)
-        # prefill workspace: each position tile's keys run as two halves, merged (balances the causal work)
+        # prefill workspace: the library rebalances the causal work over the CUs and merges split tiles
         self.ws_p = torch.empty(mtd.prefill_workspace_bytes(self.chunk), dtype=torch.uint8, device=dev)
         self.o_a = torch.empty((self.chunk, W.HQ, W.HEAD_DIM), dtype=torch.float32, device=dev)
         self.l_a = torch.empty((self.chunk, W.HQ), dtype=torch.float32, device=dev)

@@ -165,7 +165,7 @@ def mtd_attn_prefill_chunk(k_pages, v_pages, q, prefix_len: int, block_table, sc
     """Causal attention of a chunk q ([C][Hq][D] bf16) at prefix_len over the pages.
 
     workspace: None (one pass per position tile) or a uint8 device tensor of at least
-    prefill_workspace_bytes(C) bytes (key range of each tile in two halves, merged).
+    prefill_workspace_bytes(C) bytes (causal work rebalanced over the CUs, split items merged).
     Returns (out float32 [C][Hq][D], lse float32 [C][Hq]).
     """
     layer = kv_layer(k_pages, v_pages)

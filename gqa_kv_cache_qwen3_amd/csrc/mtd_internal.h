@@ -49,7 +49,8 @@ hipError_t launch_kv_append(const KvPools& kv, const uint16_t* k_new, const uint
                             hipStream_t stream);
 
 // Optional prefill workspace: partial O float32 [chunk_len][kQHeads][kHeadDim], then partial LSE
-// float32 [chunk_len][kQHeads] (the second halves of split tiles).  workspace == nullptr: no split.
+// float32 [chunk_len][kQHeads] (one part of every split item, merged after the kernel).
+// workspace == nullptr: one pass per item, no split.
 size_t prefill_workspace_bytes(int chunk_len);
 
 hipError_t launch_prefill(const KvPools& kv, const uint16_t* q, int chunk_len, int prefix_len,

@@ -11,8 +11,10 @@
 // query rows.  Wave w takes positions 16w .. 16w+15 for both heads: 32 query columns.  Workgroup
 // id = 8 * (position tile, longest first) + KV head, so the dispatcher's round-robin over the 8
 // XCDs keeps all tiles of one KV head on one XCD and its L2 serves the K/V re-reads.  With a
-// workspace, an item can instead run as two workgroups over the two halves of its key tiles,
-// merged afterwards by prefill_merge_kernel (see launch_prefill for when that pays).
+// workspace, items are rebalanced instead (see launch_prefill): tiles t and T-1-t of a chunk
+// together always hold the same number of key tiles, so each such pair runs as two workgroups of
+// equal work, or, in short chunks, every item runs as two halves.  Split items are merged
+// afterwards by prefill_merge_kernel.
 //
 // K/V staging.  A 64-key tile is one page of the KV head: 16 KiB of K and 16 KiB of V, each
 // brought into LDS by 16-byte direct-to-LDS loads (global_load_lds_dwordx4, no registers, no
@@ -281,12 +283,50 @@ __device__ __forceinline__ void pipe_step(SoftmaxState& sm, floatx16_t& s_cur, f
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// How a chunk's (position tile, KV head) items are spread over workgroups.
+enum PrefillMode : int {
+  kOnePass = 0,  // one workgroup per item, longest first
+  kHalves = 1,   // two workgroups per item, one per half of its key tiles
+  kPairs = 2,    // items t and T-1-t share two workgroups with equal key-tile counts
+};
+
+// Key tiles of position tile qt: every key up to the tile's last position.
+__device__ __forceinline__ int item_tiles(int qt, int chunk_len, int prefix_len) {
+  const int kv_end = min(prefix_len + (qt + 1) * kBQ, prefix_len + chunk_len);
+  return (kv_end + kBK - 1) / kBK;
+}
+
+// kPairs: pair p joins the long tile T-1-p (L key tiles) and the short tile p (S tiles; none when
+// T is odd and p is the middle tile).  Their combined L + S tiles are the same for every pair, so
+// cutting that sequence at w = (L + S) / 2 gives two workgroups equal work: the first takes the
+// long tile's tiles [0, w), the second its tiles [w, L) and then the whole short tile.  The long
+// tile is split when 0 < w < L; its first part goes to the workspace and is merged afterwards.
+struct PairPlan {
+  int t_long, t_short, n_long, n_short, cut;
+};
+
+__device__ __forceinline__ PairPlan pair_plan(int p, int n_qtiles, int chunk_len, int prefix_len) {
+  PairPlan pp;
+  pp.t_long = n_qtiles - 1 - p;
+  pp.t_short = p < pp.t_long ? p : -1;
+  pp.n_long = item_tiles(pp.t_long, chunk_len, prefix_len);
+  pp.n_short = pp.t_short >= 0 ? item_tiles(pp.t_short, chunk_len, prefix_len) : 0;
+  pp.cut = (pp.n_long + pp.n_short) / 2;
+  return pp;
+}
+
+// One stretch of work for a workgroup: key tiles [t0, t1) of position tile qt, written to the
+// workspace (partial, merged later) or to out / lse.
+struct Segment {
+  int qt, t0, t1, to_ws;
+};
+
 __global__ __launch_bounds__(512, 1) void prefill_kernel(
     const uint16_t* __restrict__ k_pages, const uint16_t* __restrict__ v_pages, int num_pages,
     const uint16_t* __restrict__ q, int chunk_len, int prefix_len,
     const int32_t* __restrict__ block_table, float scale_log2, float* __restrict__ out,
     float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse, int n_qtiles,
-    int split) {
+    int mode) {
   // Three stages of (K, V) tiles, 96 KiB: the tile being read, the next tile (in flight, then
   // read from the middle of the current step on) and the stage the following DMA refills.
   // Separate arrays, so the compiler can see that the DMA into one stage never aliases the reads
@@ -304,26 +344,57 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
   const int n = lane & 31;   // query column of this lane
   const int hk = lane >> 5;  // which half of each 32-key block this lane holds
   const int g = blockIdx.x % kKvHeads;
-  // Work item: position tile qt of KV head g, longest first.  When split, each item is two
-  // workgroups, one per half of its key tiles (the dispatcher then pairs long and short halves on
-  // the CUs), and the second half's partial result goes to part_o / part_lse.
   const int rank = (int)(blockIdx.x / kKvHeads);
-  const int qt = n_qtiles - 1 - (split ? rank >> 1 : rank);
-  const int half = split ? rank & 1 : 0;
+  const int total = prefix_len + chunk_len;
+
+  // This workgroup's segments (at most two, run one after the other).
+  Segment seg0{0, 0, 0, 0}, seg1{0, 0, 0, 0};
+  int n_seg = 0;
+  if (mode == kPairs) {
+    const PairPlan pp = pair_plan(rank >> 1, n_qtiles, chunk_len, prefix_len);
+    const bool split_long = pp.cut > 0 && pp.cut < pp.n_long;
+    if ((rank & 1) == 0) {
+      if (pp.cut > 0) {
+        seg0 = Segment{pp.t_long, 0, min(pp.cut, pp.n_long), split_long ? 1 : 0};
+        n_seg = 1;
+      }
+    } else {
+      const Segment short_seg{pp.t_short, 0, pp.n_short, 0};
+      if (pp.cut < pp.n_long) {
+        seg0 = Segment{pp.t_long, pp.cut, pp.n_long, 0};
+        seg1 = short_seg;
+        n_seg = pp.t_short >= 0 ? 2 : 1;
+      } else if (pp.t_short >= 0) {
+        seg0 = short_seg;
+        n_seg = 1;
+      }
+    }
+  } else {
+    // Work item: position tile qt of KV head g, longest first.  kHalves: each item is two
+    // workgroups, one per half of its key tiles (the dispatcher then pairs long and short halves
+    // on the CUs), and the second half's partial result goes to the workspace.
+    const int split = mode == kHalves;
+    const int qt = n_qtiles - 1 - (split ? rank >> 1 : rank);
+    const int half = split ? rank & 1 : 0;
+    const int n_item = item_tiles(qt, chunk_len, prefix_len);
+    const bool cut = split && n_item >= 2;
+    seg0 = Segment{qt, cut && half ? n_item / 2 : 0, cut && !half ? n_item / 2 : n_item, half};
+    n_seg = half && !cut ? 0 : 1;  // the second half of an item too short to split has nothing to do
+  }
+
+  const LdsOffsets off = make_offsets(lane);
+  for (int si = 0; si < n_seg; ++si) {
+  if (si > 0) __syncthreads();  // every wave is done with the previous segment's LDS stages
+  // Uniform across the workgroup: keep the segment in scalar registers.
+  const int qt = __builtin_amdgcn_readfirstlane(si == 0 ? seg0.qt : seg1.qt);
+  const int t0 = __builtin_amdgcn_readfirstlane(si == 0 ? seg0.t0 : seg1.t0);
+  const int t1 = __builtin_amdgcn_readfirstlane(si == 0 ? seg0.t1 : seg1.t1);
+  const int half = __builtin_amdgcn_readfirstlane(si == 0 ? seg0.to_ws : seg1.to_ws);
   const int q0 = qt * kBQ;
   const int qpos = q0 + 16 * wave + (n & 15);
   const int head = kGroup * g + (n >> 4);
   const bool qvalid = qpos < chunk_len;
   const int qabs = prefix_len + qpos;
-  const int total = prefix_len + chunk_len;
-
-  const int kv_end = min(prefix_len + q0 + kBQ, total);
-  const int n_item = (kv_end + kBK - 1) / kBK;
-  // This workgroup's key tiles [t0, t1): all of them, or one half when the item is split.
-  const bool cut = split && n_item >= 2;
-  const int t0 = cut && half ? n_item / 2 : 0;
-  const int t1 = cut && !half ? n_item / 2 : n_item;
-  if (half && !cut) return;  // the second half of an item too short to split
   // Tiles whose keys all precede the workgroup's first query need no causal mask.
   const int n_plain = min((prefix_len + q0 + 1) / kBK, t1);
   const TileArgs ta{k_pages,
@@ -356,7 +427,6 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
       qf[ks] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
-  const LdsOffsets off = make_offsets(lane);
 
   SoftmaxState sm;
 #pragma unroll
@@ -453,22 +523,29 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
                         sm.o_acc[dt][4 * a + 2] * inv, sm.o_acc[dt][4 * a + 3] * inv);
     if (hk == 0) l_dst[(size_t)qpos * kQHeads + head] = l_tot > 0.f ? (sm.m + log2f(l_tot)) * kLn2 : kNegInf;
   }
+  }  // segments
 }
 
-// Combines the two halves of every split item: out/lse hold the first half's normalised partial,
-// part_o/part_lse the second's.  One wavefront per (position, head) row; each lane takes 2 dims.
+// Combines the two parts of every split item: out/lse hold one part's normalised partial,
+// part_o/part_lse the other's.  One wavefront per (position, head) row; each lane takes 2 dims.
 // Both LSEs are read before lane 0 overwrites lse, in program order within the wave.
 __global__ __launch_bounds__(256) void prefill_merge_kernel(float* __restrict__ out, float* __restrict__ lse,
                                                             const float* __restrict__ part_o,
                                                             const float* __restrict__ part_lse,
-                                                            int chunk_len, int prefix_len) {
+                                                            int chunk_len, int prefix_len, int n_qtiles,
+                                                            int mode) {
   const int row = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);  // (position, head)
   const int lane = threadIdx.x & 63;
   if (row >= chunk_len * kQHeads) return;
-  const int qpos = row / kQHeads;
-  const int q0 = (qpos / kBQ) * kBQ;
-  const int kv_end = min(prefix_len + q0 + kBQ, prefix_len + chunk_len);
-  if ((kv_end + kBK - 1) / kBK < 2) return;  // item was not split: out/lse are final
+  const int qt = row / kQHeads / kBQ;
+  if (mode == kPairs) {
+    const int p = n_qtiles - 1 - qt;  // the pair in which qt is the long tile
+    if (p > qt) return;               // qt is a short tile: never split
+    const PairPlan pp = pair_plan(p, n_qtiles, chunk_len, prefix_len);
+    if (pp.cut <= 0 || pp.cut >= pp.n_long) return;  // not split: out/lse are final
+  } else if (item_tiles(qt, chunk_len, prefix_len) < 2) {
+    return;  // item was not split: out/lse are final
+  }
   const float l0 = lse[row], l1 = part_lse[row];
   const float mx = fmaxf(l0, l1);
   const float w0 = __expf(l0 - mx), w1 = __expf(l1 - mx);
@@ -504,26 +581,27 @@ hipError_t launch_prefill(const KvPools& kv, const uint16_t* q, int chunk_len, i
                           const int32_t* block_table, float scale, void* workspace, float* out,
                           float* lse, hipStream_t stream) {
   const int n_qtiles = (chunk_len + kBQ - 1) / kBQ;
-  // Splitting pays where one pass would leave CUs idle: when there are fewer (tile, KV head)
-  // items than CUs (chunks shorter than 32 tiles on a 256-CU part), and where the causal work per
-  // tile is very uneven (the last tile of a chunk sees prefix + chunk keys, the first only
-  // prefix).  It has costs: the merge pass, and K/V read twice from HBM because the second-round
-  // halves start at staggered times and miss the L2 reuse of workgroups that sweep the same tiles
-  // together.  With a prefix above twice the chunk the spread is under 20 % and the clock the
-  // early-idle CUs free absorbs most of it (measured: +18 % at a 0 prefix, +4 % at 4096, +0.4 % at
-  // 32,768, -1 % at 61,440 for 4096-token chunks), so such chunks run in one pass.
-  const int split = workspace != nullptr &&
-                    (prefix_len <= 2 * chunk_len || n_qtiles * kKvHeads < device_cus());
+  // Causal work is uneven over a chunk's position tiles (the last sees prefix + chunk keys, the
+  // first only prefix), and with one workgroup per CU the time is set by the longest.  With a
+  // workspace the library rebalances:
+  //   - at least as many items as CUs: pair tile t with tile T-1-t and cut their combined key
+  //     tiles into two equal workgroups (the long tile's two parts merged afterwards);
+  //   - fewer items than CUs (short chunks): split every item's keys in two halves, which also
+  //     doubles the workgroups.
+  // Both cost the merge pass over the split rows.  Without a workspace, one pass per item.
+  int mode = kOnePass;
+  if (workspace != nullptr) mode = n_qtiles * kKvHeads >= device_cus() ? kPairs : kHalves;
+  const int n_wg = mode == kPairs ? 2 * ((n_qtiles + 1) / 2) : mode == kHalves ? 2 * n_qtiles : n_qtiles;
   float* part_o = static_cast<float*>(workspace);
-  float* part_lse = split ? part_o + (size_t)chunk_len * kQHeads * kHeadDim : nullptr;
-  prefill_kernel<<<dim3(n_qtiles * kKvHeads * (split ? 2 : 1)), dim3(64 * kWaves), 0, stream>>>(
+  float* part_lse = mode != kOnePass ? part_o + (size_t)chunk_len * kQHeads * kHeadDim : nullptr;
+  prefill_kernel<<<dim3(n_wg * kKvHeads), dim3(64 * kWaves), 0, stream>>>(
       kv.k, kv.v, kv.num_pages, q, chunk_len, prefix_len, block_table, scale * kLog2e, out, lse,
-      part_o, part_lse, n_qtiles, split);
+      part_o, part_lse, n_qtiles, mode);
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess || !split) return err;
+  if (err != hipSuccess || mode == kOnePass) return err;
   const int rows = chunk_len * kQHeads;
   prefill_merge_kernel<<<dim3((rows + 3) / 4), dim3(256), 0, stream>>>(out, lse, part_o, part_lse,
-                                                                      chunk_len, prefix_len);
+                                                                      chunk_len, prefix_len, n_qtiles, mode);
   return hipGetLastError();
 }
 

@@ -132,12 +132,13 @@ int mtd_kv_append(const mtd_kv_layer_t* kv, const void* k_new, const void* v_new
  *   workspace       NULL, or device scratch of at least mtd_attn_prefill_workspace_bytes(chunk_len,
  *                   num_q_heads, head_dim) bytes (else MTD_ERR_WORKSPACE), owned by the caller,
  *                   contents ignored on entry and unspecified on return.  With a workspace, the
- *                   keys of each (128-position tile, KV head) are processed in two halves whose
- *                   partial results are merged by log-sum-exp whenever one pass would leave
- *                   compute units idle: when there are fewer such items than compute units, or
- *                   when prefix_len <= 2 * chunk_len (uneven causal work).  Otherwise, and
- *                   without a workspace, each tile is one pass.  Both give correct results; their
- *                   bits differ.  Calls on different streams need different workspaces.
+ *                   causal work of the (128-position tile, KV head) items is rebalanced over the
+ *                   compute units, and the parts of a split item are merged by log-sum-exp: with
+ *                   at least as many items as compute units, tiles t and T-1-t (T tiles in the
+ *                   chunk) share two workgroups that each take half of their combined keys;
+ *                   with fewer, every item's keys run as two halves.  Without a workspace, each
+ *                   item is one pass.  All give correct results; their bits differ.  Calls on
+ *                   different streams need different workspaces.
  *   out             float32 [chunk_len][num_q_heads][head_dim], written
  *   lse             float32 [chunk_len][num_q_heads], written: natural-log sum of exp(s_j)
  */

@@ -182,7 +182,7 @@ def test_decode_validation(lib, kw, code):
 
 
 def test_prefill_workspace_size_formula(lib):
-    # the second halves' partial O and LSE: chunk_len rows of 16 heads x (128 + 1) floats
+    # one part of every split item, partial O and LSE: chunk_len rows of 16 heads x (128 + 1) floats
     for c in (1, 2, 127, 128, 129, 4096, 131072):
         assert lib.mtd_attn_prefill_workspace_bytes(c, 16, 128) == c * 16 * 129 * 4
     assert lib.mtd_attn_prefill_workspace_bytes(0, 16, 128) == 0

@@ -1,8 +1,9 @@
 """mtd_attn_prefill_chunk on the GPU against the fp64 oracle: one-shot and chunked prefill over
 pages written by mtd_kv_append, at small ragged shapes in full and at the 90-minute and
 mixed-step sizes on sampled rows; plus chunked == one-shot and decode == 1-row prefill.  The
-checks run both without a workspace (one pass per position tile) and with one (each tile's keys
-in two halves, merged by log-sum-exp, wherever one pass would leave compute units idle)."""
+checks run both without a workspace (one pass per position tile) and with one (the causal work
+rebalanced over the compute units: tiles t and T-1-t paired into two equal workgroups, or each
+tile's keys in two halves for short chunks; split tiles merged by log-sum-exp)."""
 
 import numpy as np
 import pytest
@@ -74,7 +75,8 @@ SPLIT = pytest.mark.parametrize("split", [False, True], ids=["one-pass", "split"
 
 @SPLIT
 @pytest.mark.parametrize("prefix,chunk", [(0, 1), (0, 64), (0, 65), (5, 1), (63, 2), (50, 37), (100, 37),
-                                          (64, 64), (500, 300), (1000, 300), (0, 439), (4096, 4096)])
+                                          (64, 64), (500, 300), (1000, 300), (0, 439), (4096, 4096),
+                                          (100, 4200), (0, 8192)])
 def test_prefill_small_full_compare(prefix, chunk, split):
     log(f"prefill prefix={prefix} chunk={chunk} split={split}")
     req = Request(prefix + chunk, 200 + prefix + 7 * chunk, split=split)
