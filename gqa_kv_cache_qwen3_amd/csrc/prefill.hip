@@ -151,6 +151,7 @@ struct SoftmaxState {
 //                -> + 4096 dt + 64 (32 mt + 16 t + 8 sec)
 struct LdsOffsets {
   int kbase[2];
+  int kbase_hi[2];  // kbase + 64 KiB, for stages beyond the 16-bit immediate offset range
   int vbase;
 };
 
@@ -158,18 +159,25 @@ __device__ __forceinline__ LdsOffsets make_offsets(int lane) {
   LdsOffsets o;
   const int n = lane & 31, hk = lane >> 5, gi = lane & 15, half = (lane >> 4) & 1;
 #pragma unroll
-  for (int e = 0; e < 2; ++e) o.kbase[e] = 64 * n + 16 * ((2 * e + hk) ^ ((n >> 2) & 3));
+  for (int e = 0; e < 2; ++e) {
+    o.kbase[e] = 64 * n + 16 * ((2 * e + hk) ^ ((n >> 2) & 3));
+    o.kbase_hi[e] = o.kbase[e] + 65536;
+    asm volatile("" : "+v"(o.kbase_hi[e]));  // keep it in a register
+  }
   o.vbase = 64 * (4 * hk + (gi >> 2)) + 16 * (2 * half + ((gi & 3) >> 1)) + 8 * (gi & 1);
   return o;
 }
 
-// K fragments of 32-key block mt (keys 32mt .. 32mt+31 of the tile), one per k-step.
-__device__ __forceinline__ void load_k(bf16x8_t (&kf)[8], const uint8_t* k_lds, const LdsOffsets& off,
+// K fragments of 32-key block mt (keys 32mt .. 32mt+31 of the tile), one per k-step.  hi: the stage
+// lies past 64 KiB, so the address is formed from kbase_hi (the same byte address) to keep the
+// immediate offset within 16 bits.
+__device__ __forceinline__ void load_k(bf16x8_t (&kf)[8], const uint8_t* k_lds, bool hi, const LdsOffsets& off,
                                        int mt) {
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks)
-    kf[ks] = __builtin_bit_cast(
-        bf16x8_t, *reinterpret_cast<const uint4*>(k_lds + off.kbase[ks & 1] + 4096 * (ks >> 1) + 2048 * mt));
+  for (int ks = 0; ks < 8; ++ks) {
+    const uint8_t* p = hi ? k_lds - 65536 + off.kbase_hi[ks & 1] : k_lds + off.kbase[ks & 1];
+    kf[ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(p + 4096 * (ks >> 1) + 2048 * mt));
+  }
 }
 
 // V^T fragments of block mt: k-step t of dim tile dt holds this lane's 8 keys 32mt + 16t + 4hk +
@@ -257,7 +265,7 @@ __device__ __forceinline__ float block_exp(const floatx16_t& st, float m_use, fl
 template <bool kMask, bool kScore>
 __device__ __forceinline__ void pipe_step(SoftmaxState& sm, floatx16_t& s_cur, floatx16_t& s_next,
                                           bf16x8_t (&p_prev)[2], bf16x8_t (&v_prev)[8],
-                                          const bf16x8_t (&qf)[8], const uint8_t* k_lds, int mt_next,
+                                          const bf16x8_t (&qf)[8], const uint8_t* k_lds, bool k_hi, int mt_next,
                                           const uint8_t* v_lds, int mt_cur, const LdsOffsets& off,
                                           int key0, int hk, int qabs, float scale_log2) {
   if (__any(sm.alpha != 1.f)) {
@@ -267,7 +275,7 @@ __device__ __forceinline__ void pipe_step(SoftmaxState& sm, floatx16_t& s_cur, f
       for (int v = 0; v < 16; ++v) sm.o_acc[dt][v] *= sm.alpha;
   }
   bf16x8_t kf[8], vf[8];
-  if (kScore) load_k(kf, k_lds, off, mt_next);
+  if (kScore) load_k(kf, k_lds, k_hi, off, mt_next);
   const float m_new = block_max<kMask>(s_cur, sm.m, key0, hk, qabs, scale_log2);
   if (kScore) s_next = mma_scores(kf, qf);
   mma_pv(sm.o_acc, v_prev, p_prev);
@@ -330,12 +338,15 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
   // Three stages of (K, V) tiles, 96 KiB: the tile being read, the next tile (in flight, then
   // read from the middle of the current step on) and the stage the following DMA refills.
   // Separate arrays, so the compiler can see that the DMA into one stage never aliases the reads
-  // of another and adds no wait of its own between them.
-  __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[kTileBytes];
+  // of another and adds no wait of its own between them.  The compiler places LDS variables of
+  // equal size and alignment in name order, so the V stages take bytes 0 .. 48 KiB and every V^T
+  // read (16 per block) is a base register plus a 16-bit immediate offset; the K stages follow,
+  // and those past 64 KiB are read through kbase_hi.
+  __shared__ __attribute__((aligned(1024))) uint8_t zk_lds0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t v_lds0[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t k_lds1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t zk_lds1[kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t v_lds1[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t k_lds2[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t zk_lds2[kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t v_lds2[kTileBytes];
 
   const int tid = threadIdx.x;
@@ -409,7 +420,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
                     {dma_offset(wave, 0, lane, true, kBK), dma_offset(wave, 1, lane, true, kBK)},
                     {dma_offset(wave, 0, lane, false, kBK), dma_offset(wave, 1, lane, false, kBK)}};
 
-  issue_tile(ta, t0, tile_page(ta, t0), k_lds0, v_lds0);
+  issue_tile(ta, t0, tile_page(ta, t0), zk_lds0, v_lds0);
   int next_page = tile_page(ta, t0 + 1);
   // Stage 2's V starts as zeros: the first step multiplies it by an all-zero P^T in place of a
   // previous block.
@@ -439,14 +450,14 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
 
   wait_dma();
   __syncthreads();
-  if (t0 + 1 < t1) issue_tile(ta, t0 + 1, next_page, k_lds1, v_lds1);
+  if (t0 + 1 < t1) issue_tile(ta, t0 + 1, next_page, zk_lds1, v_lds1);
   next_page = tile_page(ta, t0 + 2);
   floatx16_t s_a, s_b;
   bf16x8_t p_prev[2], v_prev[8];
   load_v(v_prev, v_lds2, off, 1);  // zeros: stands in for the V^T of block -1
   {
     bf16x8_t kf[8];
-    load_k(kf, k_lds0, off, 0);
+    load_k(kf, zk_lds0, false, off, 0);
     s_a = mma_scores(kf, qf);
     const bf16x8_t zero = __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
     p_prev[0] = zero;
@@ -462,39 +473,39 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
   // steps with run-time stages (masked) and the last tile, then block 2n-1's O update.
 #define MTD_PREFILL_STEP(KT, CUR_K, CUR_V, PRV_V, NXT_K, PRV_K, MASK)                         \
   {                                                                                           \
-    pipe_step<MASK, true>(sm, s_a, s_b, p_prev, v_prev, qf, CUR_K, 1, CUR_V, 0, off,          \
+    pipe_step<MASK, true>(sm, s_a, s_b, p_prev, v_prev, qf, CUR_K, +(CUR_K) != +zk_lds0, 1, CUR_V, 0, off, \
                           (KT) * kBK, hk, qabs, scale_log2);                                  \
     wait_dma();                                                                               \
     tile_barrier();                                                                           \
     if ((KT) + 2 < t1) issue_tile(ta, (KT) + 2, next_page, PRV_K, PRV_V);                     \
     next_page = tile_page(ta, (KT) + 3);                                                      \
-    pipe_step<MASK, true>(sm, s_b, s_a, p_prev, v_prev, qf, NXT_K, 0, CUR_V, 1, off,          \
+    pipe_step<MASK, true>(sm, s_b, s_a, p_prev, v_prev, qf, NXT_K, +(NXT_K) != +zk_lds0, 0, CUR_V, 1, off, \
                           (KT) * kBK + 32, hk, qabs, scale_log2);                             \
   }
   const int n_main = min(n_plain, t1 - 1);
   int kt = t0;
   for (; kt + 3 <= n_main; kt += 3) {
-    MTD_PREFILL_STEP(kt, k_lds0, v_lds0, v_lds2, k_lds1, k_lds2, false)
-    MTD_PREFILL_STEP(kt + 1, k_lds1, v_lds1, v_lds0, k_lds2, k_lds0, false)
-    MTD_PREFILL_STEP(kt + 2, k_lds2, v_lds2, v_lds1, k_lds0, k_lds1, false)
+    MTD_PREFILL_STEP(kt, zk_lds0, v_lds0, v_lds2, zk_lds1, zk_lds2, false)
+    MTD_PREFILL_STEP(kt + 1, zk_lds1, v_lds1, v_lds0, zk_lds2, zk_lds0, false)
+    MTD_PREFILL_STEP(kt + 2, zk_lds2, v_lds2, v_lds1, zk_lds0, zk_lds1, false)
   }
   for (; kt < t1 - 1; ++kt) {
     const int sc = (kt - t0) % 3;
-    uint8_t* ck = sc == 0 ? k_lds0 : sc == 1 ? k_lds1 : k_lds2;
+    uint8_t* ck = sc == 0 ? zk_lds0 : sc == 1 ? zk_lds1 : zk_lds2;
     uint8_t* cv = sc == 0 ? v_lds0 : sc == 1 ? v_lds1 : v_lds2;
-    uint8_t* nk = sc == 0 ? k_lds1 : sc == 1 ? k_lds2 : k_lds0;
-    uint8_t* pk = sc == 0 ? k_lds2 : sc == 1 ? k_lds0 : k_lds1;
+    uint8_t* nk = sc == 0 ? zk_lds1 : sc == 1 ? zk_lds2 : zk_lds0;
+    uint8_t* pk = sc == 0 ? zk_lds2 : sc == 1 ? zk_lds0 : zk_lds1;
     uint8_t* pv = sc == 0 ? v_lds2 : sc == 1 ? v_lds0 : v_lds1;
     MTD_PREFILL_STEP(kt, ck, cv, pv, nk, pk, true)
   }
 #undef MTD_PREFILL_STEP
   {
     const int sc = (kt - t0) % 3;
-    const uint8_t* ck = sc == 0 ? k_lds0 : sc == 1 ? k_lds1 : k_lds2;
+    const uint8_t* ck = sc == 0 ? zk_lds0 : sc == 1 ? zk_lds1 : zk_lds2;
     const uint8_t* cv = sc == 0 ? v_lds0 : sc == 1 ? v_lds1 : v_lds2;
-    pipe_step<true, true>(sm, s_a, s_b, p_prev, v_prev, qf, ck, 1, cv, 0, off, kt * kBK, hk, qabs,
+    pipe_step<true, true>(sm, s_a, s_b, p_prev, v_prev, qf, ck, ck != zk_lds0, 1, cv, 0, off, kt * kBK, hk, qabs,
                           scale_log2);
-    pipe_step<true, false>(sm, s_b, s_a, p_prev, v_prev, qf, ck, 0, cv, 1, off, kt * kBK + 32, hk,
+    pipe_step<true, false>(sm, s_b, s_a, p_prev, v_prev, qf, ck, ck != zk_lds0, 0, cv, 1, off, kt * kBK + 32, hk,
                            qabs, scale_log2);
     if (__any(sm.alpha != 1.f)) {
 #pragma unroll
