@@ -395,145 +395,147 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
 
   const LdsOffsets off = make_offsets(lane);
   for (int si = 0; si < n_seg; ++si) {
-  if (si > 0) __syncthreads();  // every wave is done with the previous segment's LDS stages
-  // Uniform across the workgroup: keep the segment in scalar registers.
-  const int qt = __builtin_amdgcn_readfirstlane(si == 0 ? seg0.qt : seg1.qt);
-  const int t0 = __builtin_amdgcn_readfirstlane(si == 0 ? seg0.t0 : seg1.t0);
-  const int t1 = __builtin_amdgcn_readfirstlane(si == 0 ? seg0.t1 : seg1.t1);
-  const int half = __builtin_amdgcn_readfirstlane(si == 0 ? seg0.to_ws : seg1.to_ws);
-  const int q0 = qt * kBQ;
-  const int qpos = q0 + 16 * wave + (n & 15);
-  const int head = kGroup * g + (n >> 4);
-  const bool qvalid = qpos < chunk_len;
-  const int qabs = prefix_len + qpos;
-  // Tiles whose keys all precede the workgroup's first query need no causal mask.
-  const int n_plain = min((prefix_len + q0 + 1) / kBK, t1);
-  const TileArgs ta{k_pages,
-                    v_pages,
-                    block_table,
-                    num_pages,
-                    g,
-                    total,
-                    wave,
-                    lane,
-                    t1,
-                    {dma_offset(wave, 0, lane, true, kBK), dma_offset(wave, 1, lane, true, kBK)},
-                    {dma_offset(wave, 0, lane, false, kBK), dma_offset(wave, 1, lane, false, kBK)}};
+    if (si > 0) __syncthreads();  // every wave is done with the previous segment's LDS stages
+    // Uniform across the workgroup: keep the segment in scalar registers.
+    const int qt = __builtin_amdgcn_readfirstlane(si == 0 ? seg0.qt : seg1.qt);
+    const int t0 = __builtin_amdgcn_readfirstlane(si == 0 ? seg0.t0 : seg1.t0);
+    const int t1 = __builtin_amdgcn_readfirstlane(si == 0 ? seg0.t1 : seg1.t1);
+    const int half = __builtin_amdgcn_readfirstlane(si == 0 ? seg0.to_ws : seg1.to_ws);
+    const int q0 = qt * kBQ;
+    const int qpos = q0 + 16 * wave + (n & 15);
+    const int head = kGroup * g + (n >> 4);
+    const bool qvalid = qpos < chunk_len;
+    const int qabs = prefix_len + qpos;
+    // Tiles whose keys all precede the workgroup's first query need no causal mask.
+    const int n_plain = min((prefix_len + q0 + 1) / kBK, t1);
+    const TileArgs ta{k_pages,
+                      v_pages,
+                      block_table,
+                      num_pages,
+                      g,
+                      total,
+                      wave,
+                      lane,
+                      t1,
+                      {dma_offset(wave, 0, lane, true, kBK), dma_offset(wave, 1, lane, true, kBK)},
+                      {dma_offset(wave, 0, lane, false, kBK), dma_offset(wave, 1, lane, false, kBK)}};
 
-  issue_tile(ta, t0, tile_page(ta, t0), zk_lds0, v_lds0);
-  int next_page = tile_page(ta, t0 + 1);
-  // Stage 2's V starts as zeros: the first step multiplies it by an all-zero P^T in place of a
-  // previous block.
-  *reinterpret_cast<uint4*>(v_lds2 + 32 * tid) = make_uint4(0, 0, 0, 0);
-  *reinterpret_cast<uint4*>(v_lds2 + 32 * tid + 16) = make_uint4(0, 0, 0, 0);
+    issue_tile(ta, t0, tile_page(ta, t0), zk_lds0, v_lds0);
+    int next_page = tile_page(ta, t0 + 1);
+    // Stage 2's V starts as zeros: the first step multiplies it by an all-zero P^T in place of a
+    // previous block.
+    *reinterpret_cast<uint4*>(v_lds2 + 32 * tid) = make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(v_lds2 + 32 * tid + 16) = make_uint4(0, 0, 0, 0);
 
-  // Q^T fragments: k-step ks covers dims 16ks..16ks+15; this lane holds dims 16ks+8hk..+7.
-  bf16x8_t qf[8];
-  {
-    const uint16_t* qrow = q + ((size_t)(qvalid ? qpos : 0) * kQHeads + head) * kHeadDim;
+    // Q^T fragments: k-step ks covers dims 16ks..16ks+15; this lane holds dims 16ks+8hk..+7.
+    bf16x8_t qf[8];
+    {
+      const uint16_t* qrow = q + ((size_t)(qvalid ? qpos : 0) * kQHeads + head) * kHeadDim;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (qvalid) v = *reinterpret_cast<const uint4*>(qrow + 16 * ks + 8 * hk);
-      qf[ks] = __builtin_bit_cast(bf16x8_t, v);
+      for (int ks = 0; ks < 8; ++ks) {
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (qvalid) v = *reinterpret_cast<const uint4*>(qrow + 16 * ks + 8 * hk);
+        qf[ks] = __builtin_bit_cast(bf16x8_t, v);
+      }
     }
-  }
 
-  SoftmaxState sm;
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) sm.o_acc[dt][v] = 0.f;
-  sm.m = kMaxFloor;
-  sm.l = 0.f;
-  sm.alpha = 1.f;
-
-  wait_dma();
-  __syncthreads();
-  if (t0 + 1 < t1) issue_tile(ta, t0 + 1, next_page, zk_lds1, v_lds1);
-  next_page = tile_page(ta, t0 + 2);
-  floatx16_t s_a, s_b;
-  bf16x8_t p_prev[2], v_prev[8];
-  load_v(v_prev, v_lds2, off, 1);  // zeros: stands in for the V^T of block -1
-  {
-    bf16x8_t kf[8];
-    load_k(kf, zk_lds0, false, off, 0);
-    s_a = mma_scores(kf, qf);
-    const bf16x8_t zero = __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
-    p_prev[0] = zero;
-    p_prev[1] = zero;
-  }
-
-  // Tile kt lives in stage (kt - t0) % 3.  Step kt: first half = softmax of block 2kt beside the scores
-  // of block 2kt+1 and the O update of block 2kt-1, reading block 2kt's V^T; then wait for tile
-  // kt+1's DMA and barrier (everyone is done with tile kt-1's stage), start tile kt+2's DMA into
-  // that stage; second half = softmax of block 2kt+1 beside the scores of block 2kt+2 (next
-  // stage) and the O update of block 2kt, reading block 2kt+1's V^T.  Main loop: three steps per
-  // trip with compile-time stages, no causal mask, never the last tile.  Then the remaining
-  // steps with run-time stages (masked) and the last tile, then block 2n-1's O update.
-#define MTD_PREFILL_STEP(KT, CUR_K, CUR_V, PRV_V, NXT_K, PRV_K, MASK)                         \
-  {                                                                                           \
-    pipe_step<MASK, true>(sm, s_a, s_b, p_prev, v_prev, qf, CUR_K, +(CUR_K) != +zk_lds0, 1, CUR_V, 0, off, \
-                          (KT) * kBK, hk, qabs, scale_log2);                                  \
-    wait_dma();                                                                               \
-    tile_barrier();                                                                           \
-    if ((KT) + 2 < t1) issue_tile(ta, (KT) + 2, next_page, PRV_K, PRV_V);                     \
-    next_page = tile_page(ta, (KT) + 3);                                                      \
-    pipe_step<MASK, true>(sm, s_b, s_a, p_prev, v_prev, qf, NXT_K, +(NXT_K) != +zk_lds0, 0, CUR_V, 1, off, \
-                          (KT) * kBK + 32, hk, qabs, scale_log2);                             \
-  }
-  const int n_main = min(n_plain, t1 - 1);
-  int kt = t0;
-  for (; kt + 3 <= n_main; kt += 3) {
-    MTD_PREFILL_STEP(kt, zk_lds0, v_lds0, v_lds2, zk_lds1, zk_lds2, false)
-    MTD_PREFILL_STEP(kt + 1, zk_lds1, v_lds1, v_lds0, zk_lds2, zk_lds0, false)
-    MTD_PREFILL_STEP(kt + 2, zk_lds2, v_lds2, v_lds1, zk_lds0, zk_lds1, false)
-  }
-  for (; kt < t1 - 1; ++kt) {
-    const int sc = (kt - t0) % 3;
-    uint8_t* ck = sc == 0 ? zk_lds0 : sc == 1 ? zk_lds1 : zk_lds2;
-    uint8_t* cv = sc == 0 ? v_lds0 : sc == 1 ? v_lds1 : v_lds2;
-    uint8_t* nk = sc == 0 ? zk_lds1 : sc == 1 ? zk_lds2 : zk_lds0;
-    uint8_t* pk = sc == 0 ? zk_lds2 : sc == 1 ? zk_lds0 : zk_lds1;
-    uint8_t* pv = sc == 0 ? v_lds2 : sc == 1 ? v_lds0 : v_lds1;
-    MTD_PREFILL_STEP(kt, ck, cv, pv, nk, pk, true)
-  }
-#undef MTD_PREFILL_STEP
-  {
-    const int sc = (kt - t0) % 3;
-    const uint8_t* ck = sc == 0 ? zk_lds0 : sc == 1 ? zk_lds1 : zk_lds2;
-    const uint8_t* cv = sc == 0 ? v_lds0 : sc == 1 ? v_lds1 : v_lds2;
-    pipe_step<true, true>(sm, s_a, s_b, p_prev, v_prev, qf, ck, ck != zk_lds0, 1, cv, 0, off, kt * kBK, hk, qabs,
-                          scale_log2);
-    pipe_step<true, false>(sm, s_b, s_a, p_prev, v_prev, qf, ck, ck != zk_lds0, 0, cv, 1, off, kt * kBK + 32, hk,
-                           qabs, scale_log2);
-    if (__any(sm.alpha != 1.f)) {
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) sm.o_acc[dt][v] *= sm.alpha;
-    }
-    mma_pv(sm.o_acc, v_prev, p_prev);
-  }
-
-  // A second half can hold no key a row may see (early rows of a short item): its partial is then
-  // O = 0 with LSE = -inf, which the merge weighs by exactly zero.
-  const float l_tot = sum_xor32(sm.l);
-  if (qvalid) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    float* const o_dst = half ? part_o : out;
-    float* const l_dst = half ? part_lse : lse;
-    float* orow = o_dst + ((size_t)qpos * kQHeads + head) * kHeadDim;
-    // Accumulator element v of tile dt is dim 32dt + 8(v/4) + 4hk + v%4.
+    SoftmaxState sm;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
-        *reinterpret_cast<float4*>(orow + 32 * dt + 8 * a + 4 * hk) =
-            make_float4(sm.o_acc[dt][4 * a] * inv, sm.o_acc[dt][4 * a + 1] * inv,
-                        sm.o_acc[dt][4 * a + 2] * inv, sm.o_acc[dt][4 * a + 3] * inv);
-    if (hk == 0) l_dst[(size_t)qpos * kQHeads + head] = l_tot > 0.f ? (sm.m + log2f(l_tot)) * kLn2 : kNegInf;
-  }
+      for (int v = 0; v < 16; ++v) sm.o_acc[dt][v] = 0.f;
+    sm.m = kMaxFloor;
+    sm.l = 0.f;
+    sm.alpha = 1.f;
+
+    wait_dma();
+    __syncthreads();
+    if (t0 + 1 < t1) issue_tile(ta, t0 + 1, next_page, zk_lds1, v_lds1);
+    next_page = tile_page(ta, t0 + 2);
+    floatx16_t s_a, s_b;
+    bf16x8_t p_prev[2], v_prev[8];
+    load_v(v_prev, v_lds2, off, 1);  // zeros: stands in for the V^T of block -1
+    {
+      bf16x8_t kf[8];
+      load_k(kf, zk_lds0, false, off, 0);
+      s_a = mma_scores(kf, qf);
+      const bf16x8_t zero = __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
+      p_prev[0] = zero;
+      p_prev[1] = zero;
+    }
+
+    // Tile kt lives in stage (kt - t0) % 3.  Step kt: first half = softmax of block 2kt beside the scores
+    // of block 2kt+1 and the O update of block 2kt-1, reading block 2kt's V^T; then wait for tile
+    // kt+1's DMA and barrier (everyone is done with tile kt-1's stage), start tile kt+2's DMA into
+    // that stage; second half = softmax of block 2kt+1 beside the scores of block 2kt+2 (next
+    // stage) and the O update of block 2kt, reading block 2kt+1's V^T.  Main loop: three steps per
+    // trip with compile-time stages, no causal mask, never the last tile.  Then the remaining
+    // steps with run-time stages (masked) and the last tile, then block 2n-1's O update.
+#define MTD_PREFILL_STEP(KT, CUR_K, CUR_V, PRV_V, NXT_K, PRV_K, MASK)       \
+    {                                                                       \
+      pipe_step<MASK, true>(sm, s_a, s_b, p_prev, v_prev, qf,               \
+                            CUR_K, +(CUR_K) != +zk_lds0, 1, CUR_V, 0, off,  \
+                            (KT) * kBK, hk, qabs, scale_log2);              \
+      wait_dma();                                                           \
+      tile_barrier();                                                       \
+      if ((KT) + 2 < t1) issue_tile(ta, (KT) + 2, next_page, PRV_K, PRV_V); \
+      next_page = tile_page(ta, (KT) + 3);                                  \
+      pipe_step<MASK, true>(sm, s_b, s_a, p_prev, v_prev, qf,               \
+                            NXT_K, +(NXT_K) != +zk_lds0, 0, CUR_V, 1, off,  \
+                            (KT) * kBK + 32, hk, qabs, scale_log2);         \
+    }
+    const int n_main = min(n_plain, t1 - 1);
+    int kt = t0;
+    for (; kt + 3 <= n_main; kt += 3) {
+      MTD_PREFILL_STEP(kt, zk_lds0, v_lds0, v_lds2, zk_lds1, zk_lds2, false)
+      MTD_PREFILL_STEP(kt + 1, zk_lds1, v_lds1, v_lds0, zk_lds2, zk_lds0, false)
+      MTD_PREFILL_STEP(kt + 2, zk_lds2, v_lds2, v_lds1, zk_lds0, zk_lds1, false)
+    }
+    for (; kt < t1 - 1; ++kt) {
+      const int sc = (kt - t0) % 3;
+      uint8_t* ck = sc == 0 ? zk_lds0 : sc == 1 ? zk_lds1 : zk_lds2;
+      uint8_t* cv = sc == 0 ? v_lds0 : sc == 1 ? v_lds1 : v_lds2;
+      uint8_t* nk = sc == 0 ? zk_lds1 : sc == 1 ? zk_lds2 : zk_lds0;
+      uint8_t* pk = sc == 0 ? zk_lds2 : sc == 1 ? zk_lds0 : zk_lds1;
+      uint8_t* pv = sc == 0 ? v_lds2 : sc == 1 ? v_lds0 : v_lds1;
+      MTD_PREFILL_STEP(kt, ck, cv, pv, nk, pk, true)
+    }
+#undef MTD_PREFILL_STEP
+    {
+      const int sc = (kt - t0) % 3;
+      const uint8_t* ck = sc == 0 ? zk_lds0 : sc == 1 ? zk_lds1 : zk_lds2;
+      const uint8_t* cv = sc == 0 ? v_lds0 : sc == 1 ? v_lds1 : v_lds2;
+      pipe_step<true, true>(sm, s_a, s_b, p_prev, v_prev, qf, ck, ck != zk_lds0, 1, cv, 0, off, kt * kBK, hk, qabs,
+                            scale_log2);
+      pipe_step<true, false>(sm, s_b, s_a, p_prev, v_prev, qf, ck, ck != zk_lds0, 0, cv, 1, off, kt * kBK + 32, hk,
+                             qabs, scale_log2);
+      if (__any(sm.alpha != 1.f)) {
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) sm.o_acc[dt][v] *= sm.alpha;
+      }
+      mma_pv(sm.o_acc, v_prev, p_prev);
+    }
+
+    // A second half can hold no key a row may see (early rows of a short item): its partial is then
+    // O = 0 with LSE = -inf, which the merge weighs by exactly zero.
+    const float l_tot = sum_xor32(sm.l);
+    if (qvalid) {
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      float* const o_dst = half ? part_o : out;
+      float* const l_dst = half ? part_lse : lse;
+      float* orow = o_dst + ((size_t)qpos * kQHeads + head) * kHeadDim;
+      // Accumulator element v of tile dt is dim 32dt + 8(v/4) + 4hk + v%4.
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+          *reinterpret_cast<float4*>(orow + 32 * dt + 8 * a + 4 * hk) =
+              make_float4(sm.o_acc[dt][4 * a] * inv, sm.o_acc[dt][4 * a + 1] * inv,
+                          sm.o_acc[dt][4 * a + 2] * inv, sm.o_acc[dt][4 * a + 3] * inv);
+      if (hk == 0) l_dst[(size_t)qpos * kQHeads + head] = l_tot > 0.f ? (sm.m + log2f(l_tot)) * kLn2 : kNegInf;
+    }
   }  // segments
 }
 
