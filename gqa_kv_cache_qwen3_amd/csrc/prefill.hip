@@ -17,8 +17,9 @@
 // afterwards by prefill_merge_kernel.
 //
 // K/V staging.  A 64-key tile is one page of the KV head: 16 KiB of K and 16 KiB of V, each
-// brought into LDS by 16-byte direct-to-LDS loads (global_load_lds_dwordx4, no registers, no
-// VALU) into one of three stages: the tile being computed, the next one in flight, and the one
+// brought into LDS by 16-byte direct-to-LDS buffer loads (buffer_load_dwordx4 ... lds: the page's
+// address in a scalar resource descriptor, a 32-bit offset per lane, no registers, no VALU) into
+// one of three stages: the tile being computed, the next one in flight, and the one
 // the DMA after that will overwrite.  In LDS a tile is four column groups of 64 bytes (dims
 // 32j .. 32j+31) of 64 rows each: 16-byte slot of (row r, chunk c) = 256 (c/4) + 4 r +
 // ((c%4) ^ g(r)), g(r) = (r/4)%4 for K and 0 for V.  That layout makes both read patterns free
