@@ -1,10 +1,11 @@
-"""Needle probes on the GPU: one key per KV head is aligned with that group's queries so that its
-logit exceeds every other by about 40 (natural-log units).  Every other weight is then below
+"""Structural probes on the GPU.  Needle probes: one key per KV head is aligned with that group's
+queries so that its logit exceeds every other by about 40 (natural-log units).  Every other weight is then below
 e^-40 (about 1e-12 summed over 131,072 keys), the needle's weight is exactly 1, and the output is
 that key's V up to fp32 rounding.  Needles sit at the first key, on both sides of a page boundary
 (slots 63 and 64), at the last key, and, in a prefill chunk, at the last prefix key, the chunk's
 first key and inside the chunk; rows before a needle's position must not see it (causality).  Each
-call is also held to the oracle's gate on the same bits.
+call is also held to the oracle's gate on the same bits.  Position-coded probe: identical keys and
+index-coded values make every prefill row's output a closed-form mean.
 """
 
 import numpy as np
@@ -105,3 +106,47 @@ def test_prefill_needles_and_causality(prefix, chunk, split):
     qb = bits(q)
     o_ref, l_ref = oracle.attention(oracle.bf16_to_f64(qb[rows]), k, v, prefix + np.asarray(rows), W.SCALE)
     compare(out[rows], lse[rows], o_ref, l_ref, f"prefill needles P={prefix} C={chunk}{' split' if split else ''}")
+
+
+@pytest.mark.parametrize("split", [False, True], ids=["one-pass", "pairs"])
+def test_prefill_position_coded_probe(split):
+    """All keys of a KV head identical, so every row's softmax is uniform over the keys it may see;
+    V carries the token index in exact bf16 integers.  Row i then outputs the mean of those integers
+    over keys 0 .. P + i (closed form; the integer sums stay below 2^24, exact in fp32) and
+    LSE - s = ln(P + i + 1).  A key missed or seen past the diagonal shifts the mean by about 1/n."""
+    prefix, chunk = 28500, 4096
+    total = prefix + chunk
+    tables, n_pages, _ = W.place_pages([total], 33, 0)
+    table = tables[0]
+    kp = torch.empty((n_pages, W.HKV, W.PAGE, W.HEAD_DIM), dtype=torch.bfloat16, device="cuda")
+    vp = torch.empty_like(kp)
+    kp.view(torch.int16).fill_(0x7FC0)
+    vp.view(torch.int16).fill_(0x7FC0)
+    key = W.normal_bf16((W.HKV, W.HEAD_DIM), 34, "cuda")
+    j = torch.arange(total, device="cuda")
+    pages = torch.as_tensor(table.astype(np.int64), device="cuda")[j // W.PAGE]
+    vals = torch.zeros((total, W.HKV, W.HEAD_DIM), dtype=torch.float32, device="cuda")
+    vals[:, :, 0] = (j % 64).float()[:, None]
+    vals[:, :, 1] = ((j >> 6) % 256).float()[:, None]
+    vals[:, :, 2] = (j >> 14).float()[:, None]
+    kp[pages, :, j % W.PAGE, :] = key
+    vp[pages, :, j % W.PAGE, :] = vals.to(torch.bfloat16)
+    q = W.normal_bf16((chunk, W.HQ, W.HEAD_DIM), 35, "cuda")
+    ws = torch.empty(mtd.prefill_workspace_bytes(chunk), dtype=torch.uint8, device="cuda") if split else None
+    log(f"prefill position-coded probe P={prefix} C={chunk} split={split}")
+    out, lse = mtd.mtd_attn_prefill_chunk(kp, vp, q, prefix, torch.as_tensor(table.astype(np.int32), device="cuda"),
+                                          W.SCALE, workspace=ws)
+    torch.cuda.synchronize()
+    o = out.double().cpu().numpy()
+    lse = lse.double().cpu().numpy()
+    n = prefix + np.arange(chunk) + 1  # keys row i sees
+    # closed-form means of the three codes over keys 0 .. n-1
+    jj = np.arange(total)
+    means = [np.cumsum(jj % 64)[n - 1] / n, np.cumsum((jj >> 6) % 256)[n - 1] / n, np.cumsum(jj >> 14)[n - 1] / n]
+    s = W.SCALE * np.einsum("chd,hd->ch", q.double().cpu().numpy(),
+                            np.repeat(key.double().cpu().numpy(), W.HQ // W.HKV, axis=0))
+    assert np.abs(lse - (s + np.log(n)[:, None])).max() < 1e-4
+    for c in range(3):
+        err = np.abs(o[:, :, c] - means[c][:, None]) / np.maximum(1.0, means[c][:, None])
+        assert err.max() < 1e-6, (c, float(err.max()))
+    assert np.abs(o[:, :, 3:]).max() == 0.0
