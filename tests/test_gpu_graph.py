@@ -1,5 +1,5 @@
 """The library's calls captured in a HIP graph (torch.cuda.CUDAGraph, on the capture stream torch
-makes current) and replayed.
+makes current) and replayed: decode steps over several layers, and a whole chunked prompt.
 
 Every replay must reproduce the same calls made eagerly on a twin pool bit for bit, with eager
 work (the copies that stage each step's inputs) and synchronisations between replays; the last
@@ -180,3 +180,61 @@ def test_graph_attention_block_step():
         assert torch.equal(y_g, y_e), s
     for l in range(layers):
         assert torch.equal(kg[l], ke[l]) and torch.equal(vg[l], ve[l]), l
+
+
+def test_chunked_prefill_graph_replays():
+    """A whole chunked prompt in one graph: for each chunk, append its K/V, then prefill it with a
+    workspace (4096-token chunks on the pair schedule, the ragged last chunk as halves).  Three
+    replays, with eager work between them, each equal the eager calls bit for bit (outputs and
+    pools); the last chunk is also checked against the oracle on sampled rows."""
+    chunks = [4096, 4096, 1500]
+    starts = np.concatenate([[0], np.cumsum(chunks)[:-1]]).astype(np.int64)
+    total = int(sum(chunks))
+    tables, n_pages, _ = W.place_pages([total], 57, 0)
+    bt = torch.as_tensor(tables, device="cuda")
+    kg, vg = new_pool(n_pages, "cuda"), new_pool(n_pages, "cuda")  # NaN-poisoned
+    ke, ve = kg.clone(), vg.clone()
+    k_log = W.normal_bf16((total, W.HKV, W.HEAD_DIM), W.torch_seed(57, 1), "cuda")
+    v_log = W.normal_bf16((total, W.HKV, W.HEAD_DIM), W.torch_seed(57, 2), "cuda")
+    q_log = W.normal_bf16((total, W.HQ, W.HEAD_DIM), W.torch_seed(57, 3), "cuda")
+    ws = torch.empty(mtd.prefill_workspace_bytes(max(chunks)), dtype=torch.uint8, device="cuda")
+    ws_e = torch.empty_like(ws)
+    cus = [_i32([0, c]) for c in chunks]
+    sps = [_i32([s]) for s in starts]
+    outs = [torch.empty((c, W.HQ, W.HEAD_DIM), dtype=torch.float32, device="cuda") for c in chunks]
+    lses = [torch.empty((c, W.HQ), dtype=torch.float32, device="cuda") for c in chunks]
+
+    def calls(kp, vp, work, o_list, l_list):
+        for c, s, cu, sp, o, l in zip(chunks, starts, cus, sps, o_list, l_list):
+            lo, hi = int(s), int(s) + c
+            mtd.mtd_kv_append(kp, vp, k_log[lo:hi], v_log[lo:hi], cu, sp, bt)
+            mtd.mtd_attn_prefill_chunk(kp, vp, q_log[lo:hi], lo, bt[0], W.SCALE, out=o, lse=l, workspace=work)
+
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        calls(kg, vg, ws, outs, lses)
+    torch.cuda.synchronize()
+    log("prefill graph: eager twin")
+    oe = [torch.empty_like(o) for o in outs]
+    le = [torch.empty_like(l) for l in lses]
+    calls(ke, ve, ws_e, oe, le)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for o, l in zip(outs, lses):
+            o.fill_(float("nan"))
+            l.fill_(float("nan"))
+        log(f"prefill graph: replay {rep}")
+        graph.replay()
+        torch.cuda.synchronize()
+        for i in range(len(chunks)):
+            assert torch.equal(outs[i], oe[i]) and torch.equal(lses[i], le[i]), (rep, i)
+        assert torch.equal(kg.view(torch.int16), ke.view(torch.int16))
+        assert torch.equal(vg.view(torch.int16), ve.view(torch.int16))
+    c, s = chunks[-1], int(starts[-1])
+    rows = np.unique(np.linspace(0, c - 1, 24).astype(np.int64))
+    kc, vc, ident = request_pages_host(kg, vg, tables[0], total)
+    k = oracle.gather_logical(kc, ident, total)
+    v = oracle.gather_logical(vc, ident, total)
+    o_ref, l_ref = oracle.attention(oracle.bf16_to_f64(bits(q_log[s:s + c])[rows]), k, v, s + rows, W.SCALE)
+    compare(outs[-1][rows], lses[-1][rows], o_ref, l_ref, "prefill graph: last chunk")
