@@ -214,7 +214,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
     ll += __shfl_xor(ll, 8, 64);
     ll += __shfl_xor(ll, 16, 64);
     ll += __shfl_xor(ll, 32, 64);
-    const float inv = 1.f / ll;
+    const float inv = ll > 0.f ? 1.f / ll : 0.f;  // a split with no key (its pages out of the pool): O = 0
     float* orow = part_o + ((size_t)f * kQHeads + kGroup * g + hh) * kHeadDim;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
@@ -296,6 +296,11 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
   if (lane == 0) s_wave[wave] = mx;
   __syncthreads();
   mx = fmaxf(fmaxf(s_wave[0], s_wave[1]), fmaxf(s_wave[2], s_wave[3]));
+  if (mx == kNegInf) {  // no part holds a key (every page out of the pool): as for no keys at all
+    if (tid < kHeadDim) orow[tid] = 0.f;
+    if (tid == 0) lse_out[(size_t)b * kQHeads + h] = kNegInf;
+    return;
+  }
   __syncthreads();
   // weights and their sum
   float ws = 0.f;

@@ -51,8 +51,9 @@
  *   check returns a negative MTD_ERR_* code, enqueues nothing and leaves all memory untouched.
  *   Values that live on the device (table entries, lengths, offsets) are trusted: if they are
  *   inconsistent with the sizes given on the host the results are unspecified, but no kernel reads
- *   or writes outside the pools, the inputs and the outputs (page ids outside [0, num_pages) are
- *   skipped).  A failed kernel launch returns MTD_ERR_HIP; mtd_last_error() gives the detail.
+ *   or writes outside the pools, the inputs and the outputs: page ids outside [0, num_pages) are
+ *   skipped by mtd_kv_append and mtd_attn_decode and read as page 0 by mtd_attn_prefill_chunk.
+ *   A failed kernel launch returns MTD_ERR_HIP; mtd_last_error() gives the detail.
  */
 #ifndef MTD_H
 #define MTD_H
