@@ -32,11 +32,16 @@ int hip_status(hipError_t err, const char* what) {
   return fail(MTD_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
 }
 
+// The kernels move 16-byte vectors through every pool, token, output and workspace array.
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
 // Checks shared by all calls on the layer description.
 int check_layer(const mtd_kv_layer_t* kv) {
   if (kv == nullptr) return fail(MTD_ERR_INVALID_ARG, "kv is NULL");
   if (kv->k_pages == nullptr || kv->v_pages == nullptr)
     return fail(MTD_ERR_INVALID_ARG, "kv->k_pages / kv->v_pages is NULL");
+  if (!aligned16(kv->k_pages) || !aligned16(kv->v_pages))
+    return fail(MTD_ERR_INVALID_ARG, "kv->k_pages / kv->v_pages not 16-byte aligned");
   if (kv->num_pages <= 0) return fail(MTD_ERR_INVALID_ARG, "kv->num_pages = %d", kv->num_pages);
   if (kv->page_size != mtd::kPage)
     return fail(MTD_ERR_UNSUPPORTED, "page_size %d (supported: %d)", kv->page_size, mtd::kPage);
@@ -78,8 +83,6 @@ int check_proj_shape(int32_t n_tok, int32_t hidden, int32_t num_q_heads, int32_t
   return MTD_OK;
 }
 
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-
 mtd::KvPools pools(const mtd_kv_layer_t* kv) {
   return mtd::KvPools{static_cast<uint16_t*>(kv->k_pages), static_cast<uint16_t*>(kv->v_pages),
                       kv->num_pages};
@@ -99,6 +102,8 @@ int mtd_kv_append(const mtd_kv_layer_t* kv, const void* k_new, const void* v_new
   if (bt_stride <= 0) return fail(MTD_ERR_INVALID_ARG, "bt_stride = %d", bt_stride);
   if (n_new > 0 && (k_new == nullptr || v_new == nullptr))
     return fail(MTD_ERR_INVALID_ARG, "k_new / v_new is NULL");
+  if (!aligned16(k_new) || !aligned16(v_new))
+    return fail(MTD_ERR_INVALID_ARG, "k_new / v_new not 16-byte aligned");
   if (cu_new == nullptr || start_pos == nullptr || block_tables == nullptr)
     return fail(MTD_ERR_INVALID_ARG, "cu_new / start_pos / block_tables is NULL");
   if (n_new == 0) return ok();
@@ -119,6 +124,8 @@ int mtd_attn_prefill_chunk(const mtd_kv_layer_t* kv, const void* q, int32_t chun
   if ((st = check_scale(scale)) != MTD_OK) return st;
   if (q == nullptr || block_table == nullptr || out == nullptr || lse == nullptr)
     return fail(MTD_ERR_INVALID_ARG, "q / block_table / out / lse is NULL");
+  if (!aligned16(q) || !aligned16(out) || !aligned16(workspace))
+    return fail(MTD_ERR_INVALID_ARG, "q / out / workspace not 16-byte aligned");
   if (chunk_len <= 0) return fail(MTD_ERR_INVALID_ARG, "chunk_len = %d", chunk_len);
   if (prefix_len < 0) return fail(MTD_ERR_INVALID_ARG, "prefix_len = %d", prefix_len);
   const int64_t total = (int64_t)prefix_len + chunk_len;
@@ -162,6 +169,8 @@ int mtd_attn_decode(const mtd_kv_layer_t* kv, const void* q, const int32_t* kv_l
   if ((st = check_scale(scale)) != MTD_OK) return st;
   if (q == nullptr || kv_lens == nullptr || block_tables == nullptr || out == nullptr || lse == nullptr)
     return fail(MTD_ERR_INVALID_ARG, "q / kv_lens / block_tables / out / lse is NULL");
+  if (!aligned16(q) || !aligned16(out) || !aligned16(workspace))
+    return fail(MTD_ERR_INVALID_ARG, "q / out / workspace not 16-byte aligned");
   if (batch <= 0) return fail(MTD_ERR_INVALID_ARG, "batch = %d", batch);
   if (max_kv_len <= 0) return fail(MTD_ERR_INVALID_ARG, "max_kv_len = %d", max_kv_len);
   if (max_kv_len > MTD_MAX_CONTEXT)

@@ -541,15 +541,16 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
 }
 
 // Combines the two parts of every split item: out/lse hold one part's normalised partial,
-// part_o/part_lse the other's.  One wavefront per (position, head) row; each lane takes 2 dims.
-// Both LSEs are read before lane 0 overwrites lse, in program order within the wave.
+// part_o/part_lse the other's.  Rows (position, head) from row0 on; each half-wavefront takes one
+// row, 4 dims per lane.  Both LSEs are read before the row's first lane overwrites lse, in program
+// order within the wave.
 __global__ __launch_bounds__(256) void prefill_merge_kernel(float* __restrict__ out, float* __restrict__ lse,
                                                             const float* __restrict__ part_o,
                                                             const float* __restrict__ part_lse,
                                                             int chunk_len, int prefix_len, int n_qtiles,
-                                                            int mode) {
-  const int row = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);  // (position, head)
-  const int lane = threadIdx.x & 63;
+                                                            int mode, int row0) {
+  const int row = row0 + (int)blockIdx.x * 8 + (int)(threadIdx.x >> 5);  // (position, head)
+  const int lane = threadIdx.x & 31;
   if (row >= chunk_len * kQHeads) return;
   const int qt = row / kQHeads / kBQ;
   if (mode == kPairs) {
@@ -564,10 +565,11 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(float* __restrict__ 
   const float mx = fmaxf(l0, l1);
   const float w0 = __expf(l0 - mx), w1 = __expf(l1 - mx);
   const float inv = 1.f / (w0 + w1);
-  float2* o = reinterpret_cast<float2*>(out + (size_t)row * kHeadDim) + lane;
-  const float2 a = *o;
-  const float2 b = reinterpret_cast<const float2*>(part_o + (size_t)row * kHeadDim)[lane];
-  *o = make_float2((w0 * a.x + w1 * b.x) * inv, (w0 * a.y + w1 * b.y) * inv);
+  float4* o = reinterpret_cast<float4*>(out + (size_t)row * kHeadDim) + lane;
+  const float4 a = *o;
+  const float4 b = reinterpret_cast<const float4*>(part_o + (size_t)row * kHeadDim)[lane];
+  *o = make_float4((w0 * a.x + w1 * b.x) * inv, (w0 * a.y + w1 * b.y) * inv, (w0 * a.z + w1 * b.z) * inv,
+                   (w0 * a.w + w1 * b.w) * inv);
   if (lane == 0) lse[row] = mx + __logf(w0 + w1);
 }
 
@@ -613,9 +615,11 @@ hipError_t launch_prefill(const KvPools& kv, const uint16_t* q, int chunk_len, i
       part_o, part_lse, n_qtiles, mode);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || mode == kOnePass) return err;
+  // Only long tiles are split on the pair schedule: they start at tile T/2.
   const int rows = chunk_len * kQHeads;
-  prefill_merge_kernel<<<dim3((rows + 3) / 4), dim3(256), 0, stream>>>(out, lse, part_o, part_lse,
-                                                                      chunk_len, prefix_len, n_qtiles, mode);
+  const int row0 = mode == kPairs ? (n_qtiles / 2) * kBQ * kQHeads : 0;
+  prefill_merge_kernel<<<dim3((rows - row0 + 7) / 8), dim3(256), 0, stream>>>(
+      out, lse, part_o, part_lse, chunk_len, prefix_len, n_qtiles, mode, row0);
   return hipGetLastError();
 }
 

@@ -45,6 +45,9 @@
  *   Logical token p of a request is stored at page block_table[p / page_size], slot p % page_size.
  * Block tables.  int32 [n][bt_stride], row r lists request r's physical page ids in logical order.
  *   Entries a call does not need are never read.
+ * Alignment.  The pools, the query, key and value rows, the float32 outputs O and every workspace
+ *   must be 16-byte aligned (the kernels move 16-byte vectors); else MTD_ERR_INVALID_ARG.  LSE
+ *   arrays and int32 arrays need only their natural alignment.
  * Supported shape (this version).  num_q_heads = 16, num_kv_heads = 8, head_dim = 128,
  *   page_size = 64; anything else returns MTD_ERR_UNSUPPORTED.
  * Errors.  Every argument that lives on the host is checked before any work is enqueued; a failed

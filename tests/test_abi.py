@@ -113,6 +113,26 @@ def test_layer_validation(lib, kw, code):
     assert lib.mtd_last_error().decode() != ""
 
 
+MIS = FAKE + 4  # non-null, 4-byte aligned, not 16-byte aligned
+
+
+def test_alignment_validation(lib):
+    """Pools, token rows, O and workspaces must be 16-byte aligned (checked before any launch)."""
+    for kw in (dict(k_pages=MIS), dict(v_pages=MIS)):
+        kv = layer(**kw)
+        assert append(lib, kv) == mtd.MTD_ERR_INVALID_ARG
+        assert prefill(lib, kv) == mtd.MTD_ERR_INVALID_ARG
+        assert decode(lib, kv) == mtd.MTD_ERR_INVALID_ARG
+    for kw in (dict(k_new=MIS), dict(v_new=MIS)):
+        assert append(lib, layer(), **kw) == mtd.MTD_ERR_INVALID_ARG
+    ws = lib.mtd_attn_prefill_workspace_bytes(10, 16, 128)
+    for kw in (dict(q=MIS), dict(out=MIS), dict(ws=MIS, ws_bytes=ws)):
+        assert prefill(lib, layer(), **kw) == mtd.MTD_ERR_INVALID_ARG
+    for kw in (dict(q=MIS), dict(out=MIS), dict(ws=MIS)):
+        assert decode(lib, layer(), **kw) == mtd.MTD_ERR_INVALID_ARG
+    assert "16-byte" in lib.mtd_last_error().decode()
+
+
 def test_null_layer(lib):
     assert append(lib, None) == mtd.MTD_ERR_INVALID_ARG
     assert prefill(lib, None) == mtd.MTD_ERR_INVALID_ARG
