@@ -226,57 +226,39 @@ class MixedStep:
         return {"kernel": "decode_split_kernel+decode_merge_kernel", "bound": "hbm", "achieved": res["decode"]["value"],
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "per_launch": res["decode"]["bytes"], "ms": res["decode"]["ms"]}
 
-    # ---- CPU baseline: the fp64 oracle on a bounded sample of the same step ----
-    def cpu_baseline(self, budget_s=20.0):
+    # ---- CPU baseline: the fp64 oracle on the same step ----
+    def cpu_baseline(self):
+        """The fp64 oracle on this step's whole input: all 4096 prefill rows and all 31 decode
+        requests, over a process pool (one BLAS thread per worker) on the host's cores.  Timed:
+        the oracle's compute only (page walk included); copying the pool to the host and staging
+        it for the workers are not."""
         import torch
-        import oracle
-        rows_total = 0
-        t_pre = t_dec = 0.0
-        pre_flops = dec_bytes = 0.0
+        from oracle.parallel import OraclePool, cpu_model, decode_problem, prefill_problem
         torch.cuda.synchronize()
         host = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-
-        def pages_of(table_row, n):
-            used = (n + W.PAGE - 1) // W.PAGE
-            idx = torch.as_tensor(np.asarray(table_row[:used].cpu().numpy(), dtype=np.int64), device=self.k.device)
-            return host(self.k.index_select(0, idx)), host(self.v.index_select(0, idx)), np.arange(used)
-
-        # decode sample: requests in seeded order until half the budget is used
-        order = W.rng(4, 77).permutation(len(self.lens))
-        qd = host(self.q_d)
-        n_dec = 0
-        for b in order:
-            n = int(self.lens[b])
-            kc, vc, ident = pages_of(self.bt_dec[b], n)
+        kb, vb = host(self.k), host(self.v)
+        tables = self.bt_all.cpu().numpy()
+        qa, qd = host(self.q_a), host(self.q_d)
+        with OraclePool() as pool:
+            staged = pool.stage([prefill_problem(qa, kb, vb, tables[0], self.prefix)])
             t0 = time.perf_counter()
-            oracle.decode(qd[b:b + 1], kc, vc, [n], [ident], W.SCALE)
-            t_dec += time.perf_counter() - t0
-            dec_bytes += KV_BYTES_PER_TOKEN * n
-            n_dec += 1
-            if t_dec > budget_s / 2:
-                break
-        # prefill sample: blocks of 64 chunk rows, seeded order
-        total = self.prefix + self.chunk
-        kc, vc, ident = pages_of(self.bt_a, total)
-        qa = host(self.q_a)
-        blocks = W.rng(4, 78).permutation(self.chunk // 64)
-        for blk in blocks:
-            rows = np.arange(64 * blk, 64 * blk + 64)
+            pool.run(staged, W.SCALE)
+            t_pre = time.perf_counter() - t0
+            staged = pool.stage([decode_problem(qd[b:b + 1], kb, vb, tables[1 + b], int(self.lens[b]))
+                                 for b in range(len(self.lens))])
             t0 = time.perf_counter()
-            k = oracle.gather_logical(kc, ident, int(self.prefix + rows.max() + 1))
-            v = oracle.gather_logical(vc, ident, int(self.prefix + rows.max() + 1))
-            oracle.attention(oracle.bf16_to_f64(qa[rows]), k, v, self.prefix + rows, W.SCALE)
-            t_pre += time.perf_counter() - t0
-            pre_flops += 4.0 * W.HQ * W.HEAD_DIM * float((self.prefix + rows + 1).sum())
-            rows_total += 64
-            if t_pre > budget_s / 2:
-                break
+            pool.run(staged, W.SCALE)
+            t_dec = time.perf_counter() - t0
+            workers = pool.workers
+        dec_bytes = KV_BYTES_PER_TOKEN * float(self.lens.sum())
         return {
             "value": dec_bytes / t_dec / 1e9, "unit": "GB/s",
-            "prefill_tflops": pre_flops / t_pre / 1e12,
-            "cores": blas_threads(), "kind": "oracle",
-            "sample": f"decode of {n_dec} of the 31 requests ({int(dec_bytes / KV_BYTES_PER_TOKEN)} KV tokens, "
-                      f"{t_dec:.1f} s) + {rows_total} of the 4096 prefill rows ({t_pre:.1f} s); fp64 numpy",
+            "prefill_tflops": self.work["prefill_flops"] / t_pre / 1e12,
+            "cores": workers, "affinity_cores": len(os.sched_getaffinity(0)), "cpu_model": cpu_model(),
+            "kind": "oracle",
+            "sample": (f"the whole step: decode of all {len(self.lens)} requests ({int(self.lens.sum())} KV tokens, "
+                       f"{t_dec:.1f} s) and all {self.chunk} prefill rows ({t_pre:.1f} s); fp64 numpy in {workers} "
+                       "worker processes with one BLAS thread each"),
         }
 
 
@@ -542,31 +524,36 @@ class FullDepth:
         return {"kernel": "decode_split_kernel+decode_merge_kernel", "bound": "hbm", "achieved": res["decode"]["value"],
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "per_launch": res["decode"]["bytes"], "ms": res["decode"]["ms"]}
 
-    def cpu_baseline(self, budget_s=20.0):
+    def cpu_baseline(self):
+        """The fp64 oracle on 16 of the 64 requests (seeded choice) of the layer-0 decode call of the
+        last timed step, over a process pool with one BLAS thread per worker; the oracle's compute
+        only is timed (the requests' pages are copied to the host and staged beforehand)."""
         import torch
-        import oracle
+        from oracle.parallel import OraclePool, cpu_model, decode_problem
         torch.cuda.synchronize()
         host = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-        # sample: requests of the layer-0 call of the last timed step, seeded order, within budget
         s = (self.step_idx - 1) % self.steps
         kp, vp = self.inp["k_pools"][0], self.inp["v_pools"][0]
         q = host(self.inp["q"][s, 0])
-        t_dec, nbytes, n_req = 0.0, 0.0, 0
-        for b in W.rng(5, 77).permutation(len(self.lens0)):
-            n = int(self.lens0[b]) + s + 1
-            used = (n + W.PAGE - 1) // W.PAGE
+        lens = self.lens0 + s + 1
+        sample = np.sort(W.rng(5, 77).permutation(len(lens))[:16])
+        probs = []
+        for b in sample:
+            used = (int(lens[b]) + W.PAGE - 1) // W.PAGE
             idx = torch.as_tensor(self.inp["tables"][b][:used].astype(np.int64), device=kp.device)
-            kc, vc = host(kp.index_select(0, idx)), host(vp.index_select(0, idx))
+            probs.append(decode_problem(q[b:b + 1], host(kp.index_select(0, idx)), host(vp.index_select(0, idx)),
+                                        np.arange(used), int(lens[b])))
+        with OraclePool() as pool:
+            staged = pool.stage(probs)
             t0 = time.perf_counter()
-            oracle.decode(q[b:b + 1], kc, vc, [n], [np.arange(used)], W.SCALE)
-            t_dec += time.perf_counter() - t0
-            nbytes += KV_BYTES_PER_TOKEN * n
-            n_req += 1
-            if t_dec > budget_s:
-                break
-        return {"value": nbytes / t_dec / 1e9, "unit": "GB/s", "cores": blas_threads(), "kind": "oracle",
-                "sample": f"decode of {n_req} of the 64 requests of one layer call ({int(nbytes / KV_BYTES_PER_TOKEN)} "
-                          f"KV tokens, {t_dec:.1f} s); fp64 numpy"}
+            pool.run(staged, W.SCALE)
+            t_dec = time.perf_counter() - t0
+            workers = pool.workers
+        n_tok = int(lens[sample].sum())
+        return {"value": KV_BYTES_PER_TOKEN * n_tok / t_dec / 1e9, "unit": "GB/s", "cores": workers,
+                "affinity_cores": len(os.sched_getaffinity(0)), "cpu_model": cpu_model(), "kind": "oracle",
+                "sample": f"16 of the 64 requests of one layer's decode call ({n_tok} KV tokens, {t_dec:.1f} s); "
+                          f"fp64 numpy in {workers} worker processes with one BLAS thread each"}
 
 
 def proj_work(n_tok: int):
@@ -942,15 +929,6 @@ WORKLOAD_CLASSES = {c.name: c for c in (MixedStep, MixedStepOverlap, MixedBlock,
                                          FullDepth, FullDepthBlock, DecodeGraph, DecodeGraphBlock)}
 
 
-def blas_threads() -> int:
-    try:
-        from threadpoolctl import threadpool_info
-        n = [d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"]
-        return int(max(n)) if n else 1
-    except Exception:
-        return 1
-
-
 def calibrate_copy():
     """A plain copy kernel of known size: 1 GiB read + 1 GiB written per launch, 5 launches."""
     import torch
@@ -979,7 +957,6 @@ def main():
                     help="untimed steps (default: enough for ~50 ms of GPU work, past the clock ramp)")
     ap.add_argument("--workload", default="mixed_step", choices=sorted(WORKLOAD_CLASSES))
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing on the host")
-    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB elementwise copy 5 times (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -1082,7 +1059,7 @@ def main():
         line["proj"] = {name: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in d.items()}
                         for name, d in res["proj"].items()}
     if not args.no_cpu_baseline and getattr(wl, "cpu_baseline", None) is not None:
-        line["cpu_baseline"] = wl.cpu_baseline(args.cpu_budget)
+        line["cpu_baseline"] = wl.cpu_baseline()
     print(json.dumps(line), flush=True)
 
 

@@ -89,6 +89,42 @@ def compare(o_gpu: torch.Tensor, lse_gpu: torch.Tensor, o_ref: np.ndarray, lse_r
     return err_o, err_l
 
 
+def host_pool_of(pool: torch.Tensor) -> np.ndarray:
+    """The whole pool as host bf16 bits (for the oracle, which reads the exact bits on the device)."""
+    return bits(pool)
+
+
+class MixedInputs:
+    """The mixed scheduler step's inputs on one shared pool of 64-token pages: a chunk of request
+    A (C tokens at prefix P) and one new token for each decode request, appended in one call;
+    request A first in the block table, then the decode requests.  ``lens`` are the decode
+    requests' lengths including the appended token.  The same tag gives the same bits."""
+
+    def __init__(self, prefix: int, chunk: int, lens, tag: int, device="cuda"):
+        self.prefix, self.chunk = prefix, chunk
+        self.lens = np.asarray(lens, dtype=np.int64)
+        final = np.concatenate([[prefix + chunk], self.lens])
+        self.tables, self.num_pages, _ = W.place_pages(final, tag, 0)
+        self.k = torch.empty((self.num_pages, W.HKV, W.PAGE, W.HEAD_DIM), dtype=torch.bfloat16, device=device)
+        self.v = torch.empty_like(self.k)
+        fill_normal_(self.k, W.torch_seed(tag, 1))
+        fill_normal_(self.v, W.torch_seed(tag, 2))
+        n_new = chunk + len(self.lens)
+        self.k_new = W.normal_bf16((n_new, W.HKV, W.HEAD_DIM), W.torch_seed(tag, 3), device)
+        self.v_new = W.normal_bf16((n_new, W.HKV, W.HEAD_DIM), W.torch_seed(tag, 4), device)
+        self.q_a = W.normal_bf16((chunk, W.HQ, W.HEAD_DIM), W.torch_seed(tag, 5), device)
+        self.q_d = W.normal_bf16((len(self.lens), W.HQ, W.HEAD_DIM), W.torch_seed(tag, 6), device)
+        self.cu_np = np.concatenate([[0, chunk], chunk + np.arange(1, len(self.lens) + 1)]).astype(np.int32)
+        self.start_np = np.concatenate([[prefix], self.lens - 1]).astype(np.int32)
+        self.bt = torch.as_tensor(self.tables, device=device)
+        self.bt_a = self.bt[0].contiguous()
+        self.bt_dec = self.bt[1:].contiguous()
+        self.cu = torch.as_tensor(self.cu_np, device=device)
+        self.start = torch.as_tensor(self.start_np, device=device)
+        self.kv_lens = torch.as_tensor(self.lens.astype(np.int32), device=device)
+        self.max_len = int(self.lens.max())
+
+
 class DecodeBatch:
     """Decode-only pool: random K/V in every slot, unused slots poisoned, seeded placement."""
 

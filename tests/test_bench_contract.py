@@ -37,7 +37,7 @@ def test_every_workload_has_defaults():
 
 @pytest.mark.gpu
 def test_default_run_prints_one_contract_line():
-    res = subprocess.run([sys.executable, BENCH, "--steps", "3", "--warmup", "2", "--cpu-budget", "2"],
+    res = subprocess.run([sys.executable, BENCH, "--steps", "3", "--warmup", "2"],
                          capture_output=True, text=True, timeout=600, cwd=ROOT)
     assert res.returncode == 0, res.stderr[-2000:]
     lines = [l for l in res.stdout.splitlines() if l.strip()]
@@ -54,6 +54,6 @@ def test_default_run_prints_one_contract_line():
     assert 0 < r["frac"] < 1 and abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-3
     assert "traffic" in r
     c = d["cpu_baseline"]
-    for k in ("value", "unit", "cores", "kind", "sample"):
+    for k in ("value", "unit", "cores", "affinity_cores", "cpu_model", "kind", "sample", "prefill_tflops"):
         assert k in c, k
     assert c["kind"] == "oracle" and c["value"] > 0 and c["cores"] >= 1

@@ -1,9 +1,13 @@
 """mtd_attn_prefill_chunk on the GPU against the fp64 oracle: one-shot and chunked prefill over
-pages written by mtd_kv_append, at small ragged shapes in full and at the 90-minute and
-mixed-step sizes on sampled rows; plus chunked == one-shot and decode == 1-row prefill.  The
+pages written by mtd_kv_append, at small ragged shapes in full; the mixed step's 4096-token chunk
+and the 90-minute prompt's chunks 0, 8 and 16 on every row (the oracle spread over a process
+pool), its other chunks and the 128K-cap chunks on sampled rows; plus chunked == one-shot and
+decode == 1-row prefill.  The
 checks run both without a workspace (one pass per position tile) and with one (the causal work
 rebalanced over the compute units: tiles t and T-1-t paired into two equal workgroups, or each
 tile's keys in two halves for short chunks; split tiles merged by log-sum-exp)."""
+
+import hashlib
 
 import numpy as np
 import pytest
@@ -12,6 +16,7 @@ import torch
 import oracle
 import workloads as W
 from gpu_common import bits, compare, log, new_pool, request_pages_host
+from oracle.parallel import prefill_problem
 
 pytestmark = pytest.mark.gpu
 
@@ -141,10 +146,30 @@ def sample_rows(chunk: int, tag: int, n: int = 40) -> np.ndarray:
     return np.array(sorted({r for r in fixed + rnd if 0 <= r < chunk}))
 
 
+# Oracle results of full chunks, shared by the one-pass and split runs of the same inputs (keyed
+# by a digest of the exact bits the oracle read).
+_FULL_REF = {}
+
+
+def full_reference(pool, q_bits, kc, vc, table, prefix):
+    h = hashlib.blake2b(digest_size=16)
+    for a in (q_bits, kc, vc, np.asarray(table, dtype=np.int64)):
+        h.update(np.ascontiguousarray(a).view(np.uint8))
+    h.update(str(prefix).encode())
+    key = h.hexdigest()
+    if key not in _FULL_REF:
+        [_FULL_REF[key]] = pool.attention([prefill_problem(q_bits, kc, vc, table, prefix)], W.SCALE)
+    return _FULL_REF[key]
+
+
+P90_FULL_CHUNKS = (0, 8, 16)  # first chunk, the middle one (prefix 32,768) and the partial last one
+
+
 @SPLIT
-def test_prefill_90_minutes_chunked_sampled(split):
+def test_prefill_90_minutes_chunked(split, oracle_pool):
     """67,500 tokens in 17 chunks of 4096 (last 1,964), K with a rank-4 per-head component so the
-    softmax is peaked; every chunk is checked on sampled rows against the oracle."""
+    softmax is peaked.  Chunks 0, 8 and 16 are compared with the oracle on every row; the other 14
+    on 40 sampled rows each (first, last, tile edges and seeded random rows)."""
     p = W.PREFILL90.params
     total, chunk = p["total"], p["chunk"]
     req = Request(total, W.PREFILL90.tag, lowrank=True, split=split)
@@ -158,22 +183,27 @@ def test_prefill_90_minutes_chunked_sampled(split):
         c = min(chunk, total - start)
         log(f"prefill90 chunk {ci} prefix={start} len={c} split={split}")
         out, lse = req.prefill(start, c)
-        rows = sample_rows(c, ci)
-        o_ref, l_ref = oracle.attention(oracle.bf16_to_f64(qb[start + rows]), k, v, start + rows, W.SCALE)
-        compare(out[rows], lse[rows], o_ref, l_ref, f"prefill90 chunk {ci}{' split' if split else ''}")
+        if ci in P90_FULL_CHUNKS:
+            used = (start + c + W.PAGE - 1) // W.PAGE
+            o_ref, l_ref = full_reference(oracle_pool, qb[start:start + c], kc[:used], vc[:used], ident[:used], start)
+            compare(out, lse, o_ref, l_ref, f"prefill90 chunk {ci}, all {c} rows{' split' if split else ''}")
+        else:
+            rows = sample_rows(c, ci)
+            o_ref, l_ref = oracle.attention(oracle.bf16_to_f64(qb[start + rows]), k, v, start + rows, W.SCALE)
+            compare(out[rows], lse[rows], o_ref, l_ref, f"prefill90 chunk {ci}{' split' if split else ''}")
 
 
 @SPLIT
-def test_mixed_step_prefill_part_sampled(split):
-    """The mixed step's chunk: 4096 tokens of request A at prefix 32,768."""
+def test_mixed_step_prefill_part_all_rows(split, oracle_pool):
+    """The mixed step's chunk: 4096 tokens of request A at prefix 32,768, every row."""
     p = W.MIXED.params
     prefix, chunk = p["prefix"], p["chunk"]
     req = Request(prefix + chunk, W.MIXED.tag, split=split)
     log(f"mixed prefill part split={split}")
     out, lse = req.prefill(prefix, chunk)
-    rows = sample_rows(chunk, 99, 64)
-    o_ref, l_ref = req.reference(prefix, chunk, rows)
-    compare(out[rows], lse[rows], o_ref, l_ref, f"mixed prefill part{' split' if split else ''}")
+    kc, vc, ident = request_pages_host(req.k, req.v, req.table_np, prefix + chunk)
+    o_ref, l_ref = full_reference(oracle_pool, bits(req.q_log[prefix:prefix + chunk]), kc, vc, ident, prefix)
+    compare(out, lse, o_ref, l_ref, f"mixed prefill part, all rows{' split' if split else ''}")
 
 
 @SPLIT
