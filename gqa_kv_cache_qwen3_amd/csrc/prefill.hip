@@ -122,7 +122,7 @@ __device__ __forceinline__ int tile_page(const TileArgs& a, int kt) {
 
 __device__ __forceinline__ void issue_tile(const TileArgs& a, int kt, int page, uint8_t* k_lds,
                                            uint8_t* v_lds) {
-  if (page < 0 || page >= a.num_pages) page = 0;  // out-of-pool ids: defined reads, unspecified result
+  if (page < 0 || page >= a.num_pages) page = 0;  // out-of-pool id: a defined read; the tile gets no weight
   const size_t blk = ((size_t)page * kKvHeads + a.g) * (kPage * kHeadDim);
   const int nvalid = a.total - kt * kBK;
   if (nvalid >= kBK) {
@@ -136,6 +136,17 @@ __device__ __forceinline__ void issue_tile(const TileArgs& a, int kt, int page, 
     dma_tile(a.k_pages + blk, k_lds, a.wave, k_off);
     dma_tile(a.v_pages + blk, v_lds, a.wave, v_off);
   }
+}
+
+// Causal bound of this lane's query row for key tile kt: keys past it get no weight.  A segment
+// whose table holds an out-of-pool page id runs every tile through the masked steps, and such a
+// tile's bound is -1, so none of its keys gets weight (the same keys decode skips).
+__device__ __forceinline__ int tile_bound(const TileArgs& a, bool any_bad, int kt, int qabs) {
+  if (any_bad) {
+    const int page = a.block_table[kt];
+    if (page < 0 || page >= a.num_pages) return -1;
+  }
+  return qabs;
 }
 
 struct SoftmaxState {
@@ -407,8 +418,15 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
     const int head = kGroup * g + (n >> 4);
     const bool qvalid = qpos < chunk_len;
     const int qabs = prefix_len + qpos;
+    // A page id outside the pool sends the whole segment through the masked steps (tile_bound).
+    bool bad = false;
+    for (int kt = t0 + tid; kt < t1; kt += 64 * kWaves) {
+      const int page = block_table[kt];
+      bad |= page < 0 || page >= num_pages;
+    }
+    const bool any_bad = __syncthreads_or(bad) != 0;
     // Tiles whose keys all precede the workgroup's first query need no causal mask.
-    const int n_plain = min((prefix_len + q0 + 1) / kBK, t1);
+    const int n_plain = any_bad ? t0 : min((prefix_len + q0 + 1) / kBK, t1);
     const TileArgs ta{k_pages,
                       v_pages,
                       block_table,
@@ -472,25 +490,25 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
     // stage) and the O update of block 2kt, reading block 2kt+1's V^T.  Main loop: three steps per
     // trip with compile-time stages, no causal mask, never the last tile.  Then the remaining
     // steps with run-time stages (masked) and the last tile, then block 2n-1's O update.
-#define MTD_PREFILL_STEP(KT, CUR_K, CUR_V, PRV_V, NXT_K, PRV_K, MASK)       \
+#define MTD_PREFILL_STEP(KT, CUR_K, CUR_V, PRV_V, NXT_K, PRV_K, MASK, QB)   \
     {                                                                       \
       pipe_step<MASK, true>(sm, s_a, s_b, p_prev, v_prev, qf,               \
                             CUR_K, +(CUR_K) != +zk_lds0, 1, CUR_V, 0, off,  \
-                            (KT) * kBK, hk, qabs, scale_log2);              \
+                            (KT) * kBK, hk, QB, scale_log2);                \
       wait_dma();                                                           \
       tile_barrier();                                                       \
       if ((KT) + 2 < t1) issue_tile(ta, (KT) + 2, next_page, PRV_K, PRV_V); \
       next_page = tile_page(ta, (KT) + 3);                                  \
       pipe_step<MASK, true>(sm, s_b, s_a, p_prev, v_prev, qf,               \
                             NXT_K, +(NXT_K) != +zk_lds0, 0, CUR_V, 1, off,  \
-                            (KT) * kBK + 32, hk, qabs, scale_log2);         \
+                            (KT) * kBK + 32, hk, QB, scale_log2);           \
     }
     const int n_main = min(n_plain, t1 - 1);
     int kt = t0;
     for (; kt + 3 <= n_main; kt += 3) {
-      MTD_PREFILL_STEP(kt, zk_lds0, v_lds0, v_lds2, zk_lds1, zk_lds2, false)
-      MTD_PREFILL_STEP(kt + 1, zk_lds1, v_lds1, v_lds0, zk_lds2, zk_lds0, false)
-      MTD_PREFILL_STEP(kt + 2, zk_lds2, v_lds2, v_lds1, zk_lds0, zk_lds1, false)
+      MTD_PREFILL_STEP(kt, zk_lds0, v_lds0, v_lds2, zk_lds1, zk_lds2, false, qabs)
+      MTD_PREFILL_STEP(kt + 1, zk_lds1, v_lds1, v_lds0, zk_lds2, zk_lds0, false, qabs)
+      MTD_PREFILL_STEP(kt + 2, zk_lds2, v_lds2, v_lds1, zk_lds0, zk_lds1, false, qabs)
     }
     for (; kt < t1 - 1; ++kt) {
       const int sc = (kt - t0) % 3;
@@ -499,17 +517,19 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
       uint8_t* nk = sc == 0 ? zk_lds1 : sc == 1 ? zk_lds2 : zk_lds0;
       uint8_t* pk = sc == 0 ? zk_lds2 : sc == 1 ? zk_lds0 : zk_lds1;
       uint8_t* pv = sc == 0 ? v_lds2 : sc == 1 ? v_lds0 : v_lds1;
-      MTD_PREFILL_STEP(kt, ck, cv, pv, nk, pk, true)
+      const int qb = tile_bound(ta, any_bad, kt, qabs);
+      MTD_PREFILL_STEP(kt, ck, cv, pv, nk, pk, true, qb)
     }
 #undef MTD_PREFILL_STEP
     {
       const int sc = (kt - t0) % 3;
       const uint8_t* ck = sc == 0 ? zk_lds0 : sc == 1 ? zk_lds1 : zk_lds2;
       const uint8_t* cv = sc == 0 ? v_lds0 : sc == 1 ? v_lds1 : v_lds2;
-      pipe_step<true, true>(sm, s_a, s_b, p_prev, v_prev, qf, ck, ck != zk_lds0, 1, cv, 0, off, kt * kBK, hk, qabs,
+      const int qb = tile_bound(ta, any_bad, kt, qabs);
+      pipe_step<true, true>(sm, s_a, s_b, p_prev, v_prev, qf, ck, ck != zk_lds0, 1, cv, 0, off, kt * kBK, hk, qb,
                             scale_log2);
       pipe_step<true, false>(sm, s_b, s_a, p_prev, v_prev, qf, ck, ck != zk_lds0, 0, cv, 1, off, kt * kBK + 32, hk,
-                             qabs, scale_log2);
+                             qb, scale_log2);
       if (__any(sm.alpha != 1.f)) {
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
@@ -563,9 +583,14 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(float* __restrict__ 
   }
   const float l0 = lse[row], l1 = part_lse[row];
   const float mx = fmaxf(l0, l1);
+  float4* o = reinterpret_cast<float4*>(out + (size_t)row * kHeadDim) + lane;
+  if (mx == kNegInf) {  // neither part holds a key the row may see (out-of-pool pages): empty result
+    *o = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (lane == 0) lse[row] = kNegInf;
+    return;
+  }
   const float w0 = __expf(l0 - mx), w1 = __expf(l1 - mx);
   const float inv = 1.f / (w0 + w1);
-  float4* o = reinterpret_cast<float4*>(out + (size_t)row * kHeadDim) + lane;
   const float4 a = *o;
   const float4 b = reinterpret_cast<const float4*>(part_o + (size_t)row * kHeadDim)[lane];
   *o = make_float4((w0 * a.x + w1 * b.x) * inv, (w0 * a.y + w1 * b.y) * inv, (w0 * a.z + w1 * b.z) * inv,

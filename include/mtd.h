@@ -54,8 +54,10 @@
  *   check returns a negative MTD_ERR_* code, enqueues nothing and leaves all memory untouched.
  *   Values that live on the device (table entries, lengths, offsets) are trusted: if they are
  *   inconsistent with the sizes given on the host the results are unspecified, but no kernel reads
- *   or writes outside the pools, the inputs and the outputs: page ids outside [0, num_pages) are
- *   skipped by mtd_kv_append and mtd_attn_decode and read as page 0 by mtd_attn_prefill_chunk.
+ *   or writes outside the pools, the inputs and the outputs.  Page ids outside [0, num_pages) are
+ *   skipped: mtd_kv_append leaves such a token unwritten, and mtd_attn_decode and
+ *   mtd_attn_prefill_chunk give each query attention over the keys of the valid pages it may see
+ *   (a query that sees none gets O = 0 and LSE = -inf).
  *   A failed kernel launch returns MTD_ERR_HIP; mtd_last_error() gives the detail.
  */
 #ifndef MTD_H
@@ -68,7 +70,7 @@
 extern "C" {
 #endif
 
-#define MTD_ABI_VERSION 4
+#define MTD_ABI_VERSION 5
 
 /* Status codes. */
 #define MTD_OK               0
@@ -260,6 +262,27 @@ int mtd_o_proj(const float* attn, const void* w_o, int32_t n_tok, int32_t num_q_
  */
 int mtd_attn_merge(const float* o_parts, const float* lse_parts, int32_t n_parts, int32_t n_rows,
                    int32_t head_dim, float* out, float* lse, void* stream);
+
+/*
+ * mtd_measure_page_read - measurement aid, not part of attention: read K/V page blocks the way
+ * mtd_attn_decode reads them, and nothing else.
+ *
+ * Decode time is set by streaming a batch's K/V pages from HBM, so the figure to hold it against
+ * is the rate this access pattern reaches on the device.  One wavefront per (pages_per_wave
+ * consecutive entries of page_ids, KV head) reads the whole K and V blocks of those pages with the
+ * decode's lane layout and 16-byte non-temporal loads, folds the words together and writes one
+ * word per lane to sink.  Bytes read: 2 * num_kv_heads * page_size * head_dim * 2 per valid id.
+ *
+ *   page_ids        int32 [n_ids] on the device; ids outside [0, num_pages) are skipped
+ *   n_ids           >= 1;  pages_per_wave 1 .. 64
+ *   sink            uint32 [mtd_measure_page_read_sink_words(n_ids, pages_per_wave)], written
+ *                   (the folded words, meaningful only as a dependency of the loads)
+ */
+int mtd_measure_page_read(const mtd_kv_layer_t* kv, const int32_t* page_ids, int32_t n_ids,
+                          int32_t pages_per_wave, uint32_t* sink, size_t sink_words, void* stream);
+
+/* Words mtd_measure_page_read writes to sink; 0 for arguments it would reject. */
+size_t mtd_measure_page_read_sink_words(int32_t n_ids, int32_t pages_per_wave);
 
 /* Static description of a status code (never NULL). */
 const char* mtd_status_string(int status);

@@ -1,8 +1,9 @@
 """Device-resident block-table entries outside [0, num_pages) are trusted, not checked on the host;
 the header fixes what the kernels do with them: mtd_kv_append skips the token (every other byte of
 the pools is unchanged), mtd_attn_decode skips the page (the result is attention over the keys of
-the valid pages), and mtd_attn_prefill_chunk reads page 0 in its place (unspecified but finite
-values, no access outside the pools)."""
+the valid pages), and mtd_attn_prefill_chunk gives every query row attention over the keys of the
+valid pages it may see (a row that sees none gets O = 0 and LSE = -inf); no access outside the
+pools."""
 
 import numpy as np
 import pytest
@@ -64,14 +65,48 @@ def test_decode_skips_out_of_pool_pages():
     compare(out, lse, o_ref, l_ref, "decode over the valid pages")
 
 
-def test_prefill_reads_page_zero_for_out_of_pool_pages():
-    n_pages = 8
+def _prefill_valid_reference(kh, vh, q_bits, prefix, table, n_pages):
+    """Oracle over the keys of the valid pages: row i sees the valid keys at positions <= prefix + i.
+    Returns (O, LSE, rows with no valid key)."""
+    total = prefix + q_bits.shape[0]
+    keep = [j for j in range(total) if 0 <= table[j // W.PAGE] < n_pages]
+    k = np.stack([oracle.bf16_to_f64(kh[table[j // W.PAGE], :, j % W.PAGE]) for j in keep])
+    v = np.stack([oracle.bf16_to_f64(vh[table[j // W.PAGE], :, j % W.PAGE]) for j in keep])
+    seen = np.searchsorted(np.asarray(keep), prefix + np.arange(q_bits.shape[0]), side="right")
+    rows = np.nonzero(seen > 0)[0]
+    o = np.zeros((q_bits.shape[0], W.HQ, W.HEAD_DIM))
+    lse = np.full((q_bits.shape[0], W.HQ), -np.inf)
+    o[rows], lse[rows] = oracle.attention(oracle.bf16_to_f64(q_bits[rows]), k, v, seen[rows] - 1, W.SCALE)
+    return o, lse, np.nonzero(seen == 0)[0]
+
+
+@pytest.mark.parametrize("prefix,chunk,table", [
+    (3 * W.PAGE, 2 * W.PAGE - 5, [2, 9, 5, -2, 7]),          # prefix and chunk pages out of the pool
+    (0, 300, [-1, 3, 100, 6, 1]),                             # the first rows see no valid key
+    (4000, 4096, None),                                       # many tiles (pair schedule), a few bad ids
+])
+def test_prefill_skips_out_of_pool_pages(prefix, chunk, table):
+    total = prefix + chunk
+    n_used = (total + W.PAGE - 1) // W.PAGE
+    if table is None:
+        rng = np.random.default_rng(81)
+        table = rng.permutation(n_used + 4)[:n_used].astype(np.int64)
+        table[[3, 40, n_used - 70, n_used - 2]] = [-5, n_used + 4, 1 << 30, -1]
+        n_pages = n_used + 4
+    else:
+        n_pages = 8
     kp, vp = new_pool(n_pages, "cuda", seed=78), new_pool(n_pages, "cuda", seed=79)
-    prefix, chunk = 3 * W.PAGE, 2 * W.PAGE - 5
-    table = _i32([2, n_pages + 1, 5, -2, 7])
     q = W.normal_bf16((chunk, W.HQ, W.HEAD_DIM), 80, "cuda")
+    o_ref, l_ref, empty = _prefill_valid_reference(bits(kp), bits(vp), bits(q), prefix, np.asarray(table), n_pages)
+    full = [r for r in range(chunk) if r not in set(empty.tolist())]
     for ws in (None, torch.empty(mtd.prefill_workspace_bytes(chunk), dtype=torch.uint8, device="cuda")):
-        log(f"prefill with out-of-pool page ids, workspace={ws is not None}")
-        out, lse = mtd.mtd_attn_prefill_chunk(kp, vp, q, prefix, table, W.SCALE, workspace=ws)
+        log(f"prefill with out-of-pool page ids, P={prefix} C={chunk}, workspace={ws is not None}")
+        out, lse = mtd.mtd_attn_prefill_chunk(kp, vp, q, prefix, _i32(table), W.SCALE, workspace=ws)
         torch.cuda.synchronize()
-        assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+        if len(empty):
+            e = torch.as_tensor(empty, device="cuda")
+            assert torch.equal(out[e], torch.zeros_like(out[e]))
+            assert bool((lse[e] == -float("inf")).all())
+        idx = torch.as_tensor(full, device="cuda")
+        compare(out[idx], lse[idx], o_ref[full], l_ref[full],
+                f"prefill over the valid pages, P={prefix} C={chunk}{' split' if ws is not None else ''}")
