@@ -943,6 +943,96 @@ def calibrate_copy():
                                          "launches": 5, "kernel": "vectorized_elementwise_kernel (mul)"}}))
 
 
+# --------------------------------------------------------------------------------------------
+# the other target configurations and the practical ceiling, reported beside the default line
+# --------------------------------------------------------------------------------------------
+
+def _mean_event_ms(pairs):
+    return float(np.mean([a.elapsed_time(b) for a, b in pairs]))
+
+
+def extra_prefill90(dev, passes=5, warmup=3):
+    """The 90-minute prompt (17 chunks, 67,500 tokens, peaked keys): aggregate prefill TFLOP/s."""
+    import torch
+    wl = Prefill90(dev)
+    for _ in range(warmup):
+        wl.step()
+    torch.cuda.synchronize()
+    evs = [wl.timed_step() for _ in range(passes)]
+    torch.cuda.synchronize()
+    ms = float(np.mean([sum(e[1].elapsed_time(e[2]) for e in ev) for ev in evs]))
+    tfs = wl.flops / (ms * 1e-3) / 1e12
+    out = {"value": tfs, "unit": "TFLOP/s", "frac": tfs / MFMA_BF16_PEAK_TFLOPS, "ms_per_pass": ms,
+           "flops": wl.flops, "passes": passes, "chunks": len(wl.chunks),
+           "kernels": "prefill_kernel + prefill_merge_kernel (17 calls)"}
+    del wl
+    return out
+
+
+def extra_decode16(dev, steps=20, warmup=500):
+    """16 requests of 27,000-30,000 tokens: decode GB/s.  Returns (line object, workload)."""
+    import torch
+    wl = Decode16(dev)
+    for _ in range(warmup):
+        wl.step()
+    torch.cuda.synchronize()
+    all_evs = []
+    for _ in range(steps):
+        evs = wl.timer.step_events()
+        wl.step(evs)
+        all_evs.append(evs)
+    torch.cuda.synchronize()
+    for evs in all_evs:
+        wl.timer.collect(evs)
+    res = wl.results()["decode"]
+    return {"value": res["value"], "unit": "GB/s", "frac": res["frac"], "ms": res["ms"], "bytes": res["bytes"],
+            "steps": steps, "kernels": "decode_split_kernel + decode_merge_kernel"}, wl
+
+
+def ceiling(dev, dec16, copy_bytes=4 << 30, reps=10):
+    """What HBM gives on this device, measured here: a device-to-device copy of 4 GiB (bytes read +
+    bytes written per second) and mtd_measure_page_read over decode16's pages (the decode's own
+    access pattern: K and V page blocks in table order, 8 pages per wave, no arithmetic)."""
+    import torch
+    mtd = dec16.mtd
+    src = torch.empty(copy_bytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    pairs = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        pairs.append((a, b))
+    torch.cuda.synchronize()
+    copy_ms = _mean_event_ms(pairs)
+    del src, dst
+    tables = dec16.bt.cpu().numpy()
+    ids = np.concatenate([tables[b][: (int(n) + W.PAGE - 1) // W.PAGE] for b, n in enumerate(dec16.lens)])
+    ids_t = torch.as_tensor(ids.astype(np.int32), device=dev)
+    sink = mtd.mtd_measure_page_read(dec16.k, dec16.v, ids_t, 8)
+    for _ in range(20):
+        mtd.mtd_measure_page_read(dec16.k, dec16.v, ids_t, 8, sink)
+    pairs = []
+    for _ in range(reps * 5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        mtd.mtd_measure_page_read(dec16.k, dec16.v, ids_t, 8, sink)
+        b.record()
+        pairs.append((a, b))
+    torch.cuda.synchronize()
+    read_ms = _mean_event_ms(pairs)
+    read_bytes = len(ids) * KV_BYTES_PER_TOKEN * W.PAGE
+    copy_gbs = 2 * copy_bytes / (copy_ms * 1e-3) / 1e9
+    read_gbs = read_bytes / (read_ms * 1e-3) / 1e9
+    return {"copy_gbs": copy_gbs, "copy_bytes_each_way": copy_bytes, "copy_ms": copy_ms,
+            "page_read_gbs": read_gbs, "page_read_bytes": read_bytes, "page_read_ms": read_ms,
+            "page_read_frac": read_gbs / HBM_PEAK_GBS, "unit": "GB/s",
+            "kernels": "hipMemcpy D2D (torch copy_); page_read_kernel (mtd_measure_page_read)"}
+
+
 # Untimed steps per workload, each about 50 ms of GPU work or more.
 WARMUP_DEFAULT = {"mixed_step": 40, "mixed_step_overlap": 40, "mixed_block": 40, "decode16": 500,
                   "prefill90min": 3, "fulldepth_decode": 5, "fulldepth_block": 5, "decode_graph": 200,
@@ -957,6 +1047,8 @@ def main():
                     help="untimed steps (default: enough for ~50 ms of GPU work, past the clock ramp)")
     ap.add_argument("--workload", default="mixed_step", choices=sorted(WORKLOAD_CLASSES))
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing on the host")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="default workload only: skip the 90-minute prefill, decode16 and ceiling objects")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB elementwise copy 5 times (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -1058,6 +1150,18 @@ def main():
     if "proj" in res:
         line["proj"] = {name: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in d.items()}
                         for name, d in res["proj"].items()}
+    if type(wl) is MixedStep and not args.no_extras:
+        # the other configurations that carry the targets, and the measured ceiling
+        line["prefill90min"] = {k: (round(v, 5) if isinstance(v, float) else v)
+                                for k, v in extra_prefill90(dev).items()}
+        d16, dec16 = extra_decode16(dev)
+        line["decode16"] = {k: (round(v, 5) if isinstance(v, float) else v) for k, v in d16.items()}
+        ceil = ceiling(dev, dec16)
+        ceil["decode_frac_of_page_read"] = res["decode"]["value"] / ceil["page_read_gbs"]
+        ceil["decode16_frac_of_page_read"] = d16["value"] / ceil["page_read_gbs"]
+        line["ceiling"] = {k: (round(v, 5) if isinstance(v, float) else v) for k, v in ceil.items()}
+        del dec16
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline and getattr(wl, "cpu_baseline", None) is not None:
         line["cpu_baseline"] = wl.cpu_baseline()
     print(json.dumps(line), flush=True)

@@ -14,6 +14,7 @@ Names match the C entry points:
     mtd_qkv_proj(x, w_qkv, q=None, k_new=None, v_new=None)
     mtd_o_proj(attn, w_o, out=None)
     mtd_attn_merge(o_parts, lse_parts, out=None, lse=None)
+    mtd_measure_page_read(k_pages, v_pages, page_ids, pages_per_wave=8, sink=None)   (measurement aid)
 """
 
 from __future__ import annotations
@@ -93,6 +94,10 @@ def lib() -> ctypes.CDLL:
         cdll.mtd_o_proj.restype = ctypes.c_int
         cdll.mtd_attn_merge.argtypes = [_P, _P, _I, _I, _I, _P, _P, _P]
         cdll.mtd_attn_merge.restype = ctypes.c_int
+        cdll.mtd_measure_page_read.argtypes = [kvp, _P, _I, _I, _P, ctypes.c_size_t, _P]
+        cdll.mtd_measure_page_read.restype = ctypes.c_int
+        cdll.mtd_measure_page_read_sink_words.argtypes = [_I, _I]
+        cdll.mtd_measure_page_read_sink_words.restype = ctypes.c_size_t
         cdll.mtd_status_string.argtypes = [ctypes.c_int]
         cdll.mtd_status_string.restype = ctypes.c_char_p
         cdll.mtd_last_error.argtypes = []
@@ -226,6 +231,20 @@ def mtd_attn_decode(k_pages, v_pages, q, kv_lens, block_tables, max_kv_len: int,
                                  int(max_kv_len), hq, float(scale), workspace.data_ptr(),
                                  workspace.numel(), out.data_ptr(), lse.data_ptr(), _stream()))
     return out, lse
+
+
+def mtd_measure_page_read(k_pages, v_pages, page_ids, pages_per_wave: int = 8, sink=None):
+    """Measurement aid: read the K/V blocks of page_ids (int32 [n] on the device) with the decode's
+    access pattern and nothing else.  Returns the sink (uint8 view of the folded words)."""
+    layer = kv_layer(k_pages, v_pages)
+    _need(page_ids, "page_ids", torch.int32, 1)
+    words = int(lib().mtd_measure_page_read_sink_words(page_ids.shape[0], pages_per_wave))
+    if sink is None:
+        sink = torch.empty(max(4 * words, 4), dtype=torch.uint8, device=page_ids.device)
+    _need(sink, "sink", torch.uint8, 1)
+    _check(lib().mtd_measure_page_read(ctypes.byref(layer), page_ids.data_ptr(), page_ids.shape[0],
+                                       int(pages_per_wave), sink.data_ptr(), sink.numel() // 4, _stream()))
+    return sink
 
 
 def _out(t, name, shape, dtype, like):

@@ -22,7 +22,7 @@ LIB_NAME = "libmtd.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["mtd_api.cpp", "kv_append.hip", "decode.hip", "prefill.hip", "proj.hip", "merge.hip"]
+SOURCES = ["mtd_api.cpp", "kv_append.hip", "decode.hip", "prefill.hip", "proj.hip", "merge.hip", "measure.hip"]
 # Per-file flags.  The prefill kernel never sees a NaN score (keys past a request's end are read
 # from a valid row of its page), so its maxima need no NaN canonicalisation.
 FILE_FLAGS = {"prefill.hip": ["-fno-honor-nans"]}

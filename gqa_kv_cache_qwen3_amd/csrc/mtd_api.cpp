@@ -234,6 +234,26 @@ int mtd_attn_merge(const float* o_parts, const float* lse_parts, int32_t n_parts
                     "merge launch");
 }
 
+size_t mtd_measure_page_read_sink_words(int32_t n_ids, int32_t pages_per_wave) {
+  if (n_ids < 1 || pages_per_wave < 1 || pages_per_wave > 64) return 0;
+  return mtd::page_read_sink_words(n_ids, pages_per_wave);
+}
+
+int mtd_measure_page_read(const mtd_kv_layer_t* kv, const int32_t* page_ids, int32_t n_ids,
+                          int32_t pages_per_wave, uint32_t* sink, size_t sink_words, void* stream) {
+  if (int st = check_layer(kv)) return st;
+  if (n_ids < 1) return fail(MTD_ERR_INVALID_ARG, "n_ids = %d", n_ids);
+  if (pages_per_wave < 1 || pages_per_wave > 64)
+    return fail(MTD_ERR_INVALID_ARG, "pages_per_wave = %d (1 .. 64)", pages_per_wave);
+  if (page_ids == nullptr || sink == nullptr) return fail(MTD_ERR_INVALID_ARG, "page_ids / sink is NULL");
+  const size_t need = mtd::page_read_sink_words(n_ids, pages_per_wave);
+  if (sink_words < need)
+    return fail(MTD_ERR_WORKSPACE, "sink holds %zu words, %zu needed", sink_words, need);
+  return hip_status(mtd::launch_page_read(pools(kv), page_ids, n_ids, pages_per_wave, sink,
+                                          static_cast<hipStream_t>(stream)),
+                    "page read launch");
+}
+
 const char* mtd_status_string(int status) {
   switch (status) {
     case MTD_OK: return "ok";

@@ -81,4 +81,11 @@ hipError_t launch_o_proj(const float* attn, const uint16_t* w_o, int n_tok, uint
 hipError_t launch_attn_merge(const float* o_parts, const float* lse_parts, int n_parts, int n_rows,
                              float* out, float* lse, hipStream_t stream);
 
+// Measurement aid: read the K and V blocks (KV head g = every head) of pages_per_wave consecutive
+// entries of page_ids per wavefront, with the decode's access pattern; one word per lane of every
+// wave goes to sink (page_read_sink_words(n_ids, pages_per_wave) words).
+size_t page_read_sink_words(int n_ids, int pages_per_wave);
+hipError_t launch_page_read(const KvPools& kv, const int32_t* page_ids, int n_ids, int pages_per_wave,
+                            uint32_t* sink, hipStream_t stream);
+
 }  // namespace mtd

@@ -328,6 +328,36 @@ def test_merge_validation(lib, kw, code):
     assert lib.mtd_last_error().decode() != ""
 
 
+def page_read(lib, kv=None, **kw):
+    a = dict(ids=FAKE, n=100, ppw=8, sink=FAKE, words=None)
+    a.update(kw)
+    words = a["words"] if a["words"] is not None else lib.mtd_measure_page_read_sink_words(a["n"], a["ppw"])
+    return lib.mtd_measure_page_read(ctypes.byref(kv or layer()), a["ids"], a["n"], a["ppw"], a["sink"], words, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n=0), mtd.MTD_ERR_INVALID_ARG),
+    (dict(ppw=0), mtd.MTD_ERR_INVALID_ARG),
+    (dict(ppw=65), mtd.MTD_ERR_INVALID_ARG),
+    (dict(ids=None), mtd.MTD_ERR_INVALID_ARG),
+    (dict(sink=None), mtd.MTD_ERR_INVALID_ARG),
+    (dict(words=13 * 8 * 64 - 1), mtd.MTD_ERR_WORKSPACE),
+])
+def test_page_read_validation(lib, kw, code):
+    assert page_read(lib, **kw) == code
+    assert lib.mtd_last_error().decode() != ""
+
+
+def test_page_read_sink_words(lib):
+    assert lib.mtd_measure_page_read_sink_words(100, 8) == 13 * 8 * 64
+    assert lib.mtd_measure_page_read_sink_words(0, 8) == 0
+    assert lib.mtd_measure_page_read_sink_words(10, 0) == 0
+
+
+def test_page_read_checks_the_layer(lib):
+    assert page_read(lib, kv=layer(head_dim=64)) == mtd.MTD_ERR_UNSUPPORTED
+
+
 def test_merge_of_no_rows_enqueues_nothing(lib):
     assert merge(lib, n_rows=0) == mtd.MTD_OK
     assert merge(lib, n_rows=0, n_parts=mtd.MTD_MAX_MERGE_PARTS) == mtd.MTD_OK

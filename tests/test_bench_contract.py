@@ -53,6 +53,11 @@ def test_default_run_prints_one_contract_line():
     assert r["bound"] in ("hbm", "mfma") and r["unit"] in ("GB/s", "TFLOP/s")
     assert 0 < r["frac"] < 1 and abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-3
     assert "traffic" in r
+    for k in ("prefill90min", "decode16", "ceiling"):
+        assert k in d, k
+    assert d["prefill90min"]["unit"] == "TFLOP/s" and 0 < d["prefill90min"]["frac"] < 1
+    assert d["decode16"]["unit"] == "GB/s" and 0 < d["decode16"]["frac"] < 1
+    assert d["ceiling"]["copy_gbs"] > 0 and d["ceiling"]["page_read_gbs"] > 0
     c = d["cpu_baseline"]
     for k in ("value", "unit", "cores", "affinity_cores", "cpu_model", "kind", "sample", "prefill_tflops"):
         assert k in c, k
