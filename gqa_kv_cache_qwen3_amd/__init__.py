@@ -14,6 +14,7 @@ Names match the C entry points:
     mtd_qkv_proj(x, w_qkv, q=None, k_new=None, v_new=None)
     mtd_o_proj(attn, w_o, out=None)
     mtd_attn_merge(o_parts, lse_parts, out=None, lse=None)
+    mtd_attn_decode_noalloc(k_pages, v_pages, q, kv_lens, block_tables, max_kv_len, scale, out, lse)
     mtd_measure_page_read(k_pages, v_pages, page_ids, pages_per_wave=8, sink=None)   (measurement aid)
 """
 
@@ -35,6 +36,7 @@ MTD_ERR_WORKSPACE = -4
 MTD_ERR_HIP = -5
 MTD_MAX_CONTEXT = 131072
 MTD_MAX_MERGE_PARTS = 1024
+MTD_DECODE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 NUM_Q_HEADS = 16
 NUM_KV_HEADS = 8
@@ -94,6 +96,8 @@ def lib() -> ctypes.CDLL:
         cdll.mtd_o_proj.restype = ctypes.c_int
         cdll.mtd_attn_merge.argtypes = [_P, _P, _I, _I, _I, _P, _P, _P]
         cdll.mtd_attn_merge.restype = ctypes.c_int
+        cdll.mtd_attn_decode_noalloc.argtypes = [kvp, _P, _P, _P, _I, _I, _I, _I, ctypes.c_float, _P, _P, _P]
+        cdll.mtd_attn_decode_noalloc.restype = ctypes.c_int
         cdll.mtd_measure_page_read.argtypes = [kvp, _P, _I, _I, _P, ctypes.c_size_t, _P]
         cdll.mtd_measure_page_read.restype = ctypes.c_int
         cdll.mtd_measure_page_read_sink_words.argtypes = [_I, _I]
@@ -245,6 +249,27 @@ def mtd_measure_page_read(k_pages, v_pages, page_ids, pages_per_wave: int = 8, s
     _check(lib().mtd_measure_page_read(ctypes.byref(layer), page_ids.data_ptr(), page_ids.shape[0],
                                        int(pages_per_wave), sink.data_ptr(), sink.numel() // 4, _stream()))
     return sink
+
+
+def mtd_attn_decode_noalloc(k_pages, v_pages, q, kv_lens, block_tables, max_kv_len: int, scale: float,
+                            out, lse):
+    """mtd_attn_decode with the library's static scratch instead of a workspace: allocates nothing,
+    so out (float32 [B][Hq][D]) and lse (float32 [B][Hq]) must be given."""
+    layer = kv_layer(k_pages, v_pages)
+    _need(q, "q", torch.bfloat16, 3)
+    _need(kv_lens, "kv_lens", torch.int32, 1)
+    _need(block_tables, "block_tables", torch.int32, 2)
+    _need(out, "out", torch.float32, 3)
+    _need(lse, "lse", torch.float32, 2)
+    b, hq, d = q.shape
+    if kv_lens.shape[0] != b or block_tables.shape[0] != b:
+        raise ValueError("kv_lens and block_tables must have one entry/row per request")
+    if tuple(out.shape) != (b, hq, d) or tuple(lse.shape) != (b, hq):
+        raise ValueError("out must be [B][Hq][D] and lse [B][Hq]")
+    _check(lib().mtd_attn_decode_noalloc(ctypes.byref(layer), q.data_ptr(), kv_lens.data_ptr(),
+                                         block_tables.data_ptr(), block_tables.shape[1], b, int(max_kv_len),
+                                         hq, float(scale), out.data_ptr(), lse.data_ptr(), _stream()))
+    return out, lse
 
 
 def _out(t, name, shape, dtype, like):

@@ -22,6 +22,8 @@
 // chunks o and 8 + o (dims 8o..8o+7 and 64+8o..64+8o+7).  One load instruction therefore reads 8
 // whole 128-byte lines.  A slot's score is the sum over its 8 lanes (three DPP steps); values are
 // accumulated with packed bf16 dot products pairing two slots per instruction.
+#include <atomic>
+
 #include "device_util.h"
 #include "mtd_internal.h"
 
@@ -340,6 +342,32 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
 }
 
 }  // namespace
+
+// Scratch of mtd_attn_decode_noalloc: the split partials live in this file-scope device array
+// instead of a caller workspace.  Every GPU the library runs on holds its own copy until the
+// process ends.  In host code the name `scratch` is only a host-side stand-in; its device address
+// comes from hipGetSymbolAddress, once per device, and only that address is ever used.
+__device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+namespace {
+std::atomic<void*> g_scratch[kMaxDevices];
+}  // namespace
+
+hipError_t decode_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return err;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch[dev].store(p, std::memory_order_release);  // the same address if two threads race here
+  }
+  *ptr = p;
+  return hipSuccess;
+}
 
 size_t decode_workspace_bytes(int batch, int max_kv_len) {
   const size_t parts = (size_t)batch * (size_t)split_parts_bound(max_kv_len);

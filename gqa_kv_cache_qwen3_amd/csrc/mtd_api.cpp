@@ -12,6 +12,8 @@
 
 namespace {
 
+static_assert(MTD_DECODE_NOALLOC_SCRATCH_BYTES == mtd::kDecodeScratchBytes, "scratch size in the header");
+
 thread_local char g_last_error[512] = "";
 
 int fail(int status, const char* fmt, ...) {
@@ -185,6 +187,39 @@ int mtd_attn_decode(const mtd_kv_layer_t* kv, const void* q, const int32_t* kv_l
   return hip_status(mtd::launch_decode(pools(kv), static_cast<const uint16_t*>(q), kv_lens,
                                        block_tables, bt_stride, batch, max_kv_len, scale,
                                        workspace, out, lse, static_cast<hipStream_t>(stream)),
+                    "decode launch");
+}
+
+int mtd_attn_decode_noalloc(const mtd_kv_layer_t* kv, const void* q, const int32_t* kv_lens,
+                            const int32_t* block_tables, int32_t bt_stride, int32_t batch,
+                            int32_t max_kv_len, int32_t num_q_heads, float scale, float* out,
+                            float* lse, void* stream) {
+  int st = check_layer(kv);
+  if (st != MTD_OK) return st;
+  if ((st = check_heads(num_q_heads, kv->num_kv_heads)) != MTD_OK) return st;
+  if ((st = check_scale(scale)) != MTD_OK) return st;
+  if (q == nullptr || kv_lens == nullptr || block_tables == nullptr || out == nullptr || lse == nullptr)
+    return fail(MTD_ERR_INVALID_ARG, "q / kv_lens / block_tables / out / lse is NULL");
+  if (!aligned16(q) || !aligned16(out)) return fail(MTD_ERR_INVALID_ARG, "q / out not 16-byte aligned");
+  if (batch <= 0) return fail(MTD_ERR_INVALID_ARG, "batch = %d", batch);
+  if (max_kv_len <= 0) return fail(MTD_ERR_INVALID_ARG, "max_kv_len = %d", max_kv_len);
+  if (max_kv_len > MTD_MAX_CONTEXT)
+    return fail(MTD_ERR_CAPACITY, "max_kv_len %d exceeds %d", max_kv_len, MTD_MAX_CONTEXT);
+  const int64_t pages = ((int64_t)max_kv_len + mtd::kPage - 1) / mtd::kPage;
+  if (bt_stride < pages)
+    return fail(MTD_ERR_CAPACITY, "bt_stride %d < %lld pages for max_kv_len %d", bt_stride,
+                (long long)pages, max_kv_len);
+  const size_t need = mtd::decode_workspace_bytes(batch, max_kv_len);
+  if (need > mtd::kDecodeScratchBytes)
+    return fail(MTD_ERR_WORKSPACE,
+                "batch %d with max_kv_len %d needs %zu bytes of scratch; the static scratch holds %zu "
+                "(MTD_DECODE_NOALLOC_SCRATCH_BYTES)",
+                batch, max_kv_len, need, mtd::kDecodeScratchBytes);
+  void* scratch = nullptr;
+  if ((st = hip_status(mtd::decode_scratch(&scratch), "decode scratch lookup")) != MTD_OK) return st;
+  return hip_status(mtd::launch_decode(pools(kv), static_cast<const uint16_t*>(q), kv_lens,
+                                       block_tables, bt_stride, batch, max_kv_len, scale, scratch,
+                                       out, lse, static_cast<hipStream_t>(stream)),
                     "decode launch");
 }
 

@@ -61,6 +61,14 @@ hipError_t launch_prefill(const KvPools& kv, const uint16_t* q, int chunk_len, i
 // LSE float32 [max_parts][kQHeads], max_parts = batch * split_parts_bound(max_kv_len).
 size_t decode_workspace_bytes(int batch, int max_kv_len);
 
+// Allocation-free decode: the partials go to a static device array of kDecodeScratchBytes per
+// GPU (64 MiB: batch * split_parts_bound(max_kv_len) up to 8128 partials, e.g. 64 requests of
+// 64,512 tokens or 31 of 131,072).  decode_scratch gives the calling thread's current device's
+// copy (looked up with hipGetSymbolAddress on first use on that device).
+constexpr size_t kDecodeScratchBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;
+hipError_t decode_scratch(void** ptr);
+
 hipError_t launch_decode(const KvPools& kv, const uint16_t* q, const int32_t* kv_lens,
                          const int32_t* block_tables, int bt_stride, int batch, int max_kv_len,
                          float scale, void* workspace, float* out, float* lse, hipStream_t stream);

@@ -70,7 +70,7 @@
 extern "C" {
 #endif
 
-#define MTD_ABI_VERSION 5
+#define MTD_ABI_VERSION 6
 
 /* Status codes. */
 #define MTD_OK               0
@@ -199,6 +199,29 @@ int mtd_attn_decode(const mtd_kv_layer_t* kv, const void* q, const int32_t* kv_l
                     const int32_t* block_tables, int32_t bt_stride, int32_t batch,
                     int32_t max_kv_len, int32_t num_q_heads, float scale, void* workspace,
                     size_t workspace_bytes, float* out, float* lse, void* stream);
+
+/* Bytes of the static device scratch mtd_attn_decode_noalloc uses on each GPU (64 MiB). */
+#define MTD_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * mtd_attn_decode_noalloc - mtd_attn_decode without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  It allocates nothing and calls no allocating routine.
+ *
+ * Arguments, results and errors are those of mtd_attn_decode (same kernels, same bits), except:
+ * the split partials go to a static device array of MTD_DECODE_NOALLOC_SCRATCH_BYTES per GPU
+ * (mapped with the library, held until the process ends), so
+ * mtd_attn_decode_workspace_bytes(batch, num_q_heads, max_kv_len, head_dim) must not exceed it,
+ * else MTD_ERR_WORKSPACE (64 MiB holds 8128 partials: e.g. 64 requests of up to 64,512 tokens or
+ * 31 of up to 131,072).  All calls on one GPU share that array and it keeps the last call's
+ * contents: calls that overlap on one GPU (other streams, other threads) race and give
+ * unspecified results; order them on one stream.  The first call on a device looks up the array's
+ * device address (hipGetSymbolAddress); a failure there returns MTD_ERR_HIP.
+ */
+int mtd_attn_decode_noalloc(const mtd_kv_layer_t* kv, const void* q, const int32_t* kv_lens,
+                            const int32_t* block_tables, int32_t bt_stride, int32_t batch,
+                            int32_t max_kv_len, int32_t num_q_heads, float scale, float* out,
+                            float* lse, void* stream);
 
 /*
  * mtd_qkv_proj - the QKV projection of new tokens: q = Wq x, k = Wk x, v = Wv x.

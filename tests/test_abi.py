@@ -328,6 +328,44 @@ def test_merge_validation(lib, kw, code):
     assert lib.mtd_last_error().decode() != ""
 
 
+def decode_noalloc(lib, kv=None, **kw):
+    a = dict(q=FAKE, lens=FAKE, bt=FAKE, stride=2048, batch=2, max_len=1000, hq=16, scale=0.088, out=FAKE,
+             lse=FAKE)
+    a.update(kw)
+    return lib.mtd_attn_decode_noalloc(ctypes.byref(kv or layer()), a["q"], a["lens"], a["bt"], a["stride"],
+                                       a["batch"], a["max_len"], a["hq"], a["scale"], a["out"], a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), mtd.MTD_ERR_INVALID_ARG),
+    (dict(lens=None), mtd.MTD_ERR_INVALID_ARG),
+    (dict(bt=None), mtd.MTD_ERR_INVALID_ARG),
+    (dict(out=None), mtd.MTD_ERR_INVALID_ARG),
+    (dict(lse=None), mtd.MTD_ERR_INVALID_ARG),
+    (dict(out=FAKE + 4), mtd.MTD_ERR_INVALID_ARG),
+    (dict(batch=0), mtd.MTD_ERR_INVALID_ARG),
+    (dict(max_len=0), mtd.MTD_ERR_INVALID_ARG),
+    (dict(max_len=131073), mtd.MTD_ERR_CAPACITY),
+    (dict(stride=15), mtd.MTD_ERR_CAPACITY),
+    (dict(hq=8), mtd.MTD_ERR_UNSUPPORTED),
+    (dict(scale=0.0), mtd.MTD_ERR_INVALID_ARG),
+    # 33 requests at the 128K cap need more partials than the static scratch holds
+    (dict(batch=33, max_len=131072), mtd.MTD_ERR_WORKSPACE),
+])
+def test_decode_noalloc_validation(lib, kw, code):
+    assert decode_noalloc(lib, **kw) == code
+    assert lib.mtd_last_error().decode() != ""
+
+
+def test_decode_noalloc_scratch_limit_matches_the_header(lib):
+    text = open(HEADER).read()
+    assert "#define MTD_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)" in text
+    assert mtd.MTD_DECODE_NOALLOC_SCRATCH_BYTES == 64 << 20
+    # the largest batch at the cap that fits: 31 requests (7936 partials); 32 do not (8192 > 8128)
+    assert lib.mtd_attn_decode_workspace_bytes(31, 16, 131072, 128) <= mtd.MTD_DECODE_NOALLOC_SCRATCH_BYTES
+    assert lib.mtd_attn_decode_workspace_bytes(32, 16, 131072, 128) > mtd.MTD_DECODE_NOALLOC_SCRATCH_BYTES
+
+
 def page_read(lib, kv=None, **kw):
     a = dict(ids=FAKE, n=100, ppw=8, sink=FAKE, words=None)
     a.update(kw)
