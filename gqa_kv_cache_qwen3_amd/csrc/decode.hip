@@ -369,11 +369,6 @@ hipError_t decode_scratch(void** ptr) {
   return hipSuccess;
 }
 
-size_t decode_workspace_bytes(int batch, int max_kv_len) {
-  const size_t parts = (size_t)batch * (size_t)split_parts_bound(max_kv_len);
-  return parts * kQHeads * (kHeadDim + 1) * sizeof(float);
-}
-
 hipError_t launch_decode(const KvPools& kv, const uint16_t* q, const int32_t* kv_lens,
                          const int32_t* block_tables, int bt_stride, int batch, int max_kv_len,
                          float scale, void* workspace, float* out, float* lse, hipStream_t stream) {

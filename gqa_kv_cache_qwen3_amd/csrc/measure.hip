@@ -28,8 +28,9 @@ __global__ __launch_bounds__(64) void page_read_kernel(const uint16_t* __restric
   const int g = blockIdx.x % kKvHeads;
   const int sg = lane >> 3, o = lane & 7;  // the decode's layout: slots 8a + sg, chunks o and 8 + o
   u32x4_t acc = {0u, 0u, 0u, 0u};
-  const int e1 = min(n_ids, (w + 1) * pages_per_wave);
-  for (int e = w * pages_per_wave; e < e1; ++e) {
+  const int e0 = (int)min((int64_t)w * pages_per_wave, (int64_t)n_ids);
+  const int e1 = (int)min((int64_t)(w + 1) * pages_per_wave, (int64_t)n_ids);
+  for (int e = e0; e < e1; ++e) {
     const int page = page_ids[e];
     if (page < 0 || page >= num_pages) continue;
     const size_t blk = ((size_t)page * kKvHeads + g) * (kPage * kHeadDim);
@@ -52,13 +53,9 @@ __global__ __launch_bounds__(64) void page_read_kernel(const uint16_t* __restric
 
 }  // namespace
 
-size_t page_read_sink_words(int n_ids, int pages_per_wave) {
-  return (size_t)((n_ids + pages_per_wave - 1) / pages_per_wave) * kKvHeads * 64;
-}
-
 hipError_t launch_page_read(const KvPools& kv, const int32_t* page_ids, int n_ids, int pages_per_wave,
                             uint32_t* sink, hipStream_t stream) {
-  const int waves = (n_ids + pages_per_wave - 1) / pages_per_wave;
+  const int waves = (int)(((int64_t)n_ids + pages_per_wave - 1) / pages_per_wave);
   page_read_kernel<<<dim3(waves * kKvHeads), dim3(64), 0, stream>>>(kv.k, kv.v, kv.num_pages, page_ids, n_ids,
                                                                      pages_per_wave, sink);
   return hipGetLastError();

@@ -54,7 +54,6 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void attn_merge_kernel(
 
 hipError_t launch_attn_merge(const float* o_parts, const float* lse_parts, int n_parts, int n_rows,
                              float* out, float* lse, hipStream_t stream) {
-  if (n_rows == 0) return hipSuccess;
   attn_merge_kernel<<<dim3((n_rows + kRowsPerBlock - 1) / kRowsPerBlock), dim3(64 * kRowsPerBlock), 0,
                       stream>>>(o_parts, lse_parts, n_parts, n_rows, out, lse);
   return hipGetLastError();

@@ -232,6 +232,7 @@ int mtd_qkv_proj(const void* x, const void* w_qkv, int32_t n_tok, int32_t hidden
     return fail(MTD_ERR_INVALID_ARG, "x / w_qkv / q / k_new / v_new is NULL");
   if (!aligned16(x) || !aligned16(w_qkv) || !aligned16(q) || !aligned16(k_new) || !aligned16(v_new))
     return fail(MTD_ERR_INVALID_ARG, "x / w_qkv / q / k_new / v_new not 16-byte aligned");
+  if (n_tok == 0) return ok();
   return hip_status(mtd::launch_qkv_proj(static_cast<const uint16_t*>(x),
                                          static_cast<const uint16_t*>(w_qkv), n_tok,
                                          static_cast<uint16_t*>(q), static_cast<uint16_t*>(k_new),
@@ -248,6 +249,7 @@ int mtd_o_proj(const float* attn, const void* w_o, int32_t n_tok, int32_t num_q_
     return fail(MTD_ERR_INVALID_ARG, "attn / w_o / out is NULL");
   if (!aligned16(attn) || !aligned16(w_o) || !aligned16(out))
     return fail(MTD_ERR_INVALID_ARG, "attn / w_o / out not 16-byte aligned");
+  if (n_tok == 0) return ok();
   return hip_status(mtd::launch_o_proj(attn, static_cast<const uint16_t*>(w_o), n_tok,
                                        static_cast<uint16_t*>(out), static_cast<hipStream_t>(stream)),
                     "output projection launch");
@@ -264,6 +266,7 @@ int mtd_attn_merge(const float* o_parts, const float* lse_parts, int32_t n_parts
     return fail(MTD_ERR_INVALID_ARG, "o_parts / lse_parts / out / lse is NULL");
   if (!aligned16(o_parts) || !aligned16(out))
     return fail(MTD_ERR_INVALID_ARG, "o_parts / out not 16-byte aligned");
+  if (n_rows == 0) return ok();
   return hip_status(mtd::launch_attn_merge(o_parts, lse_parts, n_parts, n_rows, out, lse,
                                            static_cast<hipStream_t>(stream)),
                     "merge launch");

@@ -42,7 +42,8 @@ struct KvPools {
   int num_pages;
 };
 
-// Launchers (defined next to their kernels).  Arguments are validated by the caller.
+// Sizes are host arithmetic, inline here; launchers are defined next to their kernels.  Arguments
+// are validated by the caller.
 hipError_t launch_kv_append(const KvPools& kv, const uint16_t* k_new, const uint16_t* v_new,
                             const int32_t* cu_new, const int32_t* start_pos,
                             const int32_t* block_tables, int bt_stride, int n_req, int n_new,
@@ -51,7 +52,9 @@ hipError_t launch_kv_append(const KvPools& kv, const uint16_t* k_new, const uint
 // Optional prefill workspace: partial O float32 [chunk_len][kQHeads][kHeadDim], then partial LSE
 // float32 [chunk_len][kQHeads] (one part of every split item, merged after the kernel).
 // workspace == nullptr: one pass per item, no split.
-size_t prefill_workspace_bytes(int chunk_len);
+inline size_t prefill_workspace_bytes(int chunk_len) {
+  return (size_t)chunk_len * kQHeads * (kHeadDim + 1) * sizeof(float);
+}
 
 hipError_t launch_prefill(const KvPools& kv, const uint16_t* q, int chunk_len, int prefix_len,
                           const int32_t* block_table, float scale, void* workspace, float* out,
@@ -59,7 +62,10 @@ hipError_t launch_prefill(const KvPools& kv, const uint16_t* q, int chunk_len, i
 
 // Workspace layout of the decode: partial O float32 [max_parts][kQHeads][kHeadDim], then partial
 // LSE float32 [max_parts][kQHeads], max_parts = batch * split_parts_bound(max_kv_len).
-size_t decode_workspace_bytes(int batch, int max_kv_len);
+inline size_t decode_workspace_bytes(int batch, int max_kv_len) {
+  const size_t parts = (size_t)batch * (size_t)split_parts_bound(max_kv_len);
+  return parts * kQHeads * (kHeadDim + 1) * sizeof(float);
+}
 
 // Allocation-free decode: the partials go to a static device array of kDecodeScratchBytes per
 // GPU (64 MiB: batch * split_parts_bound(max_kv_len) up to 8128 partials, e.g. 64 requests of
@@ -73,7 +79,7 @@ hipError_t launch_decode(const KvPools& kv, const uint16_t* q, const int32_t* kv
                          const int32_t* block_tables, int bt_stride, int batch, int max_kv_len,
                          float scale, void* workspace, float* out, float* lse, hipStream_t stream);
 
-// The projections around the attention (n_tok >= 0; pointers 16-byte aligned):
+// The projections around the attention (n_tok >= 1; pointers 16-byte aligned):
 //   x bf16 [n_tok][kHidden], w_qkv bf16 [(kQHeads + 2 kKvHeads) kHeadDim][kHidden]
 //     -> q bf16 [n_tok][kQHeads][kHeadDim], k, v bf16 [n_tok][kKvHeads][kHeadDim];
 //   attn float32 [n_tok][kQHeads][kHeadDim], w_o bf16 [kHidden][kQHeads kHeadDim]
@@ -85,14 +91,16 @@ hipError_t launch_o_proj(const float* attn, const uint16_t* w_o, int n_tok, uint
 
 // LSE combination of attention results over disjoint key sets: o_parts float32
 // [n_parts][n_rows][kHeadDim], lse_parts float32 [n_parts][n_rows] -> out [n_rows][kHeadDim],
-// lse [n_rows] (n_parts >= 1, n_rows >= 0).
+// lse [n_rows] (n_parts >= 1, n_rows >= 1).
 hipError_t launch_attn_merge(const float* o_parts, const float* lse_parts, int n_parts, int n_rows,
                              float* out, float* lse, hipStream_t stream);
 
 // Measurement aid: read the K and V blocks (KV head g = every head) of pages_per_wave consecutive
 // entries of page_ids per wavefront, with the decode's access pattern; one word per lane of every
 // wave goes to sink (page_read_sink_words(n_ids, pages_per_wave) words).
-size_t page_read_sink_words(int n_ids, int pages_per_wave);
+inline size_t page_read_sink_words(int n_ids, int pages_per_wave) {
+  return ((size_t)n_ids + pages_per_wave - 1) / pages_per_wave * kKvHeads * 64;
+}
 hipError_t launch_page_read(const KvPools& kv, const int32_t* page_ids, int n_ids, int pages_per_wave,
                             uint32_t* sink, hipStream_t stream);
 

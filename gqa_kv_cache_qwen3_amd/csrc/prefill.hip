@@ -614,10 +614,6 @@ int device_cus() {
   return n;
 }
 
-size_t prefill_workspace_bytes(int chunk_len) {
-  return (size_t)chunk_len * kQHeads * (kHeadDim + 1) * sizeof(float);
-}
-
 hipError_t launch_prefill(const KvPools& kv, const uint16_t* q, int chunk_len, int prefix_len,
                           const int32_t* block_table, float scale, void* workspace, float* out,
                           float* lse, hipStream_t stream) {

@@ -374,7 +374,6 @@ int rows_major_split(int rows, size_t a_row_bytes, size_t w_bytes) {
 
 hipError_t launch_qkv_proj(const uint16_t* x, const uint16_t* w_qkv, int n_tok, uint16_t* q,
                            uint16_t* k, uint16_t* v, hipStream_t stream) {
-  if (n_tok == 0) return hipSuccess;
   constexpr int kN = (kQHeads + 2 * kKvHeads) * kHeadDim;
   const int n_tm = (n_tok + kTM - 1) / kTM;
   const int n_tn = kN / kTN;
@@ -400,7 +399,6 @@ hipError_t launch_qkv_proj(const uint16_t* x, const uint16_t* w_qkv, int n_tok, 
 
 hipError_t launch_o_proj(const float* attn, const uint16_t* w_o, int n_tok, uint16_t* out,
                          hipStream_t stream) {
-  if (n_tok == 0) return hipSuccess;
   constexpr int kK = kQHeads * kHeadDim;
   const int n_tm = (n_tok + kTM - 1) / kTM;
   const int n_tn = kHidden / kTN;
