@@ -703,12 +703,16 @@ class FullDepthBlock(FullDepth):
 
 
 class MixedStepOverlap(MixedStep):
-    """The mixed step with the decode on a second stream (default priority), so it can fill CUs the
-    prefill leaves idle: the append first, then the prefill on the library's stream and the decode
-    on the second one, joined before the next step.  The prefill runs in one pass (no workspace):
-    its uneven causal tail is what the decode fills.  Outputs are bit-identical to the sequential
-    step with a one-pass prefill; per-kernel times here include the contention between the two."""
+    """The mixed step with its prefill and decode running at the same time on separate compute
+    units: after the append, the prefill runs on the library's stream on a budget of CU_BUDGET
+    compute units (mtd_attn_prefill_chunk_cus: the chunk's causal work spread evenly over that
+    many workgroups, tiles cut at range boundaries merged), and the decode on a second stream
+    (default priority), whose waves take the CUs the prefill leaves free; the two are joined
+    before the next step.  Prefill is bound by the matrix units and decode by HBM, so the step
+    tends to max(prefill on fewer CUs, decode on the rest) instead of their sum.  Per-kernel
+    times here include the contention between the two; the step time is the figure of merit."""
     name = "mixed_step_overlap"
+    CU_BUDGET = 224
 
     def __init__(self, dev):
         super().__init__(dev)
@@ -716,6 +720,7 @@ class MixedStepOverlap(MixedStep):
         self.side = torch.cuda.Stream(device=dev)
         self.appended, self.decoded = torch.cuda.Event(), torch.cuda.Event()
         self.timer = OverlapTimer()
+        self.cu_budget = int(os.environ.get("MTD_BENCH_CU_BUDGET", self.CU_BUDGET))
 
     def step(self, events=None):
         mtd, torch = self.mtd, self.torch
@@ -724,7 +729,8 @@ class MixedStepOverlap(MixedStep):
         mtd.mtd_kv_append(self.k, self.v, self.k_new, self.v_new, self.cu, self.start, self.bt_all)
         if events: events[1].record()
         self.appended.record(main)
-        mtd.mtd_attn_prefill_chunk(self.k, self.v, self.q_a, self.prefix, self.bt_a, W.SCALE, self.o_a, self.l_a)
+        mtd.mtd_attn_prefill_chunk_cus(self.k, self.v, self.q_a, self.prefix, self.bt_a, W.SCALE, self.ws_p,
+                                       self.cu_budget, self.o_a, self.l_a)
         if events: events[2].record()
         self.side.wait_event(self.appended)
         with torch.cuda.stream(self.side):
@@ -734,28 +740,38 @@ class MixedStepOverlap(MixedStep):
             if events: events[4].record()
             self.decoded.record()
         main.wait_event(self.decoded)
+        if events: events[5].record()
 
     def config(self):
         c = super().config()
-        c["workload"] = "mixed_step_overlap: " + c["workload"].split(": ", 1)[1] + "; decode on a second stream"
+        c["workload"] = ("mixed_step_overlap: " + c["workload"].split(": ", 1)[1] +
+                         f"; prefill on {self.cu_budget} CUs beside the decode on a second stream")
+        c["prefill_cu_budget"] = self.cu_budget
         return c
+
+    def results(self):
+        res = super().results()
+        res["step"] = {"overlapped_ms": self.timer.mean_ms("step"), "append_ms": self.timer.mean_ms("append")}
+        return res
 
     cpu_baseline = None
 
 
 class OverlapTimer(Timer):
-    """append and prefill events on the library's stream, decode events on the second stream."""
+    """append and prefill events on the library's stream, decode events on the second stream, and
+    the whole step (append start to the join of both streams)."""
 
     def __init__(self):
-        super().__init__(["append", "prefill", "decode"])
+        super().__init__(["append", "prefill", "decode", "step"])
 
     def step_events(self):
-        return [self.torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        return [self.torch.cuda.Event(enable_timing=True) for _ in range(6)]
 
     def collect(self, events):
         self.samples["append"].append(events[0].elapsed_time(events[1]))
         self.samples["prefill"].append(events[1].elapsed_time(events[2]))
         self.samples["decode"].append(events[3].elapsed_time(events[4]))
+        self.samples["step"].append(events[0].elapsed_time(events[5]))
 
 
 class DecodeGraph:

@@ -8,7 +8,10 @@ without it raises.
 
 Names match the C entry points:
     mtd_kv_append(k_pages, v_pages, k_new, v_new, cu_new, start_pos, block_tables)
-    mtd_attn_prefill_chunk(k_pages, v_pages, q, prefix_len, block_table, scale, out=None, lse=None)
+    mtd_attn_prefill_chunk(k_pages, v_pages, q, prefix_len, block_table, scale, out=None, lse=None,
+                           workspace=None)
+    mtd_attn_prefill_chunk_cus(k_pages, v_pages, q, prefix_len, block_table, scale, workspace, cu_budget,
+                               out=None, lse=None)
     mtd_attn_decode(k_pages, v_pages, q, kv_lens, block_tables, max_kv_len, scale,
                     workspace=None, out=None, lse=None)
     mtd_qkv_proj(x, w_qkv, q=None, k_new=None, v_new=None)
@@ -96,6 +99,9 @@ def lib() -> ctypes.CDLL:
         cdll.mtd_o_proj.restype = ctypes.c_int
         cdll.mtd_attn_merge.argtypes = [_P, _P, _I, _I, _I, _P, _P, _P]
         cdll.mtd_attn_merge.restype = ctypes.c_int
+        cdll.mtd_attn_prefill_chunk_cus.argtypes = [kvp, _P, _I, _I, _P, _I, _I, ctypes.c_float, _P,
+                                                    ctypes.c_size_t, _I, _P, _P, _P]
+        cdll.mtd_attn_prefill_chunk_cus.restype = ctypes.c_int
         cdll.mtd_attn_decode_noalloc.argtypes = [kvp, _P, _P, _P, _I, _I, _I, _I, ctypes.c_float, _P, _P, _P]
         cdll.mtd_attn_decode_noalloc.restype = ctypes.c_int
         cdll.mtd_measure_page_read.argtypes = [kvp, _P, _I, _I, _P, ctypes.c_size_t, _P]
@@ -197,6 +203,33 @@ def mtd_attn_prefill_chunk(k_pages, v_pages, q, prefix_len: int, block_table, sc
                                         block_table.data_ptr(), block_table.shape[0], hq,
                                         float(scale), ws_ptr, ws_bytes, out.data_ptr(),
                                         lse.data_ptr(), _stream()))
+    return out, lse
+
+
+def mtd_attn_prefill_chunk_cus(k_pages, v_pages, q, prefix_len: int, block_table, scale: float, workspace,
+                               cu_budget: int, out=None, lse=None):
+    """mtd_attn_prefill_chunk on a budget of cu_budget compute units (0 = all; > 0 needs the
+    workspace), leaving the device's other CUs free for work on another stream."""
+    layer = kv_layer(k_pages, v_pages)
+    _need(q, "q", torch.bfloat16, 3)
+    _need(block_table, "block_table", torch.int32, 1)
+    c, hq, d = q.shape
+    if out is None:
+        out = torch.empty((c, hq, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((c, hq), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, 3)
+    _need(lse, "lse", torch.float32, 2)
+    if tuple(out.shape) != (c, hq, d) or tuple(lse.shape) != (c, hq):
+        raise ValueError("out must be [C][Hq][D] and lse [C][Hq]")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, 1)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
+    _check(lib().mtd_attn_prefill_chunk_cus(ctypes.byref(layer), q.data_ptr(), c, int(prefix_len),
+                                            block_table.data_ptr(), block_table.shape[0], hq, float(scale),
+                                            ws_ptr, ws_bytes, int(cu_budget), out.data_ptr(), lse.data_ptr(),
+                                            _stream()))
     return out, lse
 
 

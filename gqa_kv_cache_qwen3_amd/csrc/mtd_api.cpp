@@ -116,10 +116,10 @@ int mtd_kv_append(const mtd_kv_layer_t* kv, const void* k_new, const void* v_new
                     "kv_append launch");
 }
 
-int mtd_attn_prefill_chunk(const mtd_kv_layer_t* kv, const void* q, int32_t chunk_len,
-                           int32_t prefix_len, const int32_t* block_table, int32_t block_table_len,
-                           int32_t num_q_heads, float scale, void* workspace, size_t workspace_bytes,
-                           float* out, float* lse, void* stream) {
+int mtd_attn_prefill_chunk_cus(const mtd_kv_layer_t* kv, const void* q, int32_t chunk_len,
+                               int32_t prefix_len, const int32_t* block_table, int32_t block_table_len,
+                               int32_t num_q_heads, float scale, void* workspace, size_t workspace_bytes,
+                               int32_t cu_budget, float* out, float* lse, void* stream) {
   int st = check_layer(kv);
   if (st != MTD_OK) return st;
   if ((st = check_heads(num_q_heads, kv->num_kv_heads)) != MTD_OK) return st;
@@ -130,6 +130,7 @@ int mtd_attn_prefill_chunk(const mtd_kv_layer_t* kv, const void* q, int32_t chun
     return fail(MTD_ERR_INVALID_ARG, "q / out / workspace not 16-byte aligned");
   if (chunk_len <= 0) return fail(MTD_ERR_INVALID_ARG, "chunk_len = %d", chunk_len);
   if (prefix_len < 0) return fail(MTD_ERR_INVALID_ARG, "prefix_len = %d", prefix_len);
+  if (cu_budget < 0) return fail(MTD_ERR_INVALID_ARG, "cu_budget = %d", cu_budget);
   const int64_t total = (int64_t)prefix_len + chunk_len;
   if (total > MTD_MAX_CONTEXT)
     return fail(MTD_ERR_CAPACITY, "prefix_len + chunk_len = %lld exceeds %d", (long long)total,
@@ -141,10 +142,20 @@ int mtd_attn_prefill_chunk(const mtd_kv_layer_t* kv, const void* q, int32_t chun
   if (workspace != nullptr && workspace_bytes < mtd::prefill_workspace_bytes(chunk_len))
     return fail(MTD_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes,
                 mtd::prefill_workspace_bytes(chunk_len));
+  if (cu_budget > 0 && workspace == nullptr)
+    return fail(MTD_ERR_WORKSPACE, "a CU budget (%d) needs the workspace", cu_budget);
   return hip_status(mtd::launch_prefill(pools(kv), static_cast<const uint16_t*>(q), chunk_len,
-                                        prefix_len, block_table, scale, workspace, out, lse,
+                                        prefix_len, block_table, scale, workspace, cu_budget, out, lse,
                                         static_cast<hipStream_t>(stream)),
                     "prefill launch");
+}
+
+int mtd_attn_prefill_chunk(const mtd_kv_layer_t* kv, const void* q, int32_t chunk_len,
+                           int32_t prefix_len, const int32_t* block_table, int32_t block_table_len,
+                           int32_t num_q_heads, float scale, void* workspace, size_t workspace_bytes,
+                           float* out, float* lse, void* stream) {
+  return mtd_attn_prefill_chunk_cus(kv, q, chunk_len, prefix_len, block_table, block_table_len,
+                                    num_q_heads, scale, workspace, workspace_bytes, 0, out, lse, stream);
 }
 
 size_t mtd_attn_prefill_workspace_bytes(int32_t chunk_len, int32_t num_q_heads, int32_t head_dim) {

@@ -56,9 +56,11 @@ inline size_t prefill_workspace_bytes(int chunk_len) {
   return (size_t)chunk_len * kQHeads * (kHeadDim + 1) * sizeof(float);
 }
 
+// cu_budget: 0 = the whole device; else (with a workspace) the call's work is spread over
+// cu_budget / 8 workgroups per KV head, leaving the other CUs free.
 hipError_t launch_prefill(const KvPools& kv, const uint16_t* q, int chunk_len, int prefix_len,
-                          const int32_t* block_table, float scale, void* workspace, float* out,
-                          float* lse, hipStream_t stream);
+                          const int32_t* block_table, float scale, void* workspace, int cu_budget,
+                          float* out, float* lse, hipStream_t stream);
 
 // Workspace layout of the decode: partial O float32 [max_parts][kQHeads][kHeadDim], then partial
 // LSE float32 [max_parts][kQHeads], max_parts = batch * split_parts_bound(max_kv_len).

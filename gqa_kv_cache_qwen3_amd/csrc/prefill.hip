@@ -308,12 +308,28 @@ enum PrefillMode : int {
   kOnePass = 0,  // one workgroup per item, longest first
   kHalves = 1,   // two workgroups per item, one per half of its key tiles
   kPairs = 2,    // items t and T-1-t share two workgroups with equal key-tile counts
+  kSpread = 3,   // each KV head's items, longest first, laid end to end and cut into P equal ranges
 };
 
 // Key tiles of position tile qt: every key up to the tile's last position.
-__device__ __forceinline__ int item_tiles(int qt, int chunk_len, int prefix_len) {
+__host__ __device__ __forceinline__ int item_tiles(int qt, int chunk_len, int prefix_len) {
   const int kv_end = min(prefix_len + (qt + 1) * kBQ, prefix_len + chunk_len);
   return (kv_end + kBK - 1) / kBK;
+}
+
+// kSpread: a KV head's items in the order T-1, T-2, .., 0 (longest first) laid end to end; item t
+// starts at key tile item_start(t) of that sequence (item_start(-1) is the total).  Every item but
+// the last has ceil(P / 64) + 2 (t + 1) key tiles (P the prefix), so the sum has a closed form.
+__host__ __device__ __forceinline__ long long item_start(int t, int n_qtiles, int chunk_len, int prefix_len) {
+  if (t >= n_qtiles - 1) return 0;
+  const long long m = n_qtiles - 2 - t;  // items strictly between t and the last one
+  const long long a = (prefix_len + kBK - 1) / kBK;
+  return item_tiles(n_qtiles - 1, chunk_len, prefix_len) + m * a + (long long)(n_qtiles + t + 1) * m;
+}
+
+// Workgroup (of the P per KV head) whose range [j W / P, (j+1) W / P) holds key tile x.
+__host__ __device__ __forceinline__ int spread_owner(long long x, int spread, long long total) {
+  return (int)(((x + 1) * spread - 1) / total);
 }
 
 // kPairs: pair p joins the long tile T-1-p (L key tiles) and the short tile p (S tiles; none when
@@ -346,7 +362,7 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
     const uint16_t* __restrict__ q, int chunk_len, int prefix_len,
     const int32_t* __restrict__ block_table, float scale_log2, float* __restrict__ out,
     float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse, int n_qtiles,
-    int mode) {
+    int mode, int spread) {
   // Three stages of (K, V) tiles, 96 KiB: the tile being read, the next tile (in flight, then
   // read from the middle of the current step on) and the stage the following DMA refills.
   // Separate arrays, so the compiler can see that the DMA into one stage never aliases the reads
@@ -370,10 +386,24 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
   const int rank = (int)(blockIdx.x / kKvHeads);
   const int total = prefix_len + chunk_len;
 
-  // This workgroup's segments (at most two, run one after the other).
+  // This workgroup's segments, run one after the other: at most two, or with kSpread every item
+  // that meets the workgroup's range of the head's key tiles.
   Segment seg0{0, 0, 0, 0}, seg1{0, 0, 0, 0};
   int n_seg = 0;
-  if (mode == kPairs) {
+  int sp_t = 0;                  // kSpread: next item (position tile) and key tile of the sequence
+  long long sp_cur = 0, sp_hi = 0;
+  if (mode == kSpread) {
+    const long long w = item_start(-1, n_qtiles, chunk_len, prefix_len);
+    sp_cur = (long long)rank * w / spread;
+    sp_hi = (long long)(rank + 1) * w / spread;
+    // first item: the smallest t with item_start(t) <= sp_cur (item_start falls as t grows)
+    int lo_t = 0, hi_t = n_qtiles - 1;
+    while (lo_t < hi_t) {
+      const int mid = (lo_t + hi_t) >> 1;
+      if (item_start(mid, n_qtiles, chunk_len, prefix_len) <= sp_cur) hi_t = mid; else lo_t = mid + 1;
+    }
+    sp_t = lo_t;
+  } else if (mode == kPairs) {
     const PairPlan pp = pair_plan(rank >> 1, n_qtiles, chunk_len, prefix_len);
     const bool split_long = pp.cut > 0 && pp.cut < pp.n_long;
     if ((rank & 1) == 0) {
@@ -406,13 +436,30 @@ __global__ __launch_bounds__(512, 1) void prefill_kernel(
   }
 
   const LdsOffsets off = make_offsets(lane);
-  for (int si = 0; si < n_seg; ++si) {
+  for (int si = 0;; ++si) {
+    Segment seg;
+    if (mode == kSpread) {
+      // Item sp_t from key tile sp_cur on, up to the end of the item or of the range.  An item
+      // cut by a range boundary has two parts (no item is longer than a range): the part holding
+      // its first tile goes to the workspace, the other to out.
+      if (sp_cur >= sp_hi || sp_t < 0) break;
+      const long long f = item_start(sp_t, n_qtiles, chunk_len, prefix_len);
+      const int n_item = item_tiles(sp_t, chunk_len, prefix_len);
+      const int a = (int)(sp_cur - f);
+      const int b = (int)min(sp_hi - f, (long long)n_item);
+      seg = Segment{sp_t, a, b, a == 0 && b < n_item ? 1 : 0};
+      sp_cur = f + b;
+      --sp_t;
+    } else {
+      if (si >= n_seg) break;
+      seg = si == 0 ? seg0 : seg1;
+    }
     if (si > 0) __syncthreads();  // every wave is done with the previous segment's LDS stages
     // Uniform across the workgroup: keep the segment in scalar registers.
-    const int qt = __builtin_amdgcn_readfirstlane(si == 0 ? seg0.qt : seg1.qt);
-    const int t0 = __builtin_amdgcn_readfirstlane(si == 0 ? seg0.t0 : seg1.t0);
-    const int t1 = __builtin_amdgcn_readfirstlane(si == 0 ? seg0.t1 : seg1.t1);
-    const int half = __builtin_amdgcn_readfirstlane(si == 0 ? seg0.to_ws : seg1.to_ws);
+    const int qt = __builtin_amdgcn_readfirstlane(seg.qt);
+    const int t0 = __builtin_amdgcn_readfirstlane(seg.t0);
+    const int t1 = __builtin_amdgcn_readfirstlane(seg.t1);
+    const int half = __builtin_amdgcn_readfirstlane(seg.to_ws);
     const int q0 = qt * kBQ;
     const int qpos = q0 + 16 * wave + (n & 15);
     const int head = kGroup * g + (n >> 4);
@@ -568,7 +615,7 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(float* __restrict__ 
                                                             const float* __restrict__ part_o,
                                                             const float* __restrict__ part_lse,
                                                             int chunk_len, int prefix_len, int n_qtiles,
-                                                            int mode, int row0) {
+                                                            int mode, int spread, int row0) {
   const int row = row0 + (int)blockIdx.x * 8 + (int)(threadIdx.x >> 5);  // (position, head)
   const int lane = threadIdx.x & 31;
   if (row >= chunk_len * kQHeads) return;
@@ -578,6 +625,11 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(float* __restrict__ 
     if (p > qt) return;               // qt is a short tile: never split
     const PairPlan pp = pair_plan(p, n_qtiles, chunk_len, prefix_len);
     if (pp.cut <= 0 || pp.cut >= pp.n_long) return;  // not split: out/lse are final
+  } else if (mode == kSpread) {
+    const long long w = item_start(-1, n_qtiles, chunk_len, prefix_len);
+    const long long f = item_start(qt, n_qtiles, chunk_len, prefix_len);
+    const int n_item = item_tiles(qt, chunk_len, prefix_len);
+    if (spread_owner(f, spread, w) == spread_owner(f + n_item - 1, spread, w)) return;  // one part
   } else if (item_tiles(qt, chunk_len, prefix_len) < 2) {
     return;  // item was not split: out/lse are final
   }
@@ -615,32 +667,50 @@ int device_cus() {
 }
 
 hipError_t launch_prefill(const KvPools& kv, const uint16_t* q, int chunk_len, int prefix_len,
-                          const int32_t* block_table, float scale, void* workspace, float* out,
-                          float* lse, hipStream_t stream) {
+                          const int32_t* block_table, float scale, void* workspace, int cu_budget,
+                          float* out, float* lse, hipStream_t stream) {
   const int n_qtiles = (chunk_len + kBQ - 1) / kBQ;
   // Causal work is uneven over a chunk's position tiles (the last sees prefix + chunk keys, the
   // first only prefix), and with one workgroup per CU the time is set by the longest.  With a
   // workspace the library rebalances:
-  //   - at least as many items as CUs: pair tile t with tile T-1-t and cut their combined key
+  //   - a CU budget below the device's CUs: each KV head's work is cut into budget / 8 equal
+  //     ranges, one workgroup each, so the call occupies only that many CUs (the rest stay free for
+  //     concurrent work); the number of ranges is lowered until no item is longer than a range;
+  //   - else, at least as many items as CUs: pair tile t with tile T-1-t and cut their combined key
   //     tiles into two equal workgroups (the long tile's two parts merged afterwards);
-  //   - fewer items than CUs (short chunks): split every item's keys in two halves, which also
-  //     doubles the workgroups.
-  // Both cost the merge pass over the split rows.  Without a workspace, one pass per item.
-  int mode = kOnePass;
-  if (workspace != nullptr) mode = n_qtiles * kKvHeads >= device_cus() ? kPairs : kHalves;
-  const int n_wg = mode == kPairs ? 2 * ((n_qtiles + 1) / 2) : mode == kHalves ? 2 * n_qtiles : n_qtiles;
+  //   - else (short chunks): split every item's keys in two halves, which also doubles the
+  //     workgroups.
+  // All cost the merge pass over the split rows.  Without a workspace, one pass per item.
+  const int cus = device_cus();
+  int mode = kOnePass, spread = 0;
+  if (workspace != nullptr) {
+    if (cu_budget > 0 && cu_budget < cus) {
+      mode = kSpread;
+      const long long w = item_start(-1, n_qtiles, chunk_len, prefix_len);
+      const long long longest = item_tiles(n_qtiles - 1, chunk_len, prefix_len);
+      spread = max(1, cu_budget / kKvHeads);
+      spread = (int)min((long long)spread, w / longest);  // every item fits in one range
+      spread = max(spread, 1);
+    } else {
+      mode = n_qtiles * kKvHeads >= cus ? kPairs : kHalves;
+    }
+  }
+  const int n_wg = mode == kSpread ? spread
+                   : mode == kPairs ? 2 * ((n_qtiles + 1) / 2)
+                   : mode == kHalves ? 2 * n_qtiles
+                                     : n_qtiles;
   float* part_o = static_cast<float*>(workspace);
   float* part_lse = mode != kOnePass ? part_o + (size_t)chunk_len * kQHeads * kHeadDim : nullptr;
   prefill_kernel<<<dim3(n_wg * kKvHeads), dim3(64 * kWaves), 0, stream>>>(
       kv.k, kv.v, kv.num_pages, q, chunk_len, prefix_len, block_table, scale * kLog2e, out, lse,
-      part_o, part_lse, n_qtiles, mode);
+      part_o, part_lse, n_qtiles, mode, spread);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || mode == kOnePass) return err;
   // Only long tiles are split on the pair schedule: they start at tile T/2.
   const int rows = chunk_len * kQHeads;
   const int row0 = mode == kPairs ? (n_qtiles / 2) * kBQ * kQHeads : 0;
   prefill_merge_kernel<<<dim3((rows - row0 + 7) / 8), dim3(256), 0, stream>>>(
-      out, lse, part_o, part_lse, chunk_len, prefix_len, n_qtiles, mode, row0);
+      out, lse, part_o, part_lse, chunk_len, prefix_len, n_qtiles, mode, spread, row0);
   return hipGetLastError();
 }
 

@@ -70,7 +70,7 @@
 extern "C" {
 #endif
 
-#define MTD_ABI_VERSION 6
+#define MTD_ABI_VERSION 7
 
 /* Status codes. */
 #define MTD_OK               0
@@ -152,6 +152,29 @@ int mtd_attn_prefill_chunk(const mtd_kv_layer_t* kv, const void* q, int32_t chun
                            int32_t prefix_len, const int32_t* block_table, int32_t block_table_len,
                            int32_t num_q_heads, float scale, void* workspace, size_t workspace_bytes,
                            float* out, float* lse, void* stream);
+
+/*
+ * mtd_attn_prefill_chunk_cus - mtd_attn_prefill_chunk on a budget of compute units, so that other
+ * work of the same scheduler step can run beside it.
+ *
+ * The scheduler interleaves other requests' decode with the chunks of a long prompt ("Optimizing
+ * ASR Models ...", section Chunked Prefill for Long Audio).  Prefill is bound by the matrix units
+ * and decode by HBM, so the two overlap well only on separate compute units: with cu_budget > 0
+ * (and below the device's CU count) and a workspace, each KV head's causal work (its position
+ * tiles' key tiles, longest tile first, laid end to end) is cut into cu_budget / 8 equal ranges,
+ * one workgroup of one CU each (fewer if a range would be shorter than a tile's keys), and tiles
+ * cut by a range boundary are merged by log-sum-exp as in the other schedules.  The call then
+ * occupies at most cu_budget CUs and leaves the rest free for work launched on another stream.
+ *
+ *   cu_budget   0: the whole device (exactly mtd_attn_prefill_chunk);  > 0: needs the workspace
+ *               (else MTD_ERR_WORKSPACE);  < 0: MTD_ERR_INVALID_ARG
+ * Every other argument, result and error is that of mtd_attn_prefill_chunk; results are correct
+ * for every budget (their bits differ between schedules).
+ */
+int mtd_attn_prefill_chunk_cus(const mtd_kv_layer_t* kv, const void* q, int32_t chunk_len,
+                               int32_t prefix_len, const int32_t* block_table, int32_t block_table_len,
+                               int32_t num_q_heads, float scale, void* workspace, size_t workspace_bytes,
+                               int32_t cu_budget, float* out, float* lse, void* stream);
 
 /*
  * mtd_attn_prefill_workspace_bytes - size of the optional mtd_attn_prefill_chunk workspace:

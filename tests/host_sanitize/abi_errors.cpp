@@ -20,8 +20,8 @@ namespace mtd {
 }
 hipError_t launch_kv_append(const KvPools&, const uint16_t*, const uint16_t*, const int32_t*, const int32_t*,
                             const int32_t*, int, int, int, hipStream_t) { reached("kv_append"); }
-hipError_t launch_prefill(const KvPools&, const uint16_t*, int, int, const int32_t*, float, void*, float*, float*,
-                          hipStream_t) { reached("prefill"); }
+hipError_t launch_prefill(const KvPools&, const uint16_t*, int, int, const int32_t*, float, void*, int, float*,
+                          float*, hipStream_t) { reached("prefill"); }
 hipError_t launch_decode(const KvPools&, const uint16_t*, const int32_t*, const int32_t*, int, int, int, float,
                          void*, float*, float*, hipStream_t) { reached("decode"); }
 hipError_t launch_qkv_proj(const uint16_t*, const uint16_t*, int, uint16_t*, uint16_t*, uint16_t*, hipStream_t) {
@@ -102,6 +102,11 @@ int main() {
          "prefill: workspace small");
   expect(mtd_attn_prefill_chunk(&kv, P, 100, 0, I, 2, 16, 0.088f, odd, 1 << 30, F, F, nullptr), MTD_ERR_INVALID_ARG,
          "prefill: workspace unaligned");
+
+  expect(mtd_attn_prefill_chunk_cus(&kv, P, 100, 0, I, 2, 16, 0.088f, P, 1 << 30, -1, F, F, nullptr),
+         MTD_ERR_INVALID_ARG, "prefill_cus: negative budget");
+  expect(mtd_attn_prefill_chunk_cus(&kv, P, 100, 0, I, 2, 16, 0.088f, nullptr, 0, 64, F, F, nullptr),
+         MTD_ERR_WORKSPACE, "prefill_cus: budget without workspace");
 
   // decode and its allocation-free variant
   expect(mtd_attn_decode(&kv, P, I, I, 16, 2, 1000, 16, 0.088f, nullptr, 0, F, F, nullptr), MTD_ERR_WORKSPACE,

@@ -328,6 +328,30 @@ def test_merge_validation(lib, kw, code):
     assert lib.mtd_last_error().decode() != ""
 
 
+def prefill_cus(lib, kv=None, **kw):
+    a = dict(q=FAKE, chunk=10, prefix=0, bt=FAKE, bt_len=4, hq=16, scale=0.088, ws=FAKE, ws_bytes=1 << 30,
+             cus=64, out=FAKE, lse=FAKE)
+    a.update(kw)
+    return lib.mtd_attn_prefill_chunk_cus(ctypes.byref(kv or layer()), a["q"], a["chunk"], a["prefix"], a["bt"],
+                                          a["bt_len"], a["hq"], a["scale"], a["ws"], a["ws_bytes"], a["cus"],
+                                          a["out"], a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cus=-1), mtd.MTD_ERR_INVALID_ARG),
+    (dict(ws=None, ws_bytes=0), mtd.MTD_ERR_WORKSPACE),            # a budget needs the workspace
+    (dict(ws_bytes=100), mtd.MTD_ERR_WORKSPACE),
+    (dict(chunk=0), mtd.MTD_ERR_INVALID_ARG),
+    (dict(prefix=131072), mtd.MTD_ERR_CAPACITY),
+    (dict(bt_len=0), mtd.MTD_ERR_CAPACITY),
+    (dict(hq=8), mtd.MTD_ERR_UNSUPPORTED),
+    (dict(q=None), mtd.MTD_ERR_INVALID_ARG),
+])
+def test_prefill_cus_validation(lib, kw, code):
+    assert prefill_cus(lib, **kw) == code
+    assert lib.mtd_last_error().decode() != ""
+
+
 def decode_noalloc(lib, kv=None, **kw):
     a = dict(q=FAKE, lens=FAKE, bt=FAKE, stride=2048, batch=2, max_len=1000, hq=16, scale=0.088, out=FAKE,
              lse=FAKE)

@@ -26,9 +26,11 @@ mtd = pytest.importorskip("gqa_kv_cache_qwen3_amd")
 class Request:
     """One request's paged KV, filled through mtd_kv_append (the path under test)."""
 
-    def __init__(self, total: int, tag: int, lowrank: bool = False, spare: int = 2, split: bool = False):
+    def __init__(self, total: int, tag: int, lowrank: bool = False, spare: int = 2, split: bool = False,
+                 cu_budget: int = 0):
         self.total = total
-        self.split = split
+        self.split = split or cu_budget > 0
+        self.cu_budget = cu_budget
         tables, self.num_pages, self.spare = W.place_pages([total], tag, 0, spare=spare)
         self.table_np = tables[0]
         self.table = torch.as_tensor(self.table_np, device="cuda")
@@ -58,8 +60,12 @@ class Request:
         ws = None
         if self.split:
             ws = torch.empty(mtd.prefill_workspace_bytes(chunk), dtype=torch.uint8, device="cuda")
-        out, lse = mtd.mtd_attn_prefill_chunk(self.k, self.v, self.q_log[prefix:prefix + chunk].contiguous(),
-                                              prefix, self.table, W.SCALE, workspace=ws)
+        q = self.q_log[prefix:prefix + chunk].contiguous()
+        if self.cu_budget:
+            out, lse = mtd.mtd_attn_prefill_chunk_cus(self.k, self.v, q, prefix, self.table, W.SCALE, ws,
+                                                      self.cu_budget)
+        else:
+            out, lse = mtd.mtd_attn_prefill_chunk(self.k, self.v, q, prefix, self.table, W.SCALE, workspace=ws)
         torch.cuda.synchronize()
         return out, lse
 
@@ -234,3 +240,20 @@ def test_prefill_deterministic_and_placement_invariant(split):
     b.table = torch.as_tensor(b.table_np, device="cuda")
     o3, l3 = b.prefill(1000, 4000)
     assert torch.equal(o1, o3) and torch.equal(l1, l3)
+
+
+@pytest.mark.parametrize("cu_budget", [8, 64, 120, 240, 248])
+@pytest.mark.parametrize("prefix,chunk", [(0, 439), (4096, 4096), (100, 4200), (0, 8192), (32768, 4096),
+                                          (65536, 1964)])
+def test_prefill_on_a_cu_budget(prefix, chunk, cu_budget, oracle_pool):
+    """The spread schedule (mtd_attn_prefill_chunk_cus): each KV head's key tiles cut into
+    cu_budget / 8 equal ranges, tiles cut by a range boundary merged; every row against the
+    oracle, and the same bits on a second call."""
+    log(f"prefill on a budget of {cu_budget} CUs: prefix={prefix} chunk={chunk}")
+    req = Request(prefix + chunk, 500 + prefix % 997 + chunk, cu_budget=cu_budget)
+    out, lse = req.prefill(prefix, chunk)
+    out2, lse2 = req.prefill(prefix, chunk)
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    kc, vc, ident = request_pages_host(req.k, req.v, req.table_np, prefix + chunk)
+    o_ref, l_ref = full_reference(oracle_pool, bits(req.q_log[prefix:prefix + chunk]), kc, vc, ident, prefix)
+    compare(out, lse, o_ref, l_ref, f"prefill P={prefix} C={chunk} on {cu_budget} CUs")
