@@ -39,6 +39,8 @@
 // the host picks the split whose replicated operand is the smaller.  Within an XCD the owned
 // index varies fastest, so the workgroups in flight together touch few tiles of the replicated
 // operand and each is brought into the XCD's L2 once rather than once per owned row.
+#include <type_traits>
+
 #include "device_util.h"
 #include "mtd_internal.h"
 
@@ -139,9 +141,19 @@ __global__ __launch_bounds__(kThreads, 2) void proj_gemm_kernel(const void* __re
   const int x = id % 8, local = id / 8;
   int tm, tn;
   if (rows_major) {
-    const int m_per = (n_tm + 7) / 8;
-    tm = x + 8 * (local % m_per);
-    tn = local / m_per;
+    // Whole tile rows as above; a last, partly filled tile row is dealt out by columns over the
+    // XCDs instead (tile column x, x + 8, ...), after the XCD's whole rows, so that no XCD holds
+    // one tile row more than the others.
+    const int n_full = rows / kTM;
+    const int m_per = (n_full + 7) / 8;
+    if (local < m_per * n_tn) {
+      tm = x + 8 * (local % m_per);
+      tn = local / m_per;
+      if (tm >= n_full) tm = n_tm;  // a padding row: exit below
+    } else {
+      tm = n_full;                  // == n_tm only when there is no partial row: exit below
+      tn = x + 8 * (local - m_per * n_tn);
+    }
   } else if (n_tn % 8 == 0) {
     tn = x * (n_tn / 8) + local % (n_tn / 8);
     tm = local / (n_tn / 8);
@@ -182,8 +194,12 @@ __global__ __launch_bounds__(kThreads, 2) void proj_gemm_kernel(const void* __re
     else
       dma_slice(static_cast<const uint16_t*>(a_ptr), lda, row0, rows_valid, kt * kTK, a_dst, wave, lane);
   };
-  // K step kt: stage (cur_a, cur_w) holds slice kt; slice kt+1 goes to (nxt_a, nxt_w).
-  auto step = [&](int kt, const uint8_t* cur_a, const uint8_t* cur_w, uint8_t* nxt_a, uint8_t* nxt_w) {
+  // K step kt: stage (cur_a, cur_w) holds slice kt; slice kt+1 goes to (nxt_a, nxt_w).  In a
+  // partly filled tile (kPartial) a wave skips the MFMAs of its 32-row blocks that hold no token.
+  const int live_rows = rows_valid - 64 * wm;  // rows of this wave's 64 that hold a token
+  auto step = [&](auto partial, int kt, const uint8_t* cur_a, const uint8_t* cur_w, uint8_t* nxt_a,
+                  uint8_t* nxt_w) {
+    constexpr bool kPartial = decltype(partial)::value;
     __syncthreads();  // the current stage complete for every wave; the other no longer read
     if (kt + 1 < nk) issue(kt + 1, nxt_a, nxt_w);
 #pragma unroll
@@ -197,10 +213,12 @@ __global__ __launch_bounds__(kThreads, 2) void proj_gemm_kernel(const void* __re
                                                  cur_w + wbase[ks & 1] + 8192 * (ks >> 1) + 2048 * i));
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 2; ++i) {
+        if (kPartial && live_rows <= 32 * i) continue;
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], wf[j], acc[i][j], 0, 0, 0);
+      }
     }
     if constexpr (kAF32)
       if (kt + 1 < nk) store_f32_slice(fa, nxt_a, wave, lane);
@@ -219,9 +237,17 @@ __global__ __launch_bounds__(kThreads, 2) void proj_gemm_kernel(const void* __re
 
   issue(0, s_a0, s_w0);
   if constexpr (kAF32) store_f32_slice(fa, s_a0, wave, lane);
-  for (int kt = 0; kt < nk; kt += 2) {
-    step(kt, s_a0, s_w0, s_a1, s_w1);
-    step(kt + 1, s_a1, s_w1, s_a0, s_w0);
+  // (The float32-A kernel runs every tile whole: the second loop would not fit its registers.)
+  if (kAF32 || rows_valid == kTM) {
+    for (int kt = 0; kt < nk; kt += 2) {
+      step(std::false_type{}, kt, s_a0, s_w0, s_a1, s_w1);
+      step(std::false_type{}, kt + 1, s_a1, s_w1, s_a0, s_w0);
+    }
+  } else if constexpr (!kAF32) {
+    for (int kt = 0; kt < nk; kt += 2) {
+      step(std::true_type{}, kt, s_a0, s_w0, s_a1, s_w1);
+      step(std::true_type{}, kt + 1, s_a1, s_w1, s_a0, s_w0);
+    }
   }
 
   // Epilogue: accumulator element v of block (i, j) is C[row0 + 64wm + 32i + 8(v/4) + 4hk + v%4]
@@ -360,9 +386,14 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void proj_skinny_kernel(
   }
 }
 
-// Workgroups launched for n_tm x n_tn tiles (rows owned by XCD: padded to whole groups of 8 rows).
-int grid_tiles(int n_tm, int n_tn, int rows_major) {
-  return rows_major ? 8 * ((n_tm + 7) / 8) * n_tn : n_tm * n_tn;
+// Workgroups launched for the tiles of `rows` rows x n_tn tile columns.  Rows owned by XCD: whole
+// tile rows padded to groups of 8, plus a partly filled last row dealt out over the XCDs by column.
+int grid_tiles(int rows, int n_tn, int rows_major) {
+  const int n_tm = (rows + kTM - 1) / kTM;
+  if (!rows_major) return n_tm * n_tn;
+  const int n_full = rows / kTM;
+  const int tail = n_tm > n_full ? (n_tn + 7) / 8 : 0;
+  return 8 * (((n_full + 7) / 8) * n_tn + tail);
 }
 
 // The operand split (see Placement) that reads fewer bytes.
@@ -392,7 +423,7 @@ hipError_t launch_qkv_proj(const uint16_t* x, const uint16_t* w_qkv, int n_tok, 
     return hipGetLastError();
   }
   const int rows_major = rows_major_split(n_tok, kHidden * 2, (size_t)kN * kHidden * 2);
-  proj_gemm_kernel<false><<<dim3(grid_tiles(n_tm, n_tn, rows_major)), dim3(kThreads), 0, stream>>>(
+  proj_gemm_kernel<false><<<dim3(grid_tiles(n_tok, n_tn, rows_major)), dim3(kThreads), 0, stream>>>(
       x, kHidden, n_tok, w_qkv, kHidden, n_tm, n_tn, rows_major, om);
   return hipGetLastError();
 }
@@ -414,7 +445,7 @@ hipError_t launch_o_proj(const float* attn, const uint16_t* w_o, int n_tok, uint
     return hipGetLastError();
   }
   const int rows_major = rows_major_split(n_tok, kK * 4, (size_t)kHidden * kK * 2);
-  proj_gemm_kernel<true><<<dim3(grid_tiles(n_tm, n_tn, rows_major)), dim3(kThreads), 0, stream>>>(
+  proj_gemm_kernel<true><<<dim3(grid_tiles(n_tok, n_tn, rows_major)), dim3(kThreads), 0, stream>>>(
       attn, kK, n_tok, w_o, kK, n_tm, n_tn, rows_major, om);
   return hipGetLastError();
 }
