@@ -895,6 +895,117 @@ class DecodeGraph:
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "per_launch": res["decode"]["bytes"], "ms": res["decode"]["ms"]}
 
 
+class DecodeGraphBuckets:
+    """Decode batches padded to buckets (1, 2, 4, .., 64 requests), one captured graph per bucket,
+    as a serving loop replays one graph per token: a step is 28 x (append one token per request,
+    decode) with the batch's requests first and padding requests (no token, zero keys) after them.
+    Cases: every bucket full at the tiny workload's short context (launch-bound), 12 requests in
+    the 16-bucket and 48 in the 64-bucket (padded), decode16's 16 requests of 27,000-30,000 tokens,
+    and the full-depth batch (64 requests, log-uniform up to the 128K cap).  Each case is timed as
+    eager calls and as graph replays.  The 28 layers of a case share one pool (timing only: each
+    layer's KV is larger than the caches, so the bytes moved are those of 28 separate layers)."""
+    name = "decode_graph_buckets"
+    LAYERS = 28
+
+    def __init__(self, dev):
+        import torch
+        import gqa_kv_cache_qwen3_amd as mtd
+        self.mtd, self.torch, self.dev = mtd, torch, dev
+        tiny = W.TINY.params["prompt"]
+        p16, pf = W.DECODE16.params, W.FULLDEPTH.params
+        self.cases = [(f"{b} x {tiny} tokens", b, np.full(b, tiny)) for b in (1, 2, 4, 8, 16, 32, 64)]
+        self.cases += [("12 x 439 tokens (padded to 16)", 16, np.full(12, tiny)),
+                       ("48 x 439 tokens (padded to 64)", 64, np.full(48, tiny)),
+                       ("decode16: 16 x 27k-30k tokens", 16,
+                        W.uniform_lengths(p16["batch"], p16["lo"], p16["hi"], W.DECODE16.tag, 0)),
+                       ("full-depth batch: 64 x 4k-128k tokens", 64,
+                        W.loguniform_lengths(pf["batch"], pf["lo"], W.CONTEXT_CAP - pf["steps"], W.FULLDEPTH.tag, 0))]
+        self.rows = []
+
+    def _case(self, label, bucket, lens0, steps, warmup):
+        torch, mtd, dev = self.torch, self.mtd, self.dev
+        b = len(lens0)
+        room = steps + warmup + 1
+        tables, n_pages, _ = W.place_pages(lens0 + room, 70, bucket)
+        bound = int(lens0.max()) + room
+        stride = (bound + W.PAGE - 1) // W.PAGE
+        bt = torch.zeros((bucket, stride), dtype=torch.int32, device=dev)
+        bt[:b, : tables.shape[1]] = torch.as_tensor(tables, device=dev)
+        k = torch.empty((n_pages, W.HKV, W.PAGE, W.HEAD_DIM), dtype=torch.bfloat16, device=dev)
+        v = torch.empty_like(k)
+        fill_normal_(k, W.torch_seed(70, bucket, 1))
+        fill_normal_(v, W.torch_seed(70, bucket, 2))
+        q = W.normal_bf16((self.LAYERS, bucket, W.HQ, W.HEAD_DIM), W.torch_seed(70, bucket, 3), dev)
+        kn = W.normal_bf16((self.LAYERS, bucket, W.HKV, W.HEAD_DIM), W.torch_seed(70, bucket, 4), dev)
+        vn = W.normal_bf16((self.LAYERS, bucket, W.HKV, W.HEAD_DIM), W.torch_seed(70, bucket, 5), dev)
+        cu = torch.as_tensor(np.minimum(np.arange(bucket + 1), b).astype(np.int32), device=dev)
+        pos = torch.as_tensor(np.concatenate([lens0, np.zeros(bucket - b)]).astype(np.int32), device=dev)
+        lens = torch.as_tensor(np.concatenate([lens0 + 1, np.zeros(bucket - b)]).astype(np.int32), device=dev)
+        step_add = torch.as_tensor((np.arange(bucket) < b).astype(np.int32), device=dev)
+        ws = torch.empty(mtd.decode_workspace_bytes(bucket, bound), dtype=torch.uint8, device=dev)
+        o = torch.empty((self.LAYERS, bucket, W.HQ, W.HEAD_DIM), dtype=torch.float32, device=dev)
+        lse = torch.empty((self.LAYERS, bucket, W.HQ), dtype=torch.float32, device=dev)
+
+        def calls():
+            for l in range(self.LAYERS):
+                mtd.mtd_kv_append(k, v, kn[l], vn[l], cu, pos, bt)
+                mtd.mtd_attn_decode(k, v, q[l], lens, bt, bound, W.SCALE, ws, o[l], lse[l])
+            pos.add_(step_add)
+            lens.add_(step_add)
+
+        def reset():
+            pos.copy_(torch.as_tensor(np.concatenate([lens0, np.zeros(bucket - b)]).astype(np.int32), device=dev))
+            lens.copy_(torch.as_tensor(np.concatenate([lens0 + 1, np.zeros(bucket - b)]).astype(np.int32),
+                                       device=dev))
+
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            calls()
+        out = {}
+        for use_graph in (False, True):
+            reset()
+            for _ in range(warmup):
+                graph.replay() if use_graph else calls()
+            reset()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                graph.replay() if use_graph else calls()
+            torch.cuda.synchronize()
+            out["graph_ms" if use_graph else "eager_ms"] = (time.perf_counter() - t0) * 1e3 / steps
+        step_bytes = self.LAYERS * decode_bytes(lens0 + 1 + steps // 2)
+        del graph, k, v
+        torch.cuda.empty_cache()
+        return {"case": label, "bucket": bucket, "requests": b, "kv_tokens": int(lens0.sum()),
+                "eager_ms": out["eager_ms"], "graph_ms": out["graph_ms"], "speedup": out["eager_ms"] / out["graph_ms"],
+                "graph_gbs": step_bytes / (out["graph_ms"] * 1e-3) / 1e9}
+
+    def run(self, steps, warmup):
+        t0 = time.perf_counter()
+        for label, bucket, lens0 in self.cases:
+            n = steps if int(lens0.max()) < 10000 else max(3, steps // 50)
+            self.rows.append(self._case(label, bucket, np.asarray(lens0, dtype=np.int64), n, min(warmup, n)))
+            print(f"[decode_graph_buckets] {self.rows[-1]}", file=sys.stderr, flush=True)
+        return time.perf_counter() - t0
+
+    def config(self):
+        return {"workload": "decode_graph_buckets: decode batches padded to buckets 1..64, one HIP graph per bucket, "
+                            "28 x (append, decode) per step; eager calls vs graph replays",
+                "layers": self.LAYERS, "cases": [c[0] for c in self.cases]}
+
+    def results(self):
+        d16 = [r for r in self.rows if r["case"].startswith("decode16")][0]
+        return {"decode": {"value": d16["graph_gbs"], "unit": "GB/s", "frac": d16["graph_gbs"] / HBM_PEAK_GBS,
+                           "ms": d16["graph_ms"] / self.LAYERS, "bytes": None,
+                           "kernels": "decode_split_kernel + decode_merge_kernel (decode16 in its bucket, graph)"},
+                "buckets": self.rows}
+
+    def dominant(self, res):
+        return {"kernel": "decode_split_kernel+decode_merge_kernel", "bound": "hbm", "achieved": res["decode"]["value"],
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "per_launch": None, "ms": res["decode"]["ms"]}
+
+
 class DecodeGraphBlock(DecodeGraph):
     """decode_graph with the projections: per layer the QKV projection of the request's hidden state,
     the append of its new K/V, decode attention and the output projection, whose result is the next
@@ -942,7 +1053,8 @@ class DecodeGraphBlock(DecodeGraph):
 
 
 WORKLOAD_CLASSES = {c.name: c for c in (MixedStep, MixedStepOverlap, MixedBlock, Decode16, Decode16SeqSplit, Prefill90,
-                                         FullDepth, FullDepthBlock, DecodeGraph, DecodeGraphBlock)}
+                                         FullDepth, FullDepthBlock, DecodeGraph, DecodeGraphBlock,
+                                         DecodeGraphBuckets)}
 
 
 def calibrate_copy():
@@ -1050,7 +1162,7 @@ def ceiling(dev, dec16, copy_bytes=4 << 30, reps=10):
 
 
 # Untimed steps per workload, each about 50 ms of GPU work or more.
-WARMUP_DEFAULT = {"mixed_step": 40, "mixed_step_overlap": 40, "mixed_block": 40, "decode16": 500,
+WARMUP_DEFAULT = {"decode_graph_buckets": 20, "mixed_step": 40, "mixed_step_overlap": 40, "mixed_block": 40, "decode16": 500,
                   "prefill90min": 3, "fulldepth_decode": 5, "fulldepth_block": 5, "decode_graph": 200,
                   "decode_graph_block": 200, "decode16_seqsplit": 2000}
 
@@ -1074,7 +1186,7 @@ def main():
 
     if args.steps is None:
         args.steps = {"fulldepth_decode": 128, "fulldepth_block": 128, "decode_graph": 500,
-                      "decode_graph_block": 500}.get(args.workload, 20)
+                      "decode_graph_block": 500, "decode_graph_buckets": 200}.get(args.workload, 20)
     if args.warmup is None:
         # From idle the shader clock needs about 20 ms of sustained work to reach its steady level
         # (measured on MI355X); the default warmup covers that with margin.
@@ -1092,7 +1204,7 @@ def main():
 
     wl = WORKLOAD_CLASSES[args.workload](dev)
     torch.cuda.synchronize()
-    if not isinstance(wl, DecodeGraph):
+    if not isinstance(wl, (DecodeGraph, DecodeGraphBuckets)):
         for _ in range(args.warmup):
             wl.step()
     torch.cuda.synchronize()
@@ -1101,7 +1213,7 @@ def main():
 
     # timed region: exactly K steps between synchronisations; per-call events inside
     t0 = time.perf_counter()
-    if isinstance(wl, DecodeGraph):
+    if isinstance(wl, (DecodeGraph, DecodeGraphBuckets)):
         wall = wl.run(args.steps, args.warmup)  # warm-up and the eager passes happen inside; graph pass timed
     elif isinstance(wl, FullDepth):
         step_events = []
@@ -1163,6 +1275,9 @@ def main():
     for k in ("decode", "prefill", "append", "step"):
         if k in res:
             line[k] = {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in res[k].items()}
+    if "buckets" in res:
+        line["buckets"] = [{kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in r.items()}
+                           for r in res["buckets"]]
     if "proj" in res:
         line["proj"] = {name: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in d.items()}
                         for name, d in res["proj"].items()}

@@ -19,12 +19,14 @@ __global__ __launch_bounds__(128) void kv_append_kernel(
     const int32_t* __restrict__ block_tables, int bt_stride, int n_req) {
   const int t = blockIdx.x;
   // Owner of token t: the request r with cu_new[r] <= t < cu_new[r+1] (binary search; empty
-  // requests, where cu_new[r] == cu_new[r+1], are skipped).
+  // requests, where cu_new[r] == cu_new[r+1], are skipped).  A token no request owns (at or past
+  // cu_new[n_req], as in a batch padded to a fixed size) is not written.
   int lo = 0, hi = n_req;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
     if (cu_new[mid] <= t) lo = mid; else hi = mid;
   }
+  if (t < cu_new[lo] || t >= cu_new[lo + 1]) return;
   const int pos = start_pos[lo] + (t - cu_new[lo]);
   if (pos < 0 || pos >= kMaxContext) return;
   const int entry = pos / kPage;

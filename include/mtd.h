@@ -103,8 +103,10 @@ typedef struct mtd_kv_layer {
  *   kv          host pointer to the layer's pools (pools are modified in place)
  *   k_new       bf16 [n_new][num_kv_heads][head_dim], the new keys, requests back to back
  *   v_new       bf16 [n_new][num_kv_heads][head_dim], the new values
- *   cu_new      int32 [n_req + 1], cu_new[0] = 0, nondecreasing, cu_new[n_req] = n_new: request r
- *               owns new rows cu_new[r] .. cu_new[r+1]-1
+ *   cu_new      int32 [n_req + 1], cu_new[0] = 0, nondecreasing, cu_new[n_req] <= n_new: request r
+ *               owns new rows cu_new[r] .. cu_new[r+1]-1; rows at or past cu_new[n_req] belong to
+ *               no request and are not written (a batch padded to a fixed size, as in a captured
+ *               graph serving fewer requests than it was captured for)
  *   start_pos   int32 [n_req], logical position of request r's first new token
  *   block_tables, bt_stride   int32 [n_req][bt_stride]; entry (start_pos[r] + i) / page_size of
  *               row r must be valid for every new token i of request r

@@ -95,3 +95,25 @@ def test_append_many_requests():
     tables, n_pages, _ = W.place_pages(final, 78, 0)
     kp, vp = new_pool(n_pages, "cuda"), new_pool(n_pages, "cuda")
     check_append(kp, vp, counts, starts, tables, 900)
+
+
+def test_append_padded_batch_writes_only_owned_rows():
+    """A batch padded to 16 rows for 11 real requests (one token each, then four padding requests
+    with no token): rows 11..15 of k_new / v_new belong to no request and must not be written; the
+    pool equals the oracle's, which writes only the rows cu_new assigns."""
+    lens = W.loguniform_lengths(11, 10, 3000, 91, 0)
+    tables, n_pages, _ = W.place_pages(lens + 1, 91, 1)
+    tb = np.zeros((16, tables.shape[1]), dtype=np.int32)
+    tb[:11] = tables                       # padding rows point at page 0, which holds real tokens
+    kp, vp = new_pool(n_pages, "cuda", W.torch_seed(91, 2)), new_pool(n_pages, "cuda", W.torch_seed(91, 3))
+    k_new = W.normal_bf16((16, W.HKV, W.HEAD_DIM), W.torch_seed(91, 4), "cuda")
+    v_new = W.normal_bf16((16, W.HKV, W.HEAD_DIM), W.torch_seed(91, 5), "cuda")
+    cu = np.minimum(np.arange(17), 11).astype(np.int32)
+    start = np.concatenate([lens, np.zeros(5)]).astype(np.int32)
+    k_before, v_before = bits(kp), bits(vp)
+    log("append, 11 requests padded to 16 rows")
+    run_append(kp, vp, k_new, v_new, cu, start, tb)
+    torch.cuda.synchronize()
+    k_want, v_want = oracle.kv_append(k_before, v_before, bits(k_new), bits(v_new), cu, start, tb)
+    assert np.array_equal(bits(kp), k_want)
+    assert np.array_equal(bits(vp), v_want)

@@ -238,3 +238,88 @@ def test_chunked_prefill_graph_replays():
     v = oracle.gather_logical(vc, ident, total)
     o_ref, l_ref = oracle.attention(oracle.bf16_to_f64(bits(q_log[s:s + c])[rows]), k, v, s + rows, W.SCALE)
     compare(outs[-1][rows], lses[-1][rows], o_ref, l_ref, "prefill graph: last chunk")
+
+
+def test_graph_batch_bucket_padding():
+    """Decode batches padded to a bucket, one captured graph per bucket: the graph for 16 requests
+    (4 layers of append + decode, max_kv_len bound 20,000) serves a batch of 12 and then a batch of
+    9 other requests.  Padding requests append no token (their cu_new entries repeat) and decode
+    zero keys (O = 0, LSE = -inf).  Every replay of the real requests equals the eager calls on
+    exactly those requests bit for bit, with eager work between replays; the last step of each
+    batch is also checked against the oracle."""
+    bucket, layers, bound, tag = 16, 4, 20000, 77
+    lens_a = W.loguniform_lengths(12, 500, 16000, tag, 1)
+    lens_b = W.loguniform_lengths(9, 64, 9000, tag, 2)
+    steps = 3
+    tables, n_pages, _ = W.place_pages(np.concatenate([lens_a, lens_b]) + steps, tag, 3)
+    stride = (bound + W.PAGE - 1) // W.PAGE
+    tb = np.zeros((len(tables), stride), dtype=np.int32)
+    tb[:, : tables.shape[1]] = tables
+    kg = [new_pool(n_pages, "cuda", W.torch_seed(tag, 40, l)) for l in range(layers)]
+    vg = [new_pool(n_pages, "cuda", W.torch_seed(tag, 41, l)) for l in range(layers)]
+    ke, ve = [p.clone() for p in kg], [p.clone() for p in vg]
+    q_buf = torch.empty((layers, bucket, W.HQ, W.HEAD_DIM), dtype=torch.bfloat16, device="cuda")
+    k_buf = torch.empty((layers, bucket, W.HKV, W.HEAD_DIM), dtype=torch.bfloat16, device="cuda")
+    v_buf = torch.empty_like(k_buf)
+    cu_buf = torch.zeros(bucket + 1, dtype=torch.int32, device="cuda")
+    start_buf = torch.zeros(bucket, dtype=torch.int32, device="cuda")
+    len_buf = torch.zeros(bucket, dtype=torch.int32, device="cuda")
+    bt_buf = torch.zeros((bucket, stride), dtype=torch.int32, device="cuda")
+    o_buf = torch.empty((layers, bucket, W.HQ, W.HEAD_DIM), dtype=torch.float32, device="cuda")
+    l_buf = torch.empty((layers, bucket, W.HQ), dtype=torch.float32, device="cuda")
+    ws = torch.empty(mtd.decode_workspace_bytes(bucket, bound), dtype=torch.uint8, device="cuda")
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        for l in range(layers):
+            mtd.mtd_kv_append(kg[l], vg[l], k_buf[l], v_buf[l], cu_buf, start_buf, bt_buf)
+            mtd.mtd_attn_decode(kg[l], vg[l], q_buf[l], len_buf, bt_buf, bound, W.SCALE, ws, o_buf[l], l_buf[l])
+    torch.cuda.synchronize()
+
+    for name, rows, lens0 in (("batch of 12", np.arange(12), lens_a), ("batch of 9", 12 + np.arange(9), lens_b)):
+        b = len(rows)
+        bt_real = torch.as_tensor(tb[rows], device="cuda")
+        cu_real = _i32(np.arange(b + 1))
+        ws_e = torch.empty(mtd.decode_workspace_bytes(b, int(lens0.max()) + steps), dtype=torch.uint8,
+                           device="cuda")
+        for s in range(steps):
+            log(f"bucket graph, {name}: step {s}")
+            q = W.normal_bf16((layers, b, W.HQ, W.HEAD_DIM), W.torch_seed(tag, 50 + s, b), "cuda")
+            kn = W.normal_bf16((layers, b, W.HKV, W.HEAD_DIM), W.torch_seed(tag, 60 + s, b), "cuda")
+            vn = W.normal_bf16((layers, b, W.HKV, W.HEAD_DIM), W.torch_seed(tag, 70 + s, b), "cuda")
+            # stage the real requests into the bucket's buffers; the rest is padding
+            q_buf.zero_()
+            k_buf.zero_()
+            v_buf.zero_()
+            q_buf[:, :b] = q
+            k_buf[:, :b] = kn
+            v_buf[:, :b] = vn
+            cu_buf.copy_(_i32(np.minimum(np.arange(bucket + 1), b)))
+            start_buf.copy_(_i32(np.concatenate([lens0 + s, np.zeros(bucket - b)])))
+            len_buf.copy_(_i32(np.concatenate([lens0 + s + 1, np.zeros(bucket - b)])))
+            bt_buf.zero_()
+            bt_buf[:b] = bt_real
+            o_buf.fill_(float("nan"))
+            l_buf.fill_(float("nan"))
+            graph.replay()
+            eager = []
+            for l in range(layers):
+                mtd.mtd_kv_append(ke[l], ve[l], kn[l], vn[l], cu_real, _i32(lens0 + s), bt_real)
+                eager.append(mtd.mtd_attn_decode(ke[l], ve[l], q[l], _i32(lens0 + s + 1), bt_real,
+                                                 int(lens0.max()) + steps, W.SCALE, ws_e))
+            torch.cuda.synchronize()
+            for l, (o, lse) in enumerate(eager):
+                assert torch.equal(o_buf[l, :b], o) and torch.equal(l_buf[l, :b], lse), (name, s, l)
+                assert torch.equal(o_buf[l, b:], torch.zeros_like(o_buf[l, b:])), (name, s, l)
+                assert bool((l_buf[l, b:] == -float("inf")).all()), (name, s, l)
+        for l in range(layers):
+            assert torch.equal(kg[l], ke[l]) and torch.equal(vg[l], ve[l]), (name, l)
+        qb = bits(q[0])
+        o_ref, l_ref = [], []
+        for i, r in enumerate(rows):
+            n = int(lens0[i]) + steps
+            kc, vc, ident = request_pages_host(kg[0], vg[0], tb[r], n)
+            o, lse = oracle.decode(qb[i:i + 1], kc, vc, [n], [ident], W.SCALE)
+            o_ref.append(o[0])
+            l_ref.append(lse[0])
+        compare(o_buf[0, :b], l_buf[0, :b], np.stack(o_ref), np.stack(l_ref), f"bucket graph, {name}, last step")
