@@ -113,6 +113,16 @@ def fill_normal_(t, seed, slab=1 << 28):
     return t
 
 
+def parity(o_gpu, l_gpu, o_ref, l_ref):
+    """The parity metrics of one comparison: max |dO|, max |dLSE|, relative Frobenius error, max |O|."""
+    o = o_gpu.detach().double().cpu().numpy().reshape(o_ref.shape)
+    l = l_gpu.detach().double().cpu().numpy().reshape(l_ref.shape)
+    return {"max_abs_dO": float(np.abs(o - o_ref).max()), "max_abs_dLSE": float(np.abs(l - l_ref).max()),
+            "rel_frobenius": float(np.linalg.norm(o - o_ref) / max(np.linalg.norm(o_ref), 1e-30)),
+            "max_abs_O": float(np.abs(o_ref).max()), "within_gates": bool(np.abs(o - o_ref).max() <= 1e-2 and
+                                                                         np.abs(l - l_ref).max() <= 1e-3)}
+
+
 class Timer:
     """HIP events recorded on the library's stream (torch's current stream)."""
 
@@ -226,6 +236,30 @@ class MixedStep:
         return {"kernel": "decode_split_kernel+decode_merge_kernel", "bound": "hbm", "achieved": res["decode"]["value"],
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "per_launch": res["decode"]["bytes"], "ms": res["decode"]["ms"]}
 
+    def record(self, pool):
+        """Seeds, lengths and the parity of the last timed step's outputs against the oracle: 256 prefill
+        rows (every 16th) and all decode requests."""
+        import torch
+        from oracle.parallel import decode_problem, prefill_problem
+        torch.cuda.synchronize()
+        host = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        kb, vb = host(self.k), host(self.v)
+        tables = self.bt_all.cpu().numpy()
+        rows = np.arange(0, self.chunk, 16)
+        qa, qd = host(self.q_a), host(self.q_d)
+        probs = [{"q": qa[rows], "k_pages": kb, "v_pages": vb, "table": tables[0], "n_keys": self.prefix + self.chunk,
+                  "q_pos": self.prefix + rows}]
+        probs += [decode_problem(qd[b:b + 1], kb, vb, tables[1 + b], int(self.lens[b])) for b in range(len(self.lens))]
+        ref = pool.attention(probs, W.SCALE)
+        o_ref = np.concatenate([r[0] for r in ref[1:]])
+        l_ref = np.concatenate([r[1] for r in ref[1:]])
+        return {"seeds": {"base": W.BASE_SEED, "tag": W.MIXED.tag},
+                "lengths": {"chunk": self.chunk, "prefix": self.prefix, "decode_requests": len(self.lens),
+                            "decode_min": int(self.lens.min()), "decode_mean": float(self.lens.mean()),
+                            "decode_max": int(self.lens.max()), "decode_sum": int(self.lens.sum())},
+                "parity": {"prefill, 256 rows (every 16th)": parity(self.o_a[rows], self.l_a[rows], ref[0][0], ref[0][1]),
+                           "decode, all 31 requests": parity(self.o_d, self.l_d, o_ref, l_ref)}}
+
     # ---- CPU baseline: the fp64 oracle on the same step ----
     def cpu_baseline(self):
         """The fp64 oracle on this step's whole input: all 4096 prefill rows and all 31 decode
@@ -319,6 +353,109 @@ class Decode16:
     def dominant(self, res):
         return {"kernel": "decode_split_kernel+decode_merge_kernel", "bound": "hbm", "achieved": res["decode"]["value"],
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "per_launch": self.bytes, "ms": res["decode"]["ms"]}
+
+    def record(self, pool):
+        """Seeds, lengths and the parity of the last timed step's outputs: all 16 requests."""
+        import torch
+        from oracle.parallel import decode_problem
+        torch.cuda.synchronize()
+        host = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        kb, vb, qb = host(self.k), host(self.v), host(self.q)
+        tables = self.bt.cpu().numpy()
+        ref = pool.attention([decode_problem(qb[b:b + 1], kb, vb, tables[b], int(self.lens[b]))
+                              for b in range(len(self.lens))], W.SCALE)
+        return {"seeds": {"base": W.BASE_SEED, "tag": W.DECODE16.tag},
+                "lengths": {"requests": len(self.lens), "min": int(self.lens.min()), "mean": float(self.lens.mean()),
+                            "max": int(self.lens.max()), "sum": int(self.lens.sum())},
+                "parity": {"decode, all 16 requests": parity(self.o, self.l, np.concatenate([r[0] for r in ref]),
+                                                             np.concatenate([r[1] for r in ref]))}}
+
+
+class Tiny:
+    """The tiny configuration as a step: one request's 439-token prompt appended and prefilled in one
+    shot, then 32 decode steps of (append one token, decode).  Launch-bound and cache-resident: its
+    figures are for parity and latency, not a roofline (the appends rewrite the same slots, so every
+    step sees the same inputs)."""
+    name = "tiny"
+
+    def __init__(self, dev):
+        import torch
+        import gqa_kv_cache_qwen3_amd as mtd
+        self.mtd, self.torch = mtd, torch
+        p = W.TINY.params
+        self.prompt, self.steps = p["prompt"], p["decode_steps"]
+        total = self.prompt + self.steps
+        tables, n_pages, _ = W.place_pages([total], W.TINY.tag, 0)
+        self.table_np = tables[0]
+        self.bt = torch.as_tensor(tables, device=dev)
+        self.k = torch.zeros((n_pages, W.HKV, W.PAGE, W.HEAD_DIM), dtype=torch.bfloat16, device=dev)
+        self.v = torch.zeros_like(self.k)
+        self.k_log = W.normal_bf16((total, W.HKV, W.HEAD_DIM), W.torch_seed(1, 1), dev)
+        self.v_log = W.normal_bf16((total, W.HKV, W.HEAD_DIM), W.torch_seed(1, 2), dev)
+        self.q_log = W.normal_bf16((total, W.HQ, W.HEAD_DIM), W.torch_seed(1, 3), dev)
+        self.cu_p = torch.tensor([0, self.prompt], dtype=torch.int32, device=dev)
+        self.cu_1 = torch.tensor([0, 1], dtype=torch.int32, device=dev)
+        self.starts = [torch.tensor([x], dtype=torch.int32, device=dev) for x in range(total)]
+        self.lens = [torch.tensor([x], dtype=torch.int32, device=dev) for x in range(total + 1)]
+        self.ws = torch.empty(mtd.decode_workspace_bytes(1, total), dtype=torch.uint8, device=dev)
+        self.o_p = torch.empty((self.prompt, W.HQ, W.HEAD_DIM), dtype=torch.float32, device=dev)
+        self.l_p = torch.empty((self.prompt, W.HQ), dtype=torch.float32, device=dev)
+        self.o_d = torch.empty((self.steps, 1, W.HQ, W.HEAD_DIM), dtype=torch.float32, device=dev)
+        self.l_d = torch.empty((self.steps, 1, W.HQ), dtype=torch.float32, device=dev)
+        self.timer = Timer(["prefill", "decode"])
+
+    def step(self, events=None):
+        mtd, P = self.mtd, self.prompt
+        if events: events[0].record()
+        mtd.mtd_kv_append(self.k, self.v, self.k_log[:P], self.v_log[:P], self.cu_p, self.starts[0], self.bt)
+        mtd.mtd_attn_prefill_chunk(self.k, self.v, self.q_log[:P], 0, self.bt[0], W.SCALE, self.o_p, self.l_p)
+        if events: events[1].record()
+        for s in range(self.steps):
+            n = P + s
+            mtd.mtd_kv_append(self.k, self.v, self.k_log[n:n + 1], self.v_log[n:n + 1], self.cu_1, self.starts[n], self.bt)
+            mtd.mtd_attn_decode(self.k, self.v, self.q_log[n:n + 1], self.lens[n + 1], self.bt, P + self.steps, W.SCALE,
+                                self.ws, self.o_d[s], self.l_d[s])
+        if events: events[2].record()
+
+    def config(self):
+        return {"workload": "tiny: one 439-token one-shot prefill (30 s of audio + 64 prompt tokens), then 32 decode "
+                            "steps of (append 1 token, decode)", "prompt": self.prompt, "decode_steps": self.steps}
+
+    def results(self):
+        pre, dec = self.timer.mean_ms("prefill"), self.timer.mean_ms("decode")
+        fl = prefill_flops(0, self.prompt)
+        by = sum(decode_bytes([self.prompt + s + 1]) for s in range(self.steps))
+        return {"prefill": {"value": fl / (pre * 1e-3) / 1e12, "unit": "TFLOP/s",
+                            "frac": fl / (pre * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, "ms": pre, "flops": fl,
+                            "kernels": "kv_append_kernel + prefill_kernel (one pass)"},
+                "decode": {"value": by / (dec * 1e-3) / 1e9, "unit": "GB/s", "frac": by / (dec * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                           "ms": dec / self.steps, "bytes": by / self.steps,
+                           "kernels": "32 x (kv_append_kernel + decode_split_kernel + decode_merge_kernel)"}}
+
+    def dominant(self, res):
+        return {"kernel": "decode_split_kernel+decode_merge_kernel", "bound": "hbm", "achieved": res["decode"]["value"],
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "per_launch": res["decode"]["bytes"], "ms": res["decode"]["ms"]}
+
+    def record(self, pool):
+        import oracle
+        host = lambda t: t.contiguous().view(self.torch.int16).cpu().numpy().view(np.uint16)
+        self.torch.cuda.synchronize()
+        used = (self.prompt + self.steps + W.PAGE - 1) // W.PAGE
+        idx = self.torch.as_tensor(self.table_np[:used].astype(np.int64), device=self.k.device)
+        kc, vc = host(self.k.index_select(0, idx)), host(self.v.index_select(0, idx))
+        ident = np.arange(used)
+        qb = host(self.q_log)
+        o_ref, l_ref = oracle.prefill_chunk(qb[:self.prompt], kc, vc, ident, 0, W.SCALE)
+        par = {"prefill, all 439 rows": parity(self.o_p, self.l_p, o_ref, l_ref)}
+        od, ld = [], []
+        for s in range(self.steps):
+            n = self.prompt + s + 1
+            o, l = oracle.decode(qb[n - 1:n], kc, vc, [n], [ident], W.SCALE)
+            od.append(o[0])
+            ld.append(l[0])
+        par["decode, all 32 steps"] = parity(self.o_d[:, 0], self.l_d[:, 0], np.stack(od), np.stack(ld))
+        return {"seeds": {"base": W.BASE_SEED, "tag": W.TINY.tag}, "lengths": {"prompt": self.prompt,
+                "decode_kv_lengths": [self.prompt + 1, self.prompt + self.steps]}, "parity": par}
 
 
 class Decode16SeqSplit:
@@ -451,6 +588,20 @@ class Prefill90:
                 "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "per_launch": self.flops / len(self.chunks),
                 "ms": res["prefill"]["ms"] / len(self.chunks)}
 
+    def record(self, pool):
+        """Seeds, lengths and the parity of the last chunk's outputs (every row of the 1,964) after the timed
+        passes (the output buffer holds the last chunk)."""
+        import torch
+        from oracle.parallel import prefill_problem
+        torch.cuda.synchronize()
+        host = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        s0, c = self.chunks[-1]
+        [(o_ref, l_ref)] = pool.attention([prefill_problem(host(self.q[s0:s0 + c]), host(self.k), host(self.v),
+                                                           self.bt[0].cpu().numpy(), s0)], W.SCALE)
+        return {"seeds": {"base": W.BASE_SEED, "tag": W.PREFILL90.tag},
+                "lengths": {"total": self.total, "chunk": self.chunk, "chunks": len(self.chunks)},
+                "parity": {f"last chunk (prefix {s0}), all {c} rows": parity(self.o[:c], self.l[:c], o_ref, l_ref)}}
+
 
 class FullDepth:
     """28 layers x 64 requests, all layers resident; a step appends one token per request and
@@ -524,6 +675,34 @@ class FullDepth:
         return {"kernel": "decode_split_kernel+decode_merge_kernel", "bound": "hbm", "achieved": res["decode"]["value"],
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "per_launch": res["decode"]["bytes"], "ms": res["decode"]["ms"]}
 
+    def record(self, pool):
+        """Seeds, lengths and the parity of the last layer's decode at the last timed step: 8 requests (seeded)."""
+        import torch
+        from oracle.parallel import decode_problem
+        torch.cuda.synchronize()
+        host = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        s = (self.step_idx - 1) % self.steps
+        layer = self.layers - 1
+        kp, vp = self.inp["k_pools"][layer], self.inp["v_pools"][layer]
+        q = host(self.inp["q"][s, layer])
+        lens = self.lens0 + s + 1
+        sample = np.sort(W.rng(5, 78).permutation(len(lens))[:8])
+        probs = []
+        for b in sample:
+            used = (int(lens[b]) + W.PAGE - 1) // W.PAGE
+            idx = torch.as_tensor(self.inp["tables"][b][:used].astype(np.int64), device=kp.device)
+            probs.append(decode_problem(q[b:b + 1], host(kp.index_select(0, idx)), host(vp.index_select(0, idx)),
+                                        np.arange(used), int(lens[b])))
+        ref = pool.attention(probs, W.SCALE)
+        o_ref = np.concatenate([r[0] for r in ref])
+        l_ref = np.concatenate([r[1] for r in ref])
+        idx = torch.as_tensor(sample, device=self.o.device)
+        return {"seeds": {"base": W.BASE_SEED, "tag": W.FULLDEPTH.tag, "tried": self.seeds_tried},
+                "lengths": {"layers": self.layers, "requests": len(self.lens0), "initial_min": int(self.lens0.min()),
+                            "initial_mean": float(self.lens0.mean()), "initial_max": int(self.lens0.max()),
+                            "steps": self.steps},
+                "parity": {f"layer {layer}, step {s}, 8 requests": parity(self.o[idx], self.l[idx], o_ref, l_ref)}}
+
     def cpu_baseline(self):
         """The fp64 oracle on 16 of the 64 requests (seeded choice) of the layer-0 decode call of the
         last timed step, over a process pool with one BLAS thread per worker; the oracle's compute
@@ -586,6 +765,7 @@ class MixedBlock(MixedStep):
     the output projection maps all their attention outputs back to hidden size."""
     name = "mixed_block"
 
+    record = None  # the attention's inputs come from the projections; parity is in the tests
     def __init__(self, dev):
         super().__init__(dev)
         torch, mtd = self.torch, self.mtd
@@ -639,6 +819,7 @@ class FullDepthBlock(FullDepth):
     attention, and the output projection whose result is the next layer's input."""
     name = "fulldepth_block"
 
+    record = None  # the attention's inputs come from the projections; parity is in the tests
     def __init__(self, dev):
         import torch
         p = W.FULLDEPTH.params
@@ -1052,7 +1233,7 @@ class DecodeGraphBlock(DecodeGraph):
         return res
 
 
-WORKLOAD_CLASSES = {c.name: c for c in (MixedStep, MixedStepOverlap, MixedBlock, Decode16, Decode16SeqSplit, Prefill90,
+WORKLOAD_CLASSES = {c.name: c for c in (Tiny, MixedStep, MixedStepOverlap, MixedBlock, Decode16, Decode16SeqSplit, Prefill90,
                                          FullDepth, FullDepthBlock, DecodeGraph, DecodeGraphBlock,
                                          DecodeGraphBuckets)}
 
@@ -1162,7 +1343,7 @@ def ceiling(dev, dec16, copy_bytes=4 << 30, reps=10):
 
 
 # Untimed steps per workload, each about 50 ms of GPU work or more.
-WARMUP_DEFAULT = {"decode_graph_buckets": 20, "mixed_step": 40, "mixed_step_overlap": 40, "mixed_block": 40, "decode16": 500,
+WARMUP_DEFAULT = {"tiny": 20, "decode_graph_buckets": 20, "mixed_step": 40, "mixed_step_overlap": 40, "mixed_block": 40, "decode16": 500,
                   "prefill90min": 3, "fulldepth_decode": 5, "fulldepth_block": 5, "decode_graph": 200,
                   "decode_graph_block": 200, "decode16_seqsplit": 2000}
 
@@ -1175,6 +1356,9 @@ def main():
                     help="untimed steps (default: enough for ~50 ms of GPU work, past the clock ramp)")
     ap.add_argument("--workload", default="mixed_step", choices=sorted(WORKLOAD_CLASSES))
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing on the host")
+    ap.add_argument("--results-json", default=None,
+                    help="also write a results record (the line, device, seeds, lengths, parity of this run's "
+                         "outputs against the oracle) to this path")
     ap.add_argument("--no-extras", action="store_true",
                     help="default workload only: skip the 90-minute prefill, decode16 and ceiling objects")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -1296,6 +1480,30 @@ def main():
     if not args.no_cpu_baseline and getattr(wl, "cpu_baseline", None) is not None:
         line["cpu_baseline"] = wl.cpu_baseline()
     print(json.dumps(line), flush=True)
+    if args.results_json:
+        write_record(args.results_json, line, wl, dev)
+
+
+def write_record(path, line, wl, dev):
+    """The per-configuration results record: the bench line, the device, and (where the workload has
+    one) its seeds, length summary and the parity of this run's outputs against the fp64 oracle."""
+    import platform
+    import torch
+    from oracle.parallel import OraclePool, cpu_model
+    prop = torch.cuda.get_device_properties(dev)
+    free, total = torch.cuda.mem_get_info(dev)
+    rec = {"line": line,
+           "device": {"name": prop.name, "arch": getattr(prop, "gcnArchName", ""), "compute_units": prop.multi_processor_count,
+                      "memory_total": int(total), "memory_free_at_end": int(free), "torch": torch.__version__,
+                      "hip": torch.version.hip, "host": platform.node(), "cpu_model": cpu_model()},
+           "gates": {"max_abs_dO": 1e-2, "max_abs_dLSE": 1e-3}}
+    if getattr(wl, "record", None) is not None:
+        with OraclePool() as pool:
+            rec.update(wl.record(pool))
+    os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(f"bench.py: results record written to {path}", file=sys.stderr)
 
 
 if __name__ == "__main__":
