@@ -14,25 +14,30 @@
 //                   activation type) as it is staged into LDS; W_o bf16 [1024][2048]; C rounded
 //                   to bf16 [T][1024].
 //
-// Work split.  One workgroup (4 wavefronts) owns a 128 x 128 tile of C; wave w computes the 64 x
-// 64 quarter (w / 2, w % 2) as 2 x 2 blocks of v_mfma_f32_32x32x16_bf16 with fp32 accumulators.
-// K advances 64 at a time through two LDS stages: right after the barrier that publishes stage
-// s, the loads of the next 64-wide slice into stage s^1 are issued, so they travel while stage s
-// is multiplied.  The stages are separate arrays picked at compile time (the loop is unrolled by
-// two), which lets the compiler see that the reads of one stage never wait on the loads into the
-// other.  Two workgroups fit per CU (64 KiB of LDS each); the tile does 64 flops per staged
-// byte (a 256-row tile, with a quarter fewer staged bytes per flop, measured no faster).
-// Calls with at most 64 tokens use proj_skinny_kernel instead, which spreads K over the waves.
-// Both kernels add the products in one order (fixed K slices, see kKSlice), so a token's result
-// is the same whatever the token count and whichever kernel runs.
+// Kernels.  Calls with more than 64 tokens run tiled kernels: proj_wide_kernel for the QKV map
+// (256 x 128 tiles, 8 waves of 64 x 64, three 48 KiB stages; see its comment) and
+// proj_f32a_kernel for the output map, whose float32 A is rounded to bf16 on the way into LDS.
+// Calls with at most 64 tokens use proj_skinny_kernel, which spreads K over the waves.  All three
+// add the products in one order (fixed K slices, see kKSlice), so a token's result is the same
+// whatever the token count and whichever kernel runs.  The MFMA is v_mfma_f32_32x32x16_bf16 with
+// fp32 accumulators throughout.
 //
-// Staging.  A 128 x 64 bf16 slice is two column groups of 64 bytes (k 32j .. 32j+31) of 128 rows;
-// the 16-byte slot of (row r, chunk c) is 512 (c/4) + 4 r + ((c%4) ^ ((r/4)%4)).  bf16 slices
-// arrive by 16-byte direct-to-LDS loads (global_load_lds_dwordx4: no registers, no VALU), each
-// instruction fetching 16 rows x 64 contiguous bytes; the float32 O slice comes through registers
-// (16 lanes per 256-byte row, coalesced), is rounded to bf16 and written with ds_write_b64 into
-// the same layout.  MFMA operands are ds_read_b128 of one row's 16-byte chunk: A rows for the A
-// operand and W rows for the B operand, both free of bank conflicts under the XOR swizzle.
+// proj_f32a_kernel.  One workgroup (4 wavefronts) owns a 128 x 128 tile of C; wave w computes the
+// 64 x 64 quarter (w / 2, w % 2) as 2 x 2 MFMA blocks.  K advances 64 at a time through two LDS
+// stages: right after the barrier that publishes stage s, the loads of the next 64-wide slice
+// into stage s^1 are issued, so they travel while stage s is multiplied.  The stages are separate
+// arrays picked at compile time (the loop is unrolled by two), which lets the compiler see that
+// the reads of one stage never wait on the loads into the other.  Two workgroups fit per CU.  A
+// 128 x 64 bf16 slice is two column groups of 64 bytes (k 32j .. 32j+31) of 128 rows; the 16-byte
+// slot of (row r, chunk c) is 512 (c/4) + 4 r + ((c%4) ^ ((r/4)%4)).  W slices arrive by 16-byte
+// direct-to-LDS loads, each instruction fetching 16 rows x 64 contiguous bytes; the float32 O slice
+// comes through registers (16 lanes per 256-byte row, coalesced), is rounded to bf16 and written
+// with ds_write_b64 into the same layout.  MFMA operands are ds_read_b128 of one row's 16-byte
+// chunk, free of bank conflicts under the XOR swizzle.
+//
+// A slice's MFMAs and the addition of its sums to the running total always share a basic block:
+// with a branch between an MFMA and the read of its accumulator the compiler has been seen to
+// leave too few wait states, and the read then returned a stale value.
 //
 // Placement.  Workgroup i runs on XCD i % 8.  Each XCD owns every eighth tile row (every XCD
 // then reads W whole and an eighth of A) or an eighth of the tile columns (an eighth of W, all of A);
@@ -40,6 +45,7 @@
 // index varies fastest, so the workgroups in flight together touch few tiles of the replicated
 // operand and each is brought into the XCD's L2 once rather than once per owned row.
 #include <type_traits>
+#include <utility>
 
 #include "device_util.h"
 #include "mtd_internal.h"
@@ -52,7 +58,7 @@ constexpr int kTN = 128;    // tile columns (output features)
 constexpr int kTK = 64;     // K per stage
 constexpr int kThreads = 256;
 constexpr int kSliceBytes = kTM * kTK * 2;  // 16 KiB per operand per stage
-// Summation order, the same in both kernels: K is cut into slices of kKSlice; each slice's
+// Summation order, the same in all three kernels: K is cut into slices of kKSlice; each slice's
 // products are accumulated by one chain of MFMAs starting from zero, and the slice sums are then
 // added in slice order to a running total that starts from zero.  So a token's outputs never
 // depend on how many tokens share the call or which kernel serves it.
@@ -117,11 +123,35 @@ struct OutMap {
   int lo[3];
 };
 
-template <bool kAF32>
-__global__ __launch_bounds__(kThreads, 2) void proj_gemm_kernel(const void* __restrict__ a_ptr, int lda,
-                                                                int rows, const uint16_t* __restrict__ w,
-                                                                int k_dim, int n_tm, int n_tn,
-                                                                int rows_major, OutMap out) {
+// Tile (tm, tn) of workgroup id for tiles of tm_rows rows; see Placement.  tm == n_tm: no tile.
+__device__ __forceinline__ void tile_of(int id, int rows, int tm_rows, int n_tm, int n_tn, int rows_major,
+                                        int& tm, int& tn) {
+  const int x = id % 8, local = id / 8;
+  if (rows_major) {
+    const int n_full = rows / tm_rows;
+    const int m_per = (n_full + 7) / 8;
+    if (local < m_per * n_tn) {
+      tm = x + 8 * (local % m_per);
+      tn = local / m_per;
+      if (tm >= n_full) tm = n_tm;
+    } else {
+      tm = n_full;
+      tn = x + 8 * (local - m_per * n_tn);
+    }
+  } else if (n_tn % 8 == 0) {
+    tn = x * (n_tn / 8) + local % (n_tn / 8);
+    tm = local / (n_tn / 8);
+  } else {
+    tm = id / n_tn;
+    tn = id % n_tn;
+  }
+}
+
+// Many tokens, float32 A (the output map): a 128 x 128 tile per workgroup of 4 waves, two
+// workgroups per CU; see Work split and Staging above.
+__global__ __launch_bounds__(kThreads, 2) void proj_f32a_kernel(const float* __restrict__ a, int lda, int rows,
+                                                                const uint16_t* __restrict__ w, int k_dim,
+                                                                int n_tm, int n_tn, int rows_major, OutMap out) {
   // One array per stage: with the stage known at compile time, the compiler can see that the
   // loads into one stage never touch the LDS being read from the other, and does not wait for them.
   __shared__ __attribute__((aligned(1024))) uint8_t s_a0[kSliceBytes];
@@ -132,35 +162,8 @@ __global__ __launch_bounds__(kThreads, 2) void proj_gemm_kernel(const void* __re
   const int wave = tid >> 6;
   const int lane = tid & 63;
 
-  // Tile of this workgroup.  XCD x = blockIdx.x % 8 owns the tile rows x, x + 8, x + 16, ... (or
-  // an eighth of the tile columns); inside it the owned index varies fastest, so the workgroups
-  // running at once share a few tiles of the replicated operand and each of those is fetched into
-  // the XCD's L2 once.  With rows owned, the grid is padded to whole groups of 8 rows and the
-  // workgroups of missing rows exit at once.
-  const int id = blockIdx.x;
-  const int x = id % 8, local = id / 8;
   int tm, tn;
-  if (rows_major) {
-    // Whole tile rows as above; a last, partly filled tile row is dealt out by columns over the
-    // XCDs instead (tile column x, x + 8, ...), after the XCD's whole rows, so that no XCD holds
-    // one tile row more than the others.
-    const int n_full = rows / kTM;
-    const int m_per = (n_full + 7) / 8;
-    if (local < m_per * n_tn) {
-      tm = x + 8 * (local % m_per);
-      tn = local / m_per;
-      if (tm >= n_full) tm = n_tm;  // a padding row: exit below
-    } else {
-      tm = n_full;                  // == n_tm only when there is no partial row: exit below
-      tn = x + 8 * (local - m_per * n_tn);
-    }
-  } else if (n_tn % 8 == 0) {
-    tn = x * (n_tn / 8) + local % (n_tn / 8);
-    tm = local / (n_tn / 8);
-  } else {
-    tm = id / n_tn;
-    tn = id % n_tn;
-  }
+  tile_of(blockIdx.x, rows, kTM, n_tm, n_tn, rows_major, tm, tn);
   if (tm >= n_tm || tn >= n_tn) return;  // whole workgroup, before any barrier
   const int row0 = tm * kTM;
   const int col0 = tn * kTN;
@@ -187,21 +190,15 @@ __global__ __launch_bounds__(kThreads, 2) void proj_gemm_kernel(const void* __re
 
   const int nk = k_dim / kTK;  // even (k_dim is a multiple of kKSlice)
   F32Slice fa;
-  auto issue = [&](int kt, uint8_t* a_dst, uint8_t* w_dst) {
-    dma_slice(w, k_dim, col0, kTN, kt * kTK, w_dst, wave, lane);
-    if constexpr (kAF32)
-      load_f32_slice(fa, static_cast<const float*>(a_ptr), lda, row0, rows_valid, kt * kTK, wave, lane);
-    else
-      dma_slice(static_cast<const uint16_t*>(a_ptr), lda, row0, rows_valid, kt * kTK, a_dst, wave, lane);
-  };
-  // K step kt: stage (cur_a, cur_w) holds slice kt; slice kt+1 goes to (nxt_a, nxt_w).  In a
-  // partly filled tile (kPartial) a wave skips the MFMAs of its 32-row blocks that hold no token.
-  const int live_rows = rows_valid - 64 * wm;  // rows of this wave's 64 that hold a token
-  auto step = [&](auto partial, int kt, const uint8_t* cur_a, const uint8_t* cur_w, uint8_t* nxt_a,
-                  uint8_t* nxt_w) {
-    constexpr bool kPartial = decltype(partial)::value;
+  // K step kt: stage (cur_a, cur_w) holds slice kt; slice kt+1 goes to (nxt_a, nxt_w).  A slice's
+  // MFMAs and its addition to the total share a basic block (fold is a compile-time flag).
+  auto step = [&](auto fold, int kt, const uint8_t* cur_a, const uint8_t* cur_w, uint8_t* nxt_a,
+                  uint8_t* nxt_w) __attribute__((always_inline)) {
     __syncthreads();  // the current stage complete for every wave; the other no longer read
-    if (kt + 1 < nk) issue(kt + 1, nxt_a, nxt_w);
+    if (kt + 1 < nk) {
+      dma_slice(w, k_dim, col0, kTN, (kt + 1) * kTK, nxt_w, wave, lane);
+      load_f32_slice(fa, a, lda, row0, rows_valid, (kt + 1) * kTK, wave, lane);
+    }
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       bf16x8_t af[2], wf[2];
@@ -213,16 +210,13 @@ __global__ __launch_bounds__(kThreads, 2) void proj_gemm_kernel(const void* __re
                                                  cur_w + wbase[ks & 1] + 8192 * (ks >> 1) + 2048 * i));
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        if (kPartial && live_rows <= 32 * i) continue;
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], wf[j], acc[i][j], 0, 0, 0);
-      }
     }
-    if constexpr (kAF32)
-      if (kt + 1 < nk) store_f32_slice(fa, nxt_a, wave, lane);
-    if ((kt + 1) % (kKSlice / kTK) == 0) {
+    if (kt + 1 < nk) store_f32_slice(fa, nxt_a, wave, lane);
+    if constexpr (decltype(fold)::value) {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -235,19 +229,243 @@ __global__ __launch_bounds__(kThreads, 2) void proj_gemm_kernel(const void* __re
     }
   };
 
-  issue(0, s_a0, s_w0);
-  if constexpr (kAF32) store_f32_slice(fa, s_a0, wave, lane);
-  // (The float32-A kernel runs every tile whole: the second loop would not fit its registers.)
-  if (kAF32 || rows_valid == kTM) {
-    for (int kt = 0; kt < nk; kt += 2) {
-      step(std::false_type{}, kt, s_a0, s_w0, s_a1, s_w1);
-      step(std::false_type{}, kt + 1, s_a1, s_w1, s_a0, s_w0);
+  dma_slice(w, k_dim, col0, kTN, 0, s_w0, wave, lane);
+  load_f32_slice(fa, a, lda, row0, rows_valid, 0, wave, lane);
+  store_f32_slice(fa, s_a0, wave, lane);
+  static_assert(kKSlice == 2 * kTK, "one K slice = the two steps of a loop trip");
+  for (int kt = 0; kt < nk; kt += 2) {
+    step(std::false_type{}, kt, s_a0, s_w0, s_a1, s_w1);
+    step(std::true_type{}, kt + 1, s_a1, s_w1, s_a0, s_w0);
+  }
+
+  // Epilogue: accumulator element v of block (i, j) is C[row0 + 64wm + 32i + 8(v/4) + 4hk + v%4]
+  // [col0 + 64wn + 32j + n].
+  uint16_t* dst = out.dst[0];
+  const int ld = out.ld[0];
+  const int cbase = col0 + 64 * wn + n;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int r = 64 * wm + 32 * i + 8 * (v >> 2) + 4 * hk + (v & 3);
+      if (r < rows_valid) {
+        uint16_t* drow = dst + (size_t)(row0 + r) * ld + cbase;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) drow[32 * j] = (uint16_t)pack_bf16x2(sum[i][j][v], 0.f);
+      }
     }
-  } else if constexpr (!kAF32) {
-    for (int kt = 0; kt < nk; kt += 2) {
-      step(std::true_type{}, kt, s_a0, s_w0, s_a1, s_w1);
-      step(std::true_type{}, kt + 1, s_a1, s_w1, s_a0, s_w0);
+}
+
+// Many tokens, bf16 A (the QKV map): a 256 x 128 tile per workgroup of 8 waves, two per SIMD,
+// each computing a 64 x 64 block (wave w: rows 64 (w / 2), columns 64 (w % 2)) as 2 x 2 MFMA
+// blocks.  K advances 64 at a time through a ring of three 48 KiB LDS stages with the DMA two
+// stages ahead of the MFMAs.  Each direct-to-LDS instruction fetches 8 rows x 128 bytes, whole
+// cache lines (16 rows x 64 bytes, half lines, measured at half the rate).  A wave waits for its
+// own loads of the stage about to be read and the barrier publishes everyone's.  The whole K loop
+// is unrolled at compile time, so every step is straight-line code with its stage, wait count and
+// fold known.  At the end of each K slice a wave adds its slice sums to its total while the other
+// wave on its SIMD keeps the matrix pipe busy.
+constexpr int kWM = 256;       // tile rows (tokens)
+constexpr int kWN = 128;       // tile columns
+constexpr int kWK = 64;        // K per stage
+constexpr int kWStages = 3;
+constexpr int kWWaves = 8;
+constexpr int kWThreads = 64 * kWWaves;
+constexpr int kWStageA = kWM * kWK * 2;
+constexpr int kWStageW = kWN * kWK * 2;
+constexpr int kWLoads = (kWM + kWN) / 8 / kWWaves;  // DMA instructions per wave and stage
+
+// Byte offset in a stage of the 16-byte chunk c (k 8c .. 8c+7) of row r: rows of 128 bytes, the
+// chunks of a row permuted by (r/2) % 8, so that one chunk of 16 consecutive rows (one
+// ds_read_b128 phase) covers every bank once.
+__device__ __forceinline__ int slot128(int r, int c) { return 16 * (8 * r + (c ^ ((r >> 1) & 7))); }
+
+// Direct-to-LDS copies of an R-row block of a bf16 matrix with leading dimension ld, 64 columns
+// at a time.  Instruction i (R/8 in all, spread over the waves) fills bytes 1024 i .. 1024 i + 1023
+// of a stage = rows 8 i .. 8 i + 7; lane l takes the chunk of row 8 i + l / 8 stored in slot l % 8.
+// They are buffer loads: the block's base address sits in a resource descriptor in scalar
+// registers, the column offset of the step in a scalar offset, and each lane keeps one 32-bit byte
+// offset per instruction for the whole K loop.  Rows at or past rows_valid re-read the last valid
+// row.
+constexpr int kBufferWord3 = 0x00020000;  // raw buffer descriptor word 3 on gfx9-family parts
+
+template <int R>
+struct RowDma {
+  static constexpr int kPerWave = R / 8 / kWWaves;
+  static_assert(kPerWave * 8 * kWWaves == R, "whole instructions per wave");
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t off[kPerWave];
+  __device__ __forceinline__ RowDma(const uint16_t* block, int ld, int rows_valid, int wave, int lane) {
+    rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(block), (short)0, rows_valid * ld * 2,
+                                             kBufferWord3);
+#pragma unroll
+    for (int j = 0; j < kPerWave; ++j) {
+      const int i = kPerWave * wave + j;
+      const int r = 8 * i + (lane >> 3);
+      const int c = (lane & 7) ^ ((r >> 1) & 7);
+      const int rs = r < rows_valid ? r : rows_valid - 1;
+      off[j] = (uint32_t)(rs * ld + 8 * c) * 2u;
     }
+  }
+  __device__ __forceinline__ void issue(int k0, uint8_t* lds, int wave) const {
+#pragma unroll
+    for (int j = 0; j < kPerWave; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(lds + (kPerWave * wave + j) * 1024), 16, off[j],
+                                               k0 * 2, 0, 0);
+  }
+};
+
+// Scheduling groups for one k-step: after each of the M MFMAs, one of the V direct-to-LDS loads
+// or, once those are out, up to two of the D LDS reads.
+template <int M, int V, int D>
+__device__ __forceinline__ void interleave() {
+  if constexpr (M > 0) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    if constexpr (V > 0) {
+      __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // VMEM
+      interleave<M - 1, V - 1, D>();
+    } else if constexpr (D > 0) {
+      constexpr int d = D < 2 ? D : 2;
+      __builtin_amdgcn_sched_group_barrier(0x100, d, 0);  // LDS read
+      interleave<M - 1, 0, D - d>();
+    } else {
+      interleave<M - 1, 0, 0>();
+    }
+  } else {
+    if constexpr (V > 0) __builtin_amdgcn_sched_group_barrier(0x010, V, 0);
+    if constexpr (D > 0) __builtin_amdgcn_sched_group_barrier(0x100, D, 0);
+  }
+}
+
+// f(integral_constant<int, I>) for I = 0 .. N-1, in order, at compile time.
+template <class F, int... I>
+__device__ __forceinline__ void for_each_index(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+
+// s_waitcnt immediate: vmcnt(n) and lgkmcnt(0), expcnt left at its maximum.
+constexpr int wait_vm_lgkm0(int n) { return (n & 15) | (7 << 4) | ((n >> 4) << 14); }
+
+template <int kK>
+__global__ __launch_bounds__(kWThreads, 1) void proj_wide_kernel(const uint16_t* __restrict__ a, int lda, int rows,
+                                                                const uint16_t* __restrict__ w, int n_tm,
+                                                                int n_tn, int rows_major, OutMap out) {
+  // One array per stage, so that the compiler can see which stage each load and read touches.
+  __shared__ __attribute__((aligned(1024))) uint8_t s_a0[kWStageA];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_a1[kWStageA];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_a2[kWStageA];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_w0[kWStageW];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_w1[kWStageW];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_w2[kWStageW];
+  constexpr int nk = kK / kWK;
+  constexpr int kStepsPerSlice = kKSlice / kWK;
+  static_assert(kKSlice % kWK == 0 && nk % kStepsPerSlice == 0 && nk >= kWStages, "whole slices of whole steps");
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+
+  int tm, tn;
+  tile_of(blockIdx.x, rows, kWM, n_tm, n_tn, rows_major, tm, tn);
+  if (tm >= n_tm || tn >= n_tn) return;  // whole workgroup, before any barrier
+  const int row0 = tm * kWM;
+  const int col0 = tn * kWN;
+  const int rows_valid = min(kWM, rows - row0);
+
+  const int wm = wave >> 1, wn = wave & 1;
+  const int n = lane & 31, hk = lane >> 5;
+  // ds_read_b128 bases of k-step ks: row 64 wm + n (A) or 64 wn + n (W), chunk 2 ks + hk.
+  int abase[4], wbase[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    abase[ks] = slot128(64 * wm + n, 2 * ks + hk);
+    wbase[ks] = slot128(64 * wn + n, 2 * ks + hk);
+  }
+
+  floatx16_t acc[2][2], sum[2][2];  // the current K slice; the slices before it
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = sum[i][j][v] = 0.f;
+
+  uint8_t* const sa[kWStages] = {s_a0, s_a1, s_a2};
+  uint8_t* const sw[kWStages] = {s_w0, s_w1, s_w2};
+  const RowDma<kWN> dma_w(w + (size_t)col0 * kK, kK, kWN, wave, lane);
+  const RowDma<kWM> dma_a(a + (size_t)row0 * lda, lda, rows_valid, wave, lane);
+  auto issue = [&](int kt) __attribute__((always_inline)) {
+    dma_w.issue(kt * kWK, sw[kt % kWStages], wave);
+    dma_a.issue(kt * kWK, sa[kt % kWStages], wave);
+  };
+  // Step KT on stage KT % 3: wait for this wave's DMA of it (the loads of step KT + 1 may stay in
+  // flight) and for its reads of the stage before; the barrier publishes the stage and frees the
+  // one step KT - 1 read, which the DMA of step KT + 2 then refills.  Within the step the operands
+  // of k-step ks + 1 are read while the MFMAs of k-step ks run.  kLive: the wave's first kLive
+  // 32-row blocks hold tokens (2 but in a partly filled tile), the others get no MFMAs.
+  auto run = [&](auto live) __attribute__((always_inline)) {
+    constexpr int kLive = decltype(live)::value;
+    for_each_index(
+        [&](auto kt_) __attribute__((always_inline)) {
+          constexpr int KT = decltype(kt_)::value;
+          constexpr bool kIssue = KT + 2 < nk;
+          __builtin_amdgcn_sched_barrier(0);
+          __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(KT + 1 < nk ? kWLoads : 0));
+          asm volatile("" ::: "memory");
+          __builtin_amdgcn_s_barrier();
+          asm volatile("" ::: "memory");
+          if constexpr (kIssue) issue(KT + 2);
+          const uint8_t* cur_a = sa[KT % kWStages];
+          const uint8_t* cur_w = sw[KT % kWStages];
+          bf16x8_t af[2][2], wf[2][2];
+          auto read = [&](int ks, bf16x8_t(&a_f)[2], bf16x8_t(&w_f)[2]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < kLive; ++i)
+              a_f[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(cur_a + abase[ks] + 4096 * i));
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+              w_f[j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(cur_w + wbase[ks] + 4096 * j));
+          };
+          if constexpr (kLive > 0) read(0, af[0], wf[0]);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            if constexpr (kLive > 0)
+              if (ks < 3) read(ks + 1, af[(ks + 1) & 1], wf[(ks + 1) & 1]);
+#pragma unroll
+            for (int i = 0; i < kLive; ++i)
+#pragma unroll
+              for (int j = 0; j < 2; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][i], wf[ks & 1][j], acc[i][j], 0, 0, 0);
+            // the first k-step also carries the DMA instructions
+            if (ks == 0)
+              interleave<2 * kLive, (kIssue ? kWLoads : 0), (kLive > 0 ? kLive + 2 : 0)>();
+            else if (ks < 3)
+              interleave<2 * kLive, 0, kLive + 2>();
+            else
+              interleave<2 * kLive, 0, 0>();
+          }
+          if constexpr ((KT + 1) % kStepsPerSlice == 0) {
+#pragma unroll
+            for (int i = 0; i < kLive; ++i)
+#pragma unroll
+              for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                  sum[i][j][v] += acc[i][j][v];
+                  acc[i][j][v] = 0.f;
+                }
+          }
+        },
+        std::make_integer_sequence<int, nk>{});
+  };
+
+  issue(0);
+  issue(1);
+  const int live_blocks = min(2, max(0, (rows_valid - 64 * wm + 31) / 32));  // uniform per wave
+  switch (live_blocks) {
+    case 2: run(std::integral_constant<int, 2>{}); break;
+    case 1: run(std::integral_constant<int, 1>{}); break;
+    default: run(std::integral_constant<int, 0>{}); break;
   }
 
   // Epilogue: accumulator element v of block (i, j) is C[row0 + 64wm + 32i + 8(v/4) + 4hk + v%4]
@@ -388,10 +606,10 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void proj_skinny_kernel(
 
 // Workgroups launched for the tiles of `rows` rows x n_tn tile columns.  Rows owned by XCD: whole
 // tile rows padded to groups of 8, plus a partly filled last row dealt out over the XCDs by column.
-int grid_tiles(int rows, int n_tn, int rows_major) {
-  const int n_tm = (rows + kTM - 1) / kTM;
+int grid_tiles(int rows, int n_tn, int rows_major, int tm_rows = kTM) {
+  const int n_tm = (rows + tm_rows - 1) / tm_rows;
   if (!rows_major) return n_tm * n_tn;
-  const int n_full = rows / kTM;
+  const int n_full = rows / tm_rows;
   const int tail = n_tm > n_full ? (n_tn + 7) / 8 : 0;
   return 8 * (((n_full + 7) / 8) * n_tn + tail);
 }
@@ -406,8 +624,6 @@ int rows_major_split(int rows, size_t a_row_bytes, size_t w_bytes) {
 hipError_t launch_qkv_proj(const uint16_t* x, const uint16_t* w_qkv, int n_tok, uint16_t* q,
                            uint16_t* k, uint16_t* v, hipStream_t stream) {
   constexpr int kN = (kQHeads + 2 * kKvHeads) * kHeadDim;
-  const int n_tm = (n_tok + kTM - 1) / kTM;
-  const int n_tn = kN / kTN;
   OutMap om;
   om.dst[0] = q;
   om.dst[1] = k;
@@ -423,8 +639,10 @@ hipError_t launch_qkv_proj(const uint16_t* x, const uint16_t* w_qkv, int n_tok, 
     return hipGetLastError();
   }
   const int rows_major = rows_major_split(n_tok, kHidden * 2, (size_t)kN * kHidden * 2);
-  proj_gemm_kernel<false><<<dim3(grid_tiles(n_tok, n_tn, rows_major)), dim3(kThreads), 0, stream>>>(
-      x, kHidden, n_tok, w_qkv, kHidden, n_tm, n_tn, rows_major, om);
+  const int n_wm = (n_tok + kWM - 1) / kWM;
+  const int n_wn = kN / kWN;
+  proj_wide_kernel<kHidden><<<dim3(grid_tiles(n_tok, n_wn, rows_major, kWM)), dim3(kWThreads), 0, stream>>>(
+      x, kHidden, n_tok, w_qkv, n_wm, n_wn, rows_major, om);
   return hipGetLastError();
 }
 
@@ -445,7 +663,7 @@ hipError_t launch_o_proj(const float* attn, const uint16_t* w_o, int n_tok, uint
     return hipGetLastError();
   }
   const int rows_major = rows_major_split(n_tok, kK * 4, (size_t)kHidden * kK * 2);
-  proj_gemm_kernel<true><<<dim3(grid_tiles(n_tok, n_tn, rows_major)), dim3(kThreads), 0, stream>>>(
+  proj_f32a_kernel<<<dim3(grid_tiles(n_tok, n_tn, rows_major)), dim3(kThreads), 0, stream>>>(
       attn, kK, n_tok, w_o, kK, n_tm, n_tn, rows_major, om);
   return hipGetLastError();
 }

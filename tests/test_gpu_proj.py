@@ -50,7 +50,7 @@ def _weights(dev):
     return W.projection_weights(W.torch_seed(TAG, 0), dev)
 
 
-@pytest.mark.parametrize("n_tok", [1, 8, 9, 37, 64, 65, 128, 300, 439])
+@pytest.mark.parametrize("n_tok", [1, 8, 9, 37, 64, 65, 128, 255, 256, 257, 300, 439, 1000])
 def test_qkv_proj_matches_oracle(n_tok):
     log(f"qkv projection n_tok={n_tok}")
     w_qkv, _ = _weights("cuda")
