@@ -54,7 +54,7 @@ KERNEL_SOURCES = {
     "prefill_kernel+prefill_merge_kernel": ["prefill.hip"],
     "decode_split_kernel+decode_merge_kernel": ["decode.hip"],
     "proj_wide_kernel": ["proj.hip"],
-    "proj_f32a_kernel": ["proj.hip"],
+    "proj_ksplit_kernel": ["proj.hip"],
 }
 COMMON_SOURCES = ["device_util.h", "mtd_internal.h"]
 
@@ -747,7 +747,7 @@ def proj_work(n_tok: int):
 def proj_results(samples_qkv, samples_o, n_tok, calls_per_sample=1, workload=None):
     qkv_w, o_w = proj_work(n_tok)
     out = {}
-    kernels = {"qkv_proj": "proj_wide_kernel", "o_proj": "proj_f32a_kernel"}
+    kernels = {"qkv_proj": "proj_wide_kernel", "o_proj": "proj_ksplit_kernel"}
     for name, samples, wk in (("qkv_proj", samples_qkv, qkv_w), ("o_proj", samples_o, o_w)):
         ms = float(np.sum(samples)) / (len(samples) * calls_per_sample)
         tfs = wk["flops"] / (ms * 1e-3) / 1e12

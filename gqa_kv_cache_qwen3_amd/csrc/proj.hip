@@ -15,29 +15,21 @@
 //                   to bf16 [T][1024].
 //
 // Kernels.  Calls with more than 64 tokens run tiled kernels: proj_wide_kernel for the QKV map
-// (256 x 128 tiles, 8 waves of 64 x 64, three 48 KiB stages; see its comment) and
-// proj_f32a_kernel for the output map, whose float32 A is rounded to bf16 on the way into LDS.
-// Calls with at most 64 tokens use proj_skinny_kernel, which spreads K over the waves.  All three
-// add the products in one order (fixed K slices, see kKSlice), so a token's result is the same
-// whatever the token count and whichever kernel runs.  The MFMA is v_mfma_f32_32x32x16_bf16 with
-// fp32 accumulators throughout.
+// (256 x 128 tiles) and proj_ksplit_kernel for the output map (128 x 128 tiles with K split
+// between two sets of waves); see their comments.  A last partial tile of at most 64 rows goes to
+// proj_skinny_kernel in a second launch, and so do whole calls of at most 64 tokens: it spreads
+// K over the waves.  All three add the products in one order (fixed K slices and groups of them,
+// see kKSlice), so a token's result is the same whatever the token count and whichever kernel
+// runs.  The MFMA is v_mfma_f32_32x32x16_bf16 with fp32 accumulators throughout.
 //
-// proj_f32a_kernel.  One workgroup (4 wavefronts) owns a 128 x 128 tile of C; wave w computes the
-// 64 x 64 quarter (w / 2, w % 2) as 2 x 2 MFMA blocks.  K advances 64 at a time through two LDS
-// stages: right after the barrier that publishes stage s, the loads of the next 64-wide slice
-// into stage s^1 are issued, so they travel while stage s is multiplied.  The stages are separate
-// arrays picked at compile time (the loop is unrolled by two), which lets the compiler see that
-// the reads of one stage never wait on the loads into the other.  Two workgroups fit per CU.  A
-// 128 x 64 bf16 slice is two column groups of 64 bytes (k 32j .. 32j+31) of 128 rows; the 16-byte
-// slot of (row r, chunk c) is 512 (c/4) + 4 r + ((c%4) ^ ((r/4)%4)).  W slices arrive by 16-byte
-// direct-to-LDS loads, each instruction fetching 16 rows x 64 contiguous bytes; the float32 O slice
-// comes through registers (16 lanes per 256-byte row, coalesced), is rounded to bf16 and written
-// with ds_write_b64 into the same layout.  MFMA operands are ds_read_b128 of one row's 16-byte
-// chunk, free of bank conflicts under the XOR swizzle.
-//
-// A slice's MFMAs and the addition of its sums to the running total always share a basic block:
-// with a branch between an MFMA and the read of its accumulator the compiler has been seen to
-// leave too few wait states, and the read then returned a stale value.
+// Staging.  Operands reach LDS by 16-byte direct-to-LDS buffer loads (no registers, no VALU),
+// each instruction fetching whole 128-byte rows where it can (strided half-row fetches measured
+// at about 60 % of the rate).  MFMA operands are ds_read_b128 of one row's 16-byte chunk, the
+// chunks of each row permuted so that every read is free of bank conflicts.  The tiled kernels'
+// K loops are unrolled at compile time, so every step is straight-line code, and a slice's MFMAs
+// and the addition of its sums to the running total always share a basic block: with a branch
+// between an MFMA and the read of its accumulator the compiler has been seen to leave too few
+// wait states, and the read then returned a stale value.
 //
 // Placement.  Workgroup i runs on XCD i % 8.  Each XCD owns every eighth tile row (every XCD
 // then reads W whole and an eighth of A) or an eighth of the tile columns (an eighth of W, all of A);
@@ -53,67 +45,20 @@
 namespace mtd {
 namespace {
 
-constexpr int kTM = 128;    // tile rows (tokens)
-constexpr int kTN = 128;    // tile columns (output features)
-constexpr int kTK = 64;     // K per stage
-constexpr int kThreads = 256;
-constexpr int kSliceBytes = kTM * kTK * 2;  // 16 KiB per operand per stage
-// Summation order, the same in all three kernels: K is cut into slices of kKSlice; each slice's
+// Summation order, the same in all the kernels: K is cut into slices of kKSlice; each slice's
 // products are accumulated by one chain of MFMAs starting from zero, and the slice sums are then
 // added in slice order to a running total that starts from zero.  So a token's outputs never
 // depend on how many tokens share the call or which kernel serves it.
 constexpr int kKSlice = 128;
+// Groups of kSliceGroup consecutive slices (1024 inputs) are summed first, each in slice order
+// from zero, and the group totals are then added in order to a total that starts from zero.  The
+// QKV map (K = 1024) is one group; the output map (K = 2048) is two, which proj_ksplit_kernel
+// gives to two sets of waves.
+constexpr int kSliceGroup = 8;
 constexpr int kSkinnyRows = 64;  // calls with at most this many tokens use proj_skinny_kernel
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef const __attribute__((address_space(1))) void global_cvoid_t;
-
-// Byte offset in a staged slice of the 16-byte slot (row r, chunk c).
-__device__ __forceinline__ int slot_bytes(int r, int c) {
-  return 16 * (512 * (c >> 2) + 4 * r + ((c & 3) ^ ((r >> 2) & 3)));
-}
-
-// Direct-to-LDS copy of rows row0 .. row0+127, columns k0 .. k0+63 of a bf16 matrix with leading
-// dimension ld.  Instruction i (4 per wave) fills slots 64 i .. 64 i + 63: column group i / 8,
-// rows 16 (i % 8) + lane / 4.  Rows at or past rows_valid re-read the last valid row.
-__device__ __forceinline__ void dma_slice(const uint16_t* __restrict__ m, int ld, int row0,
-                                          int rows_valid, int k0, uint8_t* lds, int wave, int lane) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int i = 4 * wave + j;
-    const int r = 16 * (i & 7) + (lane >> 2);
-    const int c = 4 * (i >> 3) + ((lane & 3) ^ ((r >> 2) & 3));
-    const int rs = r < rows_valid ? r : rows_valid - 1;
-    __builtin_amdgcn_global_load_lds((global_cvoid_t*)(m + (size_t)(row0 + rs) * ld + k0 + 8 * c),
-                                     (lds_void_t*)(lds + i * 1024), 16, 0, 0);
-  }
-}
-
-// float32 A slice through registers: wave w, load j covers rows 32w + 4j + lane/16, floats
-// 4 (lane%16) .. +3 of the 64.
-struct F32Slice {
-  float4 v[8];
-};
-
-__device__ __forceinline__ void load_f32_slice(F32Slice& s, const float* __restrict__ a, int ld,
-                                               int row0, int rows_valid, int k0, int wave, int lane) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = 32 * wave + 4 * j + (lane >> 4);
-    const int rs = r < rows_valid ? r : rows_valid - 1;
-    s.v[j] = *reinterpret_cast<const float4*>(a + (size_t)(row0 + rs) * ld + k0 + 4 * (lane & 15));
-  }
-}
-
-__device__ __forceinline__ void store_f32_slice(const F32Slice& s, uint8_t* lds, int wave, int lane) {
-  const int f = lane & 15;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = 32 * wave + 4 * j + (lane >> 4);
-    const uint2 packed = make_uint2(pack_bf16x2(s.v[j].x, s.v[j].y), pack_bf16x2(s.v[j].z, s.v[j].w));
-    *reinterpret_cast<uint2*>(lds + slot_bytes(r, f >> 1) + 8 * (f & 1)) = packed;
-  }
-}
 
 // Where the columns of C go: columns [lo_r, lo_{r+1}) of region r land in dst[r] (bf16, leading
 // dimension ld[r]) at column n - lo_r.  One region for the output projection, three for QKV.
@@ -145,115 +90,6 @@ __device__ __forceinline__ void tile_of(int id, int rows, int tm_rows, int n_tm,
     tm = id / n_tn;
     tn = id % n_tn;
   }
-}
-
-// Many tokens, float32 A (the output map): a 128 x 128 tile per workgroup of 4 waves, two
-// workgroups per CU; see Work split and Staging above.
-__global__ __launch_bounds__(kThreads, 2) void proj_f32a_kernel(const float* __restrict__ a, int lda, int rows,
-                                                                const uint16_t* __restrict__ w, int k_dim,
-                                                                int n_tm, int n_tn, int rows_major, OutMap out) {
-  // One array per stage: with the stage known at compile time, the compiler can see that the
-  // loads into one stage never touch the LDS being read from the other, and does not wait for them.
-  __shared__ __attribute__((aligned(1024))) uint8_t s_a0[kSliceBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t s_a1[kSliceBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t s_w0[kSliceBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t s_w1[kSliceBytes];
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-
-  int tm, tn;
-  tile_of(blockIdx.x, rows, kTM, n_tm, n_tn, rows_major, tm, tn);
-  if (tm >= n_tm || tn >= n_tn) return;  // whole workgroup, before any barrier
-  const int row0 = tm * kTM;
-  const int col0 = tn * kTN;
-  const int rows_valid = min(kTM, rows - row0);
-
-  const int wm = wave >> 1, wn = wave & 1;
-  const int n = lane & 31, hk = lane >> 5;
-  // ds_read_b128 bases: row 64 wm + n (A) or 64 wn + n (W), chunk 2 ks + hk, for ks even / odd.
-  int abase[2], wbase[2];
-#pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    const int sw = ((2 * e + hk) ^ ((n >> 2) & 3)) * 16;
-    abase[e] = 64 * (64 * wm + n) + sw;
-    wbase[e] = 64 * (64 * wn + n) + sw;
-  }
-
-  floatx16_t acc[2][2], sum[2][2];  // the current K slice; the slices before it
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = sum[i][j][v] = 0.f;
-
-  const int nk = k_dim / kTK;  // even (k_dim is a multiple of kKSlice)
-  F32Slice fa;
-  // K step kt: stage (cur_a, cur_w) holds slice kt; slice kt+1 goes to (nxt_a, nxt_w).  A slice's
-  // MFMAs and its addition to the total share a basic block (fold is a compile-time flag).
-  auto step = [&](auto fold, int kt, const uint8_t* cur_a, const uint8_t* cur_w, uint8_t* nxt_a,
-                  uint8_t* nxt_w) __attribute__((always_inline)) {
-    __syncthreads();  // the current stage complete for every wave; the other no longer read
-    if (kt + 1 < nk) {
-      dma_slice(w, k_dim, col0, kTN, (kt + 1) * kTK, nxt_w, wave, lane);
-      load_f32_slice(fa, a, lda, row0, rows_valid, (kt + 1) * kTK, wave, lane);
-    }
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      bf16x8_t af[2], wf[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        af[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(
-                                                 cur_a + abase[ks & 1] + 8192 * (ks >> 1) + 2048 * i));
-        wf[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(
-                                                 cur_w + wbase[ks & 1] + 8192 * (ks >> 1) + 2048 * i));
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], wf[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) store_f32_slice(fa, nxt_a, wave, lane);
-    if constexpr (decltype(fold)::value) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            sum[i][j][v] += acc[i][j][v];
-            acc[i][j][v] = 0.f;
-          }
-    }
-  };
-
-  dma_slice(w, k_dim, col0, kTN, 0, s_w0, wave, lane);
-  load_f32_slice(fa, a, lda, row0, rows_valid, 0, wave, lane);
-  store_f32_slice(fa, s_a0, wave, lane);
-  static_assert(kKSlice == 2 * kTK, "one K slice = the two steps of a loop trip");
-  for (int kt = 0; kt < nk; kt += 2) {
-    step(std::false_type{}, kt, s_a0, s_w0, s_a1, s_w1);
-    step(std::true_type{}, kt + 1, s_a1, s_w1, s_a0, s_w0);
-  }
-
-  // Epilogue: accumulator element v of block (i, j) is C[row0 + 64wm + 32i + 8(v/4) + 4hk + v%4]
-  // [col0 + 64wn + 32j + n].
-  uint16_t* dst = out.dst[0];
-  const int ld = out.ld[0];
-  const int cbase = col0 + 64 * wn + n;
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int r = 64 * wm + 32 * i + 8 * (v >> 2) + 4 * hk + (v & 3);
-      if (r < rows_valid) {
-        uint16_t* drow = dst + (size_t)(row0 + r) * ld + cbase;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) drow[32 * j] = (uint16_t)pack_bf16x2(sum[i][j][v], 0.f);
-      }
-    }
 }
 
 // Many tokens, bf16 A (the QKV map): a 256 x 128 tile per workgroup of 8 waves, two per SIMD,
@@ -487,6 +323,219 @@ __global__ __launch_bounds__(kWThreads, 1) void proj_wide_kernel(const uint16_t*
     }
 }
 
+// Many tokens, float32 A (the output map): a 128 x 128 tile per workgroup of 8 waves, two per
+// SIMD, with K split between them: waves 0-3 take the first 1024 inputs and waves 4-7 the last
+// 1024, each wave a 64 x 64 block (wave w: rows 64 ((w % 4) / 2), columns 64 (w % 2)) as 2 x 2 MFMA
+// blocks.  The two halves' totals meet in LDS at the end.  Against a whole-K tile of 4 waves this
+// doubles the waves per CU (the 264 tiles of a 4127-token call give one workgroup per CU) without
+// more staged bytes per flop.  K advances 32 per half at a time through a ring of three 48 KiB
+// stages, the DMA two stages ahead: per half, the float32 A block (128 rows of 128 bytes, whole
+// cache lines) and the W block (128 rows of 64 bytes).  A stays float32 in LDS; each MFMA operand
+// is read as two 16-byte chunks and rounded to bf16 in registers.
+constexpr int kOM = 128;       // tile rows (tokens)
+constexpr int kON = 128;       // tile columns
+constexpr int kOK = 32;        // K per stage and half
+constexpr int kOStages = 3;
+constexpr int kOWaves = 8;
+constexpr int kOThreads = 64 * kOWaves;
+constexpr int kOHalf = kOM * kOK * 4;        // float32 A block of one half and stage: 16 KiB
+constexpr int kOHalfW = kON * kOK * 2;       // W block of one half and stage: 8 KiB
+constexpr int kOLoadsA = 2 * kOM / 8 / kOWaves;   // A: 8 rows per instruction, both halves
+constexpr int kOLoadsW = 2 * kON / 16 / kOWaves;  // W: 16 rows per instruction, both halves
+constexpr int kOLoads = kOLoadsA + kOLoadsW;
+
+// Byte offset of 16-byte chunk c of row r in a block with 64-byte rows: chunks permuted by
+// (r/4) % 4, so that one chunk of 16 consecutive rows covers every bank once.
+__device__ __forceinline__ int slot64(int r, int c) { return 16 * (4 * r + (c ^ ((r >> 2) & 3))); }
+
+template <int kK>
+__global__ __launch_bounds__(kOThreads, 1) void proj_ksplit_kernel(const float* __restrict__ a, int lda, int rows,
+                                                                  const uint16_t* __restrict__ w, int n_tm,
+                                                                  int n_tn, int rows_major, OutMap out) {
+  __shared__ __attribute__((aligned(1024))) uint8_t s_a0[2 * kOHalf];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_a1[2 * kOHalf];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_a2[2 * kOHalf];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_w0[2 * kOHalfW];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_w1[2 * kOHalfW];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_w2[2 * kOHalfW];
+  constexpr int kHalfK = kK / 2;
+  constexpr int nk = kHalfK / kOK;
+  constexpr int kStepsPerSlice = kKSlice / kOK;
+  static_assert(kHalfK == kSliceGroup * kKSlice, "each half is one group of K slices");
+  static_assert(nk % kStepsPerSlice == 0 && nk >= kOStages, "whole slices of whole steps");
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+
+  int tm, tn;
+  tile_of(blockIdx.x, rows, kOM, n_tm, n_tn, rows_major, tm, tn);
+  if (tm >= n_tm || tn >= n_tn) return;  // whole workgroup, before any barrier
+  const int row0 = tm * kOM;
+  const int col0 = tn * kON;
+  const int rows_valid = min(kOM, rows - row0);
+
+  const int half = wave >> 2;
+  const int wm = (wave >> 1) & 1, wn = wave & 1;
+  const int n = lane & 31, hk = lane >> 5;
+  // LDS bases of k-step ks: A row 64 wm + n, float chunks 4 ks + 2 hk and + 1 (4 floats each);
+  // W row 64 wn + n, chunk 2 ks + hk; each within this half's block.
+  int abase[2][2], wbase[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) abase[ks][e] = half * kOHalf + slot128(64 * wm + n, 4 * ks + 2 * hk + e);
+    wbase[ks] = half * kOHalfW + slot64(64 * wn + n, 2 * ks + hk);
+  }
+
+  floatx16_t acc[2][2], sum[2][2];  // the current K slice; the slices before it (this half)
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = sum[i][j][v] = 0.f;
+
+  // DMA of one stage: buffer loads with per-lane byte offsets fixed for the whole K loop and the
+  // step's column in the scalar offset.  A instruction i: half i / 16, rows 8 (i % 16) + lane / 8;
+  // W instruction i: half i / 8, rows 16 (i % 8) + lane / 4.  Rows past rows_valid re-read the
+  // last valid row.
+  const __amdgpu_buffer_rsrc_t rsrc_a = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(a + (size_t)row0 * lda), (short)0, rows_valid * lda * 4, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rsrc_w = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(w + (size_t)col0 * kK), (short)0, kON * kK * 2, kBufferWord3);
+  uint32_t off_a[kOLoadsA], off_w[kOLoadsW];
+#pragma unroll
+  for (int j = 0; j < kOLoadsA; ++j) {
+    const int i = kOLoadsA * wave + j;
+    const int r = 8 * (i % 16) + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    const int rs = r < rows_valid ? r : rows_valid - 1;
+    off_a[j] = (uint32_t)(rs * lda + (i / 16) * kHalfK + 4 * c) * 4u;
+  }
+#pragma unroll
+  for (int j = 0; j < kOLoadsW; ++j) {
+    const int i = kOLoadsW * wave + j;
+    const int r = 16 * (i % 8) + (lane >> 2);
+    const int c = (lane & 3) ^ ((r >> 2) & 3);
+    off_w[j] = (uint32_t)(r * kK + (i / 8) * kHalfK + 8 * c) * 2u;
+  }
+  uint8_t* const sa[kOStages] = {s_a0, s_a1, s_a2};
+  uint8_t* const sw[kOStages] = {s_w0, s_w1, s_w2};
+  auto issue = [&](int kt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < kOLoadsA; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_a, (lds_void_t*)(sa[kt % kOStages] + (kOLoadsA * wave + j) * 1024),
+                                               16, off_a[j], kt * kOK * 4, 0, 0);
+#pragma unroll
+    for (int j = 0; j < kOLoadsW; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_w, (lds_void_t*)(sw[kt % kOStages] + (kOLoadsW * wave + j) * 1024),
+                                               16, off_w[j], kt * kOK * 2, 0, 0);
+  };
+  // Step KT on stage KT % 3, as in proj_wide_kernel; kLive: the wave's first kLive 32-row blocks
+  // hold tokens (2 but in a partly filled tile).
+  auto run = [&](auto live) __attribute__((always_inline)) {
+    constexpr int kLive = decltype(live)::value;
+    for_each_index(
+        [&](auto kt_) __attribute__((always_inline)) {
+          constexpr int KT = decltype(kt_)::value;
+          constexpr bool kIssue = KT + 2 < nk;
+          __builtin_amdgcn_sched_barrier(0);
+          __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(KT + 1 < nk ? kOLoads : 0));
+          asm volatile("" ::: "memory");
+          __builtin_amdgcn_s_barrier();
+          asm volatile("" ::: "memory");
+          if constexpr (kIssue) issue(KT + 2);
+          const uint8_t* cur_a = sa[KT % kOStages];
+          const uint8_t* cur_w = sw[KT % kOStages];
+          bf16x8_t af[2][2], wf[2][2];
+          auto read = [&](int ks, bf16x8_t(&a_f)[2], bf16x8_t(&w_f)[2]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < kLive; ++i) {
+              const float4 lo = *reinterpret_cast<const float4*>(cur_a + abase[ks][0] + 4096 * i);
+              const float4 hi = *reinterpret_cast<const float4*>(cur_a + abase[ks][1] + 4096 * i);
+              a_f[i] = __builtin_bit_cast(bf16x8_t, make_uint4(pack_bf16x2(lo.x, lo.y), pack_bf16x2(lo.z, lo.w),
+                                                               pack_bf16x2(hi.x, hi.y), pack_bf16x2(hi.z, hi.w)));
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+              w_f[j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(cur_w + wbase[ks] + 2048 * j));
+          };
+          if constexpr (kLive > 0) read(0, af[0], wf[0]);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            if constexpr (kLive > 0)
+              if (ks < 1) read(ks + 1, af[1], wf[1]);
+#pragma unroll
+            for (int i = 0; i < kLive; ++i)
+#pragma unroll
+              for (int j = 0; j < 2; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks][i], wf[ks][j], acc[i][j], 0, 0, 0);
+            if (ks == 0)
+              interleave<2 * kLive, (kIssue ? kOLoads : 0), (kLive > 0 ? 2 * kLive + 2 : 0)>();
+            else
+              interleave<2 * kLive, 0, 0>();
+          }
+          if constexpr ((KT + 1) % kStepsPerSlice == 0) {
+#pragma unroll
+            for (int i = 0; i < kLive; ++i)
+#pragma unroll
+              for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                  sum[i][j][v] += acc[i][j][v];
+                  acc[i][j][v] = 0.f;
+                }
+          }
+        },
+        std::make_integer_sequence<int, nk>{});
+  };
+
+  issue(0);
+  issue(1);
+  const int live_blocks = min(2, max(0, (rows_valid - 64 * wm + 31) / 32));  // uniform per wave
+  switch (live_blocks) {
+    case 2: run(std::integral_constant<int, 2>{}); break;
+    case 1: run(std::integral_constant<int, 1>{}); break;
+    default: run(std::integral_constant<int, 0>{}); break;
+  }
+
+  // The second half's totals go through LDS to the waves of the first half, which add them to
+  // their own: (0 + first) + second, the order proj_skinny_kernel uses.
+  __syncthreads();  // every wave is done with the stages
+  // Row block i of the second half's totals goes to stage i's A array (32 KiB each):
+  // [wave of the half][column block][accumulator element][lane].
+  float* const s_sum[2] = {reinterpret_cast<float*>(s_a0), reinterpret_cast<float*>(s_a1)};
+  const int wq = wave & 3;
+  if (half == 1) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s_sum[i][((wq * 2 + j) * 16 + v) * 64 + lane] = sum[i][j][v];
+  }
+  __syncthreads();
+  if (half == 1) return;
+  uint16_t* dst = out.dst[0];
+  const int ld = out.ld[0];
+  const int cbase = col0 + 64 * wn + n;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int r = 64 * wm + 32 * i + 8 * (v >> 2) + 4 * hk + (v & 3);
+      if (r < rows_valid) {
+        uint16_t* drow = dst + (size_t)(row0 + r) * ld + cbase;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const float total = (0.f + sum[i][j][v]) + s_sum[i][((wq * 2 + j) * 16 + v) * 64 + lane];
+          drow[32 * j] = (uint16_t)pack_bf16x2(total, 0.f);
+        }
+      }
+    }
+}
+
 // Few tokens (at most 64): the weights dominate the bytes, so the grid is spread over K instead
 // of tokens.  Workgroup (column block x, row block y) = 32 columns of W against 32 tokens, 8
 // waves; wave w takes the K slices w * q .. w * q + q - 1 (q = k_dim / kKSlice / 8: 1 for QKV,
@@ -599,14 +648,18 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void proj_skinny_kernel(
     const int rr = 8 * (v >> 2) + 4 * (l >> 5) + (v & 3);
     if (rr >= rows_valid) continue;
     float total = 0.f;
-    for (int sl = 0; sl < n_slices; ++sl) total += s_part[(sl * 16 + v) * 64 + l];
+    for (int g0 = 0; g0 < n_slices; g0 += kSliceGroup) {
+      float group = 0.f;
+      for (int sl = g0; sl < g0 + kSliceGroup; ++sl) group += s_part[(sl * 16 + v) * 64 + l];
+      total += group;
+    }
     dst[(size_t)(row0 + rr) * ld + col0 - out.lo[reg] + (l & 31)] = (uint16_t)pack_bf16x2(total, 0.f);
   }
 }
 
 // Workgroups launched for the tiles of `rows` rows x n_tn tile columns.  Rows owned by XCD: whole
 // tile rows padded to groups of 8, plus a partly filled last row dealt out over the XCDs by column.
-int grid_tiles(int rows, int n_tn, int rows_major, int tm_rows = kTM) {
+int grid_tiles(int rows, int n_tn, int rows_major, int tm_rows) {
   const int n_tm = (rows + tm_rows - 1) / tm_rows;
   if (!rows_major) return n_tm * n_tn;
   const int n_full = rows / tm_rows;
@@ -621,6 +674,23 @@ int rows_major_split(int rows, size_t a_row_bytes, size_t w_bytes) {
 
 }  // namespace
 
+// A call's rows: whole tiles go to the tiled kernel; a last partial tile of at most kSkinnyRows
+// rows goes to proj_skinny_kernel in a second launch (both give a token the same bits), since as
+// a tile of its own it would take a whole extra round of the grid for a few rows.
+struct RowSplit {
+  int tiled, tail;
+};
+RowSplit split_rows(int n_tok, int tile_rows) {
+  const int rem = n_tok % tile_rows;
+  if (n_tok > tile_rows && rem > 0 && rem <= kSkinnyRows) return {n_tok - rem, rem};
+  return {n_tok, 0};
+}
+
+OutMap shift_rows(OutMap om, int rows) {
+  for (int r = 0; r < 3; ++r) om.dst[r] += (size_t)rows * om.ld[r];
+  return om;
+}
+
 hipError_t launch_qkv_proj(const uint16_t* x, const uint16_t* w_qkv, int n_tok, uint16_t* q,
                            uint16_t* k, uint16_t* v, hipStream_t stream) {
   constexpr int kN = (kQHeads + 2 * kKvHeads) * kHeadDim;
@@ -633,38 +703,40 @@ hipError_t launch_qkv_proj(const uint16_t* x, const uint16_t* w_qkv, int n_tok, 
   om.lo[0] = 0;
   om.lo[1] = kQHeads * kHeadDim;
   om.lo[2] = (kQHeads + kKvHeads) * kHeadDim;
-  if (n_tok <= kSkinnyRows) {
-    proj_skinny_kernel<false><<<dim3(kN / 32, (n_tok + 31) / 32), dim3(64 * kSkinnyWaves), 0, stream>>>(
-        x, kHidden, n_tok, w_qkv, kHidden, om);
-    return hipGetLastError();
+  const RowSplit rs = n_tok <= kSkinnyRows ? RowSplit{0, n_tok} : split_rows(n_tok, kWM);
+  if (rs.tiled > 0) {
+    const int rows_major = rows_major_split(rs.tiled, kHidden * 2, (size_t)kN * kHidden * 2);
+    const int n_wm = (rs.tiled + kWM - 1) / kWM;
+    const int n_wn = kN / kWN;
+    proj_wide_kernel<kHidden><<<dim3(grid_tiles(rs.tiled, n_wn, rows_major, kWM)), dim3(kWThreads), 0, stream>>>(
+        x, kHidden, rs.tiled, w_qkv, n_wm, n_wn, rows_major, om);
   }
-  const int rows_major = rows_major_split(n_tok, kHidden * 2, (size_t)kN * kHidden * 2);
-  const int n_wm = (n_tok + kWM - 1) / kWM;
-  const int n_wn = kN / kWN;
-  proj_wide_kernel<kHidden><<<dim3(grid_tiles(n_tok, n_wn, rows_major, kWM)), dim3(kWThreads), 0, stream>>>(
-      x, kHidden, n_tok, w_qkv, n_wm, n_wn, rows_major, om);
+  if (rs.tail > 0)
+    proj_skinny_kernel<false><<<dim3(kN / 32, (rs.tail + 31) / 32), dim3(64 * kSkinnyWaves), 0, stream>>>(
+        x + (size_t)rs.tiled * kHidden, kHidden, rs.tail, w_qkv, kHidden, shift_rows(om, rs.tiled));
   return hipGetLastError();
 }
 
 hipError_t launch_o_proj(const float* attn, const uint16_t* w_o, int n_tok, uint16_t* out,
                          hipStream_t stream) {
   constexpr int kK = kQHeads * kHeadDim;
-  const int n_tm = (n_tok + kTM - 1) / kTM;
-  const int n_tn = kHidden / kTN;
   OutMap om;
   for (int r = 0; r < 3; ++r) {
     om.dst[r] = out;
     om.ld[r] = kHidden;
     om.lo[r] = 0;
   }
-  if (n_tok <= kSkinnyRows) {
-    proj_skinny_kernel<true><<<dim3(kHidden / 32, (n_tok + 31) / 32), dim3(64 * kSkinnyWaves), 0, stream>>>(
-        attn, kK, n_tok, w_o, kK, om);
-    return hipGetLastError();
+  const RowSplit rs = n_tok <= kSkinnyRows ? RowSplit{0, n_tok} : split_rows(n_tok, kOM);
+  if (rs.tiled > 0) {
+    const int n_tm = (rs.tiled + kOM - 1) / kOM;
+    const int n_tn = kHidden / kON;
+    const int rows_major = rows_major_split(rs.tiled, kK * 4, (size_t)kHidden * kK * 2);
+    proj_ksplit_kernel<kK><<<dim3(grid_tiles(rs.tiled, n_tn, rows_major, kOM)), dim3(kOThreads), 0, stream>>>(
+        attn, kK, rs.tiled, w_o, n_tm, n_tn, rows_major, om);
   }
-  const int rows_major = rows_major_split(n_tok, kK * 4, (size_t)kHidden * kK * 2);
-  proj_f32a_kernel<<<dim3(grid_tiles(n_tok, n_tn, rows_major)), dim3(kThreads), 0, stream>>>(
-      attn, kK, n_tok, w_o, kK, n_tm, n_tn, rows_major, om);
+  if (rs.tail > 0)
+    proj_skinny_kernel<true><<<dim3(kHidden / 32, (rs.tail + 31) / 32), dim3(64 * kSkinnyWaves), 0, stream>>>(
+        attn + (size_t)rs.tiled * kK, kK, rs.tail, w_o, kK, shift_rows(om, rs.tiled));
   return hipGetLastError();
 }
 

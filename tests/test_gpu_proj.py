@@ -67,7 +67,7 @@ def test_qkv_proj_matches_oracle(n_tok):
     _check("v", v, v_ref, bound[:, nq + nkv:].reshape(v_ref.shape))
 
 
-@pytest.mark.parametrize("n_tok", [1, 8, 9, 37, 64, 65, 300, 439])
+@pytest.mark.parametrize("n_tok", [1, 8, 9, 37, 64, 65, 128, 129, 255, 300, 439, 1000])
 def test_o_proj_matches_oracle(n_tok):
     log(f"output projection n_tok={n_tok}")
     _, w_o = _weights("cuda")
