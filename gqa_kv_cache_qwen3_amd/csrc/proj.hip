@@ -31,11 +31,14 @@
 // between an MFMA and the read of its accumulator the compiler has been seen to leave too few
 // wait states, and the read then returned a stale value.
 //
-// Placement.  Workgroup i runs on XCD i % 8.  Each XCD owns every eighth tile row (every XCD
-// then reads W whole and an eighth of A) or an eighth of the tile columns (an eighth of W, all of A);
-// the host picks the split whose replicated operand is the smaller.  Within an XCD the owned
-// index varies fastest, so the workgroups in flight together touch few tiles of the replicated
-// operand and each is brought into the XCD's L2 once rather than once per owned row.
+// Placement.  Workgroup i runs on XCD i % 8, and each XCD has its own L2.  The QKV map splits both
+// ways when its tile rows come in fours: XCD x owns the tile rows = x / 2 (mod 4) and half x % 2
+// of the tile columns, so A is read by 2 XCDs and W by 4.  Otherwise each XCD owns every eighth
+// tile row (every XCD then reads W whole and an eighth of A) or an eighth of the tile columns (an
+// eighth of W, all of A), whichever replicates the smaller operand; the output map's float32 A is
+// the larger, so its XCDs own rows.  Within an XCD the owned row index varies fastest, so the
+// workgroups in flight together touch few tiles of the replicated operand and each is brought
+// into the XCD's L2 once rather than once per owned row.
 #include <type_traits>
 #include <utility>
 
@@ -68,10 +71,20 @@ struct OutMap {
   int lo[3];
 };
 
+constexpr int kSplit2D = 2;  // tile placement: rows and columns both split over the XCDs
+
 // Tile (tm, tn) of workgroup id for tiles of tm_rows rows; see Placement.  tm == n_tm: no tile.
 __device__ __forceinline__ void tile_of(int id, int rows, int tm_rows, int n_tm, int n_tn, int rows_major,
                                         int& tm, int& tn) {
   const int x = id % 8, local = id / 8;
+  if (rows_major == kSplit2D) {
+    // XCD x owns the tile rows = x / 2 (mod 4) and half x % 2 of the tile columns: each operand is
+    // read by fewer XCDs (A by 2, W by 4) than with either one-sided split (A by 1, W by 8).
+    const int per_col = n_tn / 2;
+    tm = x / 2 + 4 * (local % (n_tm / 4));
+    tn = (x % 2) * per_col + local / (n_tm / 4);
+    return;
+  }
   if (rows_major) {
     const int n_full = rows / tm_rows;
     const int m_per = (n_full + 7) / 8;
@@ -661,7 +674,7 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void proj_skinny_kernel(
 // tile rows padded to groups of 8, plus a partly filled last row dealt out over the XCDs by column.
 int grid_tiles(int rows, int n_tn, int rows_major, int tm_rows) {
   const int n_tm = (rows + tm_rows - 1) / tm_rows;
-  if (!rows_major) return n_tm * n_tn;
+  if (!rows_major || rows_major == kSplit2D) return n_tm * n_tn;
   const int n_full = rows / tm_rows;
   const int tail = n_tm > n_full ? (n_tn + 7) / 8 : 0;
   return 8 * (((n_full + 7) / 8) * n_tn + tail);
@@ -705,9 +718,11 @@ hipError_t launch_qkv_proj(const uint16_t* x, const uint16_t* w_qkv, int n_tok, 
   om.lo[2] = (kQHeads + kKvHeads) * kHeadDim;
   const RowSplit rs = n_tok <= kSkinnyRows ? RowSplit{0, n_tok} : split_rows(n_tok, kWM);
   if (rs.tiled > 0) {
-    const int rows_major = rows_major_split(rs.tiled, kHidden * 2, (size_t)kN * kHidden * 2);
     const int n_wm = (rs.tiled + kWM - 1) / kWM;
     const int n_wn = kN / kWN;
+    const int rows_major = n_wm % 4 == 0 && n_wn % 2 == 0
+                               ? kSplit2D
+                               : rows_major_split(rs.tiled, kHidden * 2, (size_t)kN * kHidden * 2);
     proj_wide_kernel<kHidden><<<dim3(grid_tiles(rs.tiled, n_wn, rows_major, kWM)), dim3(kWThreads), 0, stream>>>(
         x, kHidden, rs.tiled, w_qkv, n_wm, n_wn, rows_major, om);
   }

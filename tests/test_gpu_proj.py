@@ -9,9 +9,10 @@ S = sum |x_i w_i| the accumulated error is at most K 2^-24 S, so
 
 The output projection rounds its float32 input to bf16 first; the oracle takes the same
 decision in the same precision (float32 -> bf16, nearest even), so both multiply the same bf16
-values.  Sizes: single tokens, ragged counts that leave a partial 128-row tile, the tiny
-workload's 439-token prompt, the full-depth decode batch (64), and a whole 4096-token prefill
-chunk.
+values.  Sizes: single tokens; counts around the tile heights (256 rows for QKV, 128 for the
+output map) that leave a partial tile, or a tail of exactly 64 or 65 rows (a tail of at most 64
+rows goes to the few-token kernel); the tiny workload's 439-token prompt; the full-depth decode
+batch (64); and the mixed step's 4127 new tokens.
 """
 
 import numpy as np
@@ -50,7 +51,7 @@ def _weights(dev):
     return W.projection_weights(W.torch_seed(TAG, 0), dev)
 
 
-@pytest.mark.parametrize("n_tok", [1, 8, 9, 37, 64, 65, 128, 255, 256, 257, 300, 439, 1000])
+@pytest.mark.parametrize("n_tok", [1, 8, 9, 37, 64, 65, 128, 255, 256, 257, 300, 320, 321, 439, 1000])
 def test_qkv_proj_matches_oracle(n_tok):
     log(f"qkv projection n_tok={n_tok}")
     w_qkv, _ = _weights("cuda")
@@ -67,7 +68,7 @@ def test_qkv_proj_matches_oracle(n_tok):
     _check("v", v, v_ref, bound[:, nq + nkv:].reshape(v_ref.shape))
 
 
-@pytest.mark.parametrize("n_tok", [1, 8, 9, 37, 64, 65, 128, 129, 255, 300, 439, 1000])
+@pytest.mark.parametrize("n_tok", [1, 8, 9, 37, 64, 65, 128, 129, 192, 193, 255, 300, 439, 1000])
 def test_o_proj_matches_oracle(n_tok):
     log(f"output projection n_tok={n_tok}")
     _, w_o = _weights("cuda")
@@ -109,17 +110,19 @@ def test_projections_full_chunk():
 
 
 def test_token_results_do_not_depend_on_the_batch():
-    """Rows of a 300-token call equal, bit for bit, the same tokens projected alone or in a
-    different-sized call, whichever kernel serves the call (at most 64 tokens: K split over the
-    waves; more: 128 x 128 tiles): both sum each 128-wide K slice with one MFMA chain from zero
-    and add the slice sums in order."""
+    """Rows of an 1100-token call equal, bit for bit, the same tokens projected alone or in a
+    different-sized call, whichever kernel serves the rows (at most 64 tokens, or a tail of at
+    most 64 rows: K split over the waves of one workgroup; more: 256 x 128 tiles for QKV, 128 x 128
+    tiles with K split in halves for the output map): all of them sum each 128-wide K slice with
+    one MFMA chain from zero, add the slice sums of each 1024-wide group in order, and add the
+    group sums in order."""
     log("projections: batch invariance")
     w_qkv, w_o = _weights("cuda")
-    x = W.normal_bf16((300, W.HIDDEN), W.torch_seed(TAG, 5), "cuda")
-    attn = W.normal_bf16((300, W.HQ, W.HEAD_DIM), W.torch_seed(TAG, 6), "cuda").float()
+    x = W.normal_bf16((1100, W.HIDDEN), W.torch_seed(TAG, 5), "cuda")
+    attn = W.normal_bf16((1100, W.HQ, W.HEAD_DIM), W.torch_seed(TAG, 6), "cuda").float()
     full = mtd.mtd_qkv_proj(x, w_qkv)
     y_full = mtd.mtd_o_proj(attn, w_o)
-    for lo, hi in [(0, 37), (128, 129), (0, 64), (0, 65), (200, 300)]:
+    for lo, hi in [(0, 37), (128, 129), (0, 64), (0, 65), (200, 300), (0, 1000), (1024, 1100), (1088, 1100)]:
         part = mtd.mtd_qkv_proj(x[lo:hi].contiguous(), w_qkv)
         y_part = mtd.mtd_o_proj(attn[lo:hi].contiguous(), w_o)
         for a, b in zip(full, part):
