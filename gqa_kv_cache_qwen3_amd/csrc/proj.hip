@@ -16,9 +16,9 @@
 //
 // Kernels.  Calls with more than 64 tokens run tiled kernels: proj_wide_kernel for the QKV map
 // (256 x 128 tiles) and proj_ksplit_kernel for the output map (128 x 128 tiles with K split
-// between two sets of waves); see their comments.  A last partial tile of at most 64 rows goes to
-// proj_skinny_kernel in a second launch, and so do whole calls of at most 64 tokens: it spreads
-// K over the waves.  All three add the products in one order (fixed K slices and groups of them,
+// between two sets of waves); see their comments.  Calls of at most 64 tokens run
+// proj_skinny_kernel, which spreads K over the waves, and a tiled launch computes a last partial
+// tile of at most 64 rows with the same algorithm in its first workgroups (tail_block).  All three add the products in one order (fixed K slices and groups of them,
 // see kKSlice), so a token's result is the same whatever the token count and whichever kernel
 // runs.  The MFMA is v_mfma_f32_32x32x16_bf16 with fp32 accumulators throughout.
 //
@@ -71,6 +71,12 @@ struct OutMap {
   int lo[3];
 };
 
+// The map for the rows from `rows` on.
+__host__ __device__ __forceinline__ OutMap shift_rows(OutMap om, int rows) {
+  for (int r = 0; r < 3; ++r) om.dst[r] += (size_t)rows * om.ld[r];
+  return om;
+}
+
 constexpr int kSplit2D = 2;  // tile placement: rows and columns both split over the XCDs
 
 // Tile (tm, tn) of workgroup id for tiles of tm_rows rows; see Placement.  tm == n_tm: no tile.
@@ -103,6 +109,157 @@ __device__ __forceinline__ void tile_of(int id, int rows, int tm_rows, int n_tm,
     tm = id / n_tn;
     tn = id % n_tn;
   }
+}
+
+// Few tokens (at most 64): the weights dominate the bytes, so the grid is spread over K instead
+// of tokens.  Workgroup (column block x, row block y) = 32 columns of W against 32 tokens, 8
+// waves; wave w takes the K slices w * q .. w * q + q - 1 (q = k_dim / kKSlice / 8: 1 for QKV,
+// 2 for o_proj).  For each slice the wave stages its 32 x 128 pieces of A and W in its own 16 KiB
+// of LDS with coalesced loads (each direct-to-LDS instruction fetches 8 rows x 128 contiguous
+// bytes; the float32 A comes through registers, 512 contiguous bytes per row, and is rounded to
+// bf16 on the way), then runs the slice's MFMA chain from ds_read_b128 fragments.  The slice sums
+// meet in LDS and are added in slice order.
+//
+// Per-wave staging of a 32-row x 128-column bf16 piece: two column groups of 128 bytes (8 chunks of
+// 16 bytes); the slot of (row r, chunk c) is 256 (c/8) + 8 r + ((c%8) ^ ((r/2)%4)), which keeps
+// the 8 lanes of each ds_read_b128 phase on distinct banks.
+constexpr int kSkinnyWaves = 8;
+constexpr int kSkinnyStage = 16384;  // per wave: the A piece, then the W piece
+
+__device__ __forceinline__ int slot32_bytes(int r, int c) {
+  return 16 * (256 * (c >> 3) + 8 * r + ((c & 7) ^ ((r >> 1) & 3)));
+}
+
+// Direct-to-LDS copy of rows row0 .. row0+31 (at or past rows_valid: the last valid row), columns
+// k0 .. k0+127 of a bf16 matrix: instruction i fills slots 64 i .. 64 i + 63 = column group i / 4,
+// rows 8 (i % 4) + lane / 8.
+__device__ __forceinline__ void dma_piece32(const uint16_t* __restrict__ m, int ld, int row0,
+                                            int rows_valid, int k0, uint8_t* lds, int lane) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = 8 * (i & 3) + (lane >> 3);
+    const int c = 8 * (i >> 2) + ((lane & 7) ^ ((r >> 1) & 3));
+    const int rs = r < rows_valid ? r : rows_valid - 1;
+    __builtin_amdgcn_global_load_lds((global_cvoid_t*)(m + (size_t)(row0 + rs) * ld + k0 + 8 * c),
+                                     (lds_void_t*)(lds + i * 1024), 16, 0, 0);
+  }
+}
+
+// The float32 piece through registers: load j covers row 2j + lane/32, floats 4 (lane%32) .. +3.
+__device__ __forceinline__ void stage_f32_piece32(const float* __restrict__ a, int ld, int row0,
+                                                  int rows_valid, int k0, uint8_t* lds, int lane) {
+  float4 v[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int r = 2 * j + (lane >> 5);
+    const int rs = r < rows_valid ? r : rows_valid - 1;
+    v[j] = *reinterpret_cast<const float4*>(a + (size_t)(row0 + rs) * ld + k0 + 4 * (lane & 31));
+  }
+  const int f = lane & 31;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int r = 2 * j + (lane >> 5);
+    *reinterpret_cast<uint2*>(lds + slot32_bytes(r, f >> 1) + 8 * (f & 1)) =
+        make_uint2(pack_bf16x2(v[j].x, v[j].y), pack_bf16x2(v[j].z, v[j].w));
+  }
+}
+
+// One 32-column x 32-row block of C (column block cb, row block rb) by 8 waves: wave w stages its
+// K slices in its own 16 KiB of LDS (wave_lds), and the slice sums meet in part(slice) (4 KiB per
+// slice, 8 consecutive slices contiguous), which may overlap the waves' stages.
+template <bool kAF32, class WaveLds, class Part>
+__device__ __forceinline__ void skinny_block(const void* __restrict__ a_ptr, int lda, int rows,
+                                             const uint16_t* __restrict__ w, int k_dim, const OutMap& out,
+                                             int cb, int rb, WaveLds wave_lds, Part part) {
+  constexpr int kMaxPerWave = 2;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int n_slices = k_dim / kKSlice;
+  const int per_wave = n_slices / kSkinnyWaves;
+  const int n = lane & 31, hk = lane >> 5;
+  const int col0 = 32 * cb;
+  const int row0 = 32 * rb;
+  const int rows_valid = min(32, rows - row0);
+  uint8_t* a_lds = wave_lds(wave);
+  uint8_t* w_lds = a_lds + kSkinnyStage / 2;
+
+  floatx16_t acc[kMaxPerWave];
+#pragma unroll
+  for (int t = 0; t < kMaxPerWave; ++t) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[t][v] = 0.f;
+    if (t >= per_wave) continue;
+    const int k0 = (wave * per_wave + t) * kKSlice;
+    dma_piece32(w, k_dim, col0, 32, k0, w_lds, lane);
+    if constexpr (kAF32)
+      stage_f32_piece32(static_cast<const float*>(a_ptr), lda, row0, rows_valid, k0, a_lds, lane);
+    else
+      dma_piece32(static_cast<const uint16_t*>(a_ptr), lda, row0, rows_valid, k0, a_lds, lane);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's pieces are in its LDS
+#pragma unroll
+    for (int ks = 0; ks < kKSlice / 16; ++ks) {
+      const int off = slot32_bytes(n, 2 * ks + hk);
+      const bf16x8_t af = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(a_lds + off));
+      const bf16x8_t wf = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(w_lds + off));
+      acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, wf, acc[t], 0, 0, 0);
+    }
+  }
+  __syncthreads();  // every wave is done with its pieces; the LDS now holds the slice sums
+#pragma unroll
+  for (int t = 0; t < kMaxPerWave; ++t) {
+    if (t >= per_wave) continue;
+    float* s_part = part(wave * per_wave + t);  // [accumulator element][lane]
+#pragma unroll
+    for (int v = 0; v < 16; ++v) s_part[v * 64 + lane] = acc[t][v];
+  }
+  __syncthreads();
+
+  // Element e = (accumulator element v, lane l): C[row0 + 8(v/4) + 4(l/32) + v%4][col0 + l%32].
+  const int reg = (col0 >= out.lo[2]) ? 2 : (col0 >= out.lo[1]) ? 1 : 0;
+  uint16_t* dst = out.dst[reg];
+  const int ld = out.ld[reg];
+  for (int e = tid; e < 16 * 64; e += blockDim.x) {
+    const int v = e >> 6, l = e & 63;
+    const int rr = 8 * (v >> 2) + 4 * (l >> 5) + (v & 3);
+    if (rr >= rows_valid) continue;
+    float total = 0.f;
+    for (int g0 = 0; g0 < n_slices; g0 += kSliceGroup) {
+      float group = 0.f;
+      for (int sl = g0; sl < g0 + kSliceGroup; ++sl) group += part(sl)[v * 64 + l];
+      total += group;
+    }
+    dst[(size_t)(row0 + rr) * ld + col0 - out.lo[reg] + (l & 31)] = (uint16_t)pack_bf16x2(total, 0.f);
+  }
+}
+
+// The first tail_blocks workgroups of a tiled launch compute the rows past its tiles (at most 64,
+// see split_rows) with the few-token algorithm, in LDS borrowed from the tiled kernel's stage
+// arrays: wave w stages in a0 / a1 / a2 (two waves each) or w0 / w1, and the slice sums of the
+// first and second 1024-input groups go to a0 and a1.  They come first in the grid, so they run
+// beside the first round of tiles rather than after the last.
+template <bool kAF32>
+__device__ __forceinline__ void tail_block(const void* a_ptr, int lda, int rows, int tail_rows,
+                                           const uint16_t* w, int k_dim, int n_cols, const OutMap& out,
+                                           uint8_t* a0, uint8_t* a1, uint8_t* a2, uint8_t* w0, uint8_t* w1) {
+  const int ncb = n_cols / 32;
+  const void* a_tail = kAF32 ? (const void*)(static_cast<const float*>(a_ptr) + (size_t)rows * lda)
+                             : (const void*)(static_cast<const uint16_t*>(a_ptr) + (size_t)rows * lda);
+  skinny_block<kAF32>(
+      a_tail, lda, tail_rows, w, k_dim, shift_rows(out, rows), blockIdx.x % ncb, blockIdx.x / ncb,
+      [&](int wave) -> uint8_t* {
+        switch (wave) {
+          case 0: return a0;
+          case 1: return a0 + kSkinnyStage;
+          case 2: return a1;
+          case 3: return a1 + kSkinnyStage;
+          case 4: return a2;
+          case 5: return a2 + kSkinnyStage;
+          case 6: return w0;
+          default: return w1;
+        }
+      },
+      [&](int slice) { return reinterpret_cast<float*>(slice < kSliceGroup ? a0 : a1) + (slice % kSliceGroup) * 16 * 64; });
 }
 
 // Many tokens, bf16 A (the QKV map): a 256 x 128 tile per workgroup of 8 waves, two per SIMD,
@@ -198,7 +355,8 @@ constexpr int wait_vm_lgkm0(int n) { return (n & 15) | (7 << 4) | ((n >> 4) << 1
 template <int kK>
 __global__ __launch_bounds__(kWThreads, 1) void proj_wide_kernel(const uint16_t* __restrict__ a, int lda, int rows,
                                                                 const uint16_t* __restrict__ w, int n_tm,
-                                                                int n_tn, int rows_major, OutMap out) {
+                                                                int n_tn, int rows_major, OutMap out,
+                                                                int tail_blocks, int tail_rows) {
   // One array per stage, so that the compiler can see which stage each load and read touches.
   __shared__ __attribute__((aligned(1024))) uint8_t s_a0[kWStageA];
   __shared__ __attribute__((aligned(1024))) uint8_t s_a1[kWStageA];
@@ -213,8 +371,15 @@ __global__ __launch_bounds__(kWThreads, 1) void proj_wide_kernel(const uint16_t*
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
 
+  static_assert(kWStageA >= 2 * kSkinnyStage && kWStageW >= kSkinnyStage && kWThreads == 64 * kSkinnyWaves &&
+                    kWStageA >= kSliceGroup * 16 * 64 * 4,
+                "the tail blocks fit the stage arrays");
+  if ((int)blockIdx.x < tail_blocks) {
+    tail_block<false>(a, lda, rows, tail_rows, w, kK, n_tn * kWN, out, s_a0, s_a1, s_a2, s_w0, s_w1);
+    return;
+  }
   int tm, tn;
-  tile_of(blockIdx.x, rows, kWM, n_tm, n_tn, rows_major, tm, tn);
+  tile_of(blockIdx.x - tail_blocks, rows, kWM, n_tm, n_tn, rows_major, tm, tn);
   if (tm >= n_tm || tn >= n_tn) return;  // whole workgroup, before any barrier
   const int row0 = tm * kWM;
   const int col0 = tn * kWN;
@@ -364,7 +529,8 @@ __device__ __forceinline__ int slot64(int r, int c) { return 16 * (4 * r + (c ^ 
 template <int kK>
 __global__ __launch_bounds__(kOThreads, 1) void proj_ksplit_kernel(const float* __restrict__ a, int lda, int rows,
                                                                   const uint16_t* __restrict__ w, int n_tm,
-                                                                  int n_tn, int rows_major, OutMap out) {
+                                                                  int n_tn, int rows_major, OutMap out,
+                                                                  int tail_blocks, int tail_rows) {
   __shared__ __attribute__((aligned(1024))) uint8_t s_a0[2 * kOHalf];
   __shared__ __attribute__((aligned(1024))) uint8_t s_a1[2 * kOHalf];
   __shared__ __attribute__((aligned(1024))) uint8_t s_a2[2 * kOHalf];
@@ -380,8 +546,15 @@ __global__ __launch_bounds__(kOThreads, 1) void proj_ksplit_kernel(const float* 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
 
+  static_assert(2 * kOHalf >= 2 * kSkinnyStage && 2 * kOHalfW >= kSkinnyStage && kOThreads == 64 * kSkinnyWaves &&
+                    2 * kOHalf >= kSliceGroup * 16 * 64 * 4,
+                "the tail blocks fit the stage arrays");
+  if ((int)blockIdx.x < tail_blocks) {
+    tail_block<true>(a, lda, rows, tail_rows, w, kK, n_tn * kON, out, s_a0, s_a1, s_a2, s_w0, s_w1);
+    return;
+  }
   int tm, tn;
-  tile_of(blockIdx.x, rows, kOM, n_tm, n_tn, rows_major, tm, tn);
+  tile_of(blockIdx.x - tail_blocks, rows, kOM, n_tm, n_tn, rows_major, tm, tn);
   if (tm >= n_tm || tn >= n_tn) return;  // whole workgroup, before any barrier
   const int row0 = tm * kOM;
   const int col0 = tn * kON;
@@ -549,125 +722,15 @@ __global__ __launch_bounds__(kOThreads, 1) void proj_ksplit_kernel(const float* 
     }
 }
 
-// Few tokens (at most 64): the weights dominate the bytes, so the grid is spread over K instead
-// of tokens.  Workgroup (column block x, row block y) = 32 columns of W against 32 tokens, 8
-// waves; wave w takes the K slices w * q .. w * q + q - 1 (q = k_dim / kKSlice / 8: 1 for QKV,
-// 2 for o_proj).  For each slice the wave stages its 32 x 128 pieces of A and W in its own 16 KiB
-// of LDS with coalesced loads (each direct-to-LDS instruction fetches 8 rows x 128 contiguous
-// bytes; the float32 A comes through registers, 512 contiguous bytes per row, and is rounded to
-// bf16 on the way), then runs the slice's MFMA chain from ds_read_b128 fragments.  The slice sums
-// meet in LDS and are added in slice order.
-//
-// Per-wave staging of a 32-row x 128-column bf16 piece: two column groups of 128 bytes (8 chunks of
-// 16 bytes); the slot of (row r, chunk c) is 256 (c/8) + 8 r + ((c%8) ^ ((r/2)%4)), which keeps
-// the 8 lanes of each ds_read_b128 phase on distinct banks.
-constexpr int kSkinnyWaves = 8;
-constexpr int kSkinnyStage = 16384;  // per wave: the A piece, then the W piece
-
-__device__ __forceinline__ int slot32_bytes(int r, int c) {
-  return 16 * (256 * (c >> 3) + 8 * r + ((c & 7) ^ ((r >> 1) & 3)));
-}
-
-// Direct-to-LDS copy of rows row0 .. row0+31 (at or past rows_valid: the last valid row), columns
-// k0 .. k0+127 of a bf16 matrix: instruction i fills slots 64 i .. 64 i + 63 = column group i / 4,
-// rows 8 (i % 4) + lane / 8.
-__device__ __forceinline__ void dma_piece32(const uint16_t* __restrict__ m, int ld, int row0,
-                                            int rows_valid, int k0, uint8_t* lds, int lane) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = 8 * (i & 3) + (lane >> 3);
-    const int c = 8 * (i >> 2) + ((lane & 7) ^ ((r >> 1) & 3));
-    const int rs = r < rows_valid ? r : rows_valid - 1;
-    __builtin_amdgcn_global_load_lds((global_cvoid_t*)(m + (size_t)(row0 + rs) * ld + k0 + 8 * c),
-                                     (lds_void_t*)(lds + i * 1024), 16, 0, 0);
-  }
-}
-
-// The float32 piece through registers: load j covers row 2j + lane/32, floats 4 (lane%32) .. +3.
-__device__ __forceinline__ void stage_f32_piece32(const float* __restrict__ a, int ld, int row0,
-                                                  int rows_valid, int k0, uint8_t* lds, int lane) {
-  float4 v[16];
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int r = 2 * j + (lane >> 5);
-    const int rs = r < rows_valid ? r : rows_valid - 1;
-    v[j] = *reinterpret_cast<const float4*>(a + (size_t)(row0 + rs) * ld + k0 + 4 * (lane & 31));
-  }
-  const int f = lane & 31;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int r = 2 * j + (lane >> 5);
-    *reinterpret_cast<uint2*>(lds + slot32_bytes(r, f >> 1) + 8 * (f & 1)) =
-        make_uint2(pack_bf16x2(v[j].x, v[j].y), pack_bf16x2(v[j].z, v[j].w));
-  }
-}
-
 template <bool kAF32>
 __global__ __launch_bounds__(64 * kSkinnyWaves) void proj_skinny_kernel(
     const void* __restrict__ a_ptr, int lda, int rows, const uint16_t* __restrict__ w, int k_dim,
     OutMap out) {
-  constexpr int kMaxPerWave = 2;
   __shared__ __attribute__((aligned(1024))) uint8_t s_mem[kSkinnyWaves * kSkinnyStage];
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int n_slices = k_dim / kKSlice;
-  const int per_wave = n_slices / kSkinnyWaves;
-  const int n = lane & 31, hk = lane >> 5;
-  const int col0 = 32 * blockIdx.x;
-  const int row0 = 32 * blockIdx.y;
-  const int rows_valid = min(32, rows - row0);
-  uint8_t* a_lds = s_mem + wave * kSkinnyStage;
-  uint8_t* w_lds = a_lds + kSkinnyStage / 2;
-
-  floatx16_t acc[kMaxPerWave];
-#pragma unroll
-  for (int t = 0; t < kMaxPerWave; ++t) {
-#pragma unroll
-    for (int v = 0; v < 16; ++v) acc[t][v] = 0.f;
-    if (t >= per_wave) continue;
-    const int k0 = (wave * per_wave + t) * kKSlice;
-    dma_piece32(w, k_dim, col0, 32, k0, w_lds, lane);
-    if constexpr (kAF32)
-      stage_f32_piece32(static_cast<const float*>(a_ptr), lda, row0, rows_valid, k0, a_lds, lane);
-    else
-      dma_piece32(static_cast<const uint16_t*>(a_ptr), lda, row0, rows_valid, k0, a_lds, lane);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's pieces are in its LDS
-#pragma unroll
-    for (int ks = 0; ks < kKSlice / 16; ++ks) {
-      const int off = slot32_bytes(n, 2 * ks + hk);
-      const bf16x8_t af = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(a_lds + off));
-      const bf16x8_t wf = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(w_lds + off));
-      acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, wf, acc[t], 0, 0, 0);
-    }
-  }
-  __syncthreads();  // every wave is done with its pieces; the LDS now holds the slice sums
-  float* s_part = reinterpret_cast<float*>(s_mem);  // [slice][accumulator element][lane]
-#pragma unroll
-  for (int t = 0; t < kMaxPerWave; ++t) {
-    if (t >= per_wave) continue;
-    const int slice = wave * per_wave + t;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) s_part[(slice * 16 + v) * 64 + lane] = acc[t][v];
-  }
-  __syncthreads();
-
-  // Element e = (accumulator element v, lane l): C[row0 + 8(v/4) + 4(l/32) + v%4][col0 + l%32].
-  const int reg = (col0 >= out.lo[2]) ? 2 : (col0 >= out.lo[1]) ? 1 : 0;
-  uint16_t* dst = out.dst[reg];
-  const int ld = out.ld[reg];
-  for (int e = tid; e < 16 * 64; e += blockDim.x) {
-    const int v = e >> 6, l = e & 63;
-    const int rr = 8 * (v >> 2) + 4 * (l >> 5) + (v & 3);
-    if (rr >= rows_valid) continue;
-    float total = 0.f;
-    for (int g0 = 0; g0 < n_slices; g0 += kSliceGroup) {
-      float group = 0.f;
-      for (int sl = g0; sl < g0 + kSliceGroup; ++sl) group += s_part[(sl * 16 + v) * 64 + l];
-      total += group;
-    }
-    dst[(size_t)(row0 + rr) * ld + col0 - out.lo[reg] + (l & 31)] = (uint16_t)pack_bf16x2(total, 0.f);
-  }
+  skinny_block<kAF32>(
+      a_ptr, lda, rows, w, k_dim, out, blockIdx.x, blockIdx.y,
+      [&](int wave) { return s_mem + wave * kSkinnyStage; },
+      [&](int slice) { return reinterpret_cast<float*>(s_mem) + slice * 16 * 64; });
 }
 
 // Workgroups launched for the tiles of `rows` rows x n_tn tile columns.  Rows owned by XCD: whole
@@ -688,8 +751,9 @@ int rows_major_split(int rows, size_t a_row_bytes, size_t w_bytes) {
 }  // namespace
 
 // A call's rows: whole tiles go to the tiled kernel; a last partial tile of at most kSkinnyRows
-// rows goes to proj_skinny_kernel in a second launch (both give a token the same bits), since as
-// a tile of its own it would take a whole extra round of the grid for a few rows.
+// rows goes to the tiled launch's first workgroups, which run the few-token algorithm (both give a
+// token the same bits), since as a tile of its own it would take a whole extra round of the grid
+// for a few rows.
 struct RowSplit {
   int tiled, tail;
 };
@@ -699,10 +763,6 @@ RowSplit split_rows(int n_tok, int tile_rows) {
   return {n_tok, 0};
 }
 
-OutMap shift_rows(OutMap om, int rows) {
-  for (int r = 0; r < 3; ++r) om.dst[r] += (size_t)rows * om.ld[r];
-  return om;
-}
 
 hipError_t launch_qkv_proj(const uint16_t* x, const uint16_t* w_qkv, int n_tok, uint16_t* q,
                            uint16_t* k, uint16_t* v, hipStream_t stream) {
@@ -723,12 +783,14 @@ hipError_t launch_qkv_proj(const uint16_t* x, const uint16_t* w_qkv, int n_tok, 
     const int rows_major = n_wm % 4 == 0 && n_wn % 2 == 0
                                ? kSplit2D
                                : rows_major_split(rs.tiled, kHidden * 2, (size_t)kN * kHidden * 2);
-    proj_wide_kernel<kHidden><<<dim3(grid_tiles(rs.tiled, n_wn, rows_major, kWM)), dim3(kWThreads), 0, stream>>>(
-        x, kHidden, rs.tiled, w_qkv, n_wm, n_wn, rows_major, om);
-  }
-  if (rs.tail > 0)
+    const int tail_blocks = (kN / 32) * ((rs.tail + 31) / 32);
+    proj_wide_kernel<kHidden>
+        <<<dim3(tail_blocks + grid_tiles(rs.tiled, n_wn, rows_major, kWM)), dim3(kWThreads), 0, stream>>>(
+            x, kHidden, rs.tiled, w_qkv, n_wm, n_wn, rows_major, om, tail_blocks, rs.tail);
+  } else {
     proj_skinny_kernel<false><<<dim3(kN / 32, (rs.tail + 31) / 32), dim3(64 * kSkinnyWaves), 0, stream>>>(
-        x + (size_t)rs.tiled * kHidden, kHidden, rs.tail, w_qkv, kHidden, shift_rows(om, rs.tiled));
+        x, kHidden, rs.tail, w_qkv, kHidden, om);
+  }
   return hipGetLastError();
 }
 
@@ -746,12 +808,14 @@ hipError_t launch_o_proj(const float* attn, const uint16_t* w_o, int n_tok, uint
     const int n_tm = (rs.tiled + kOM - 1) / kOM;
     const int n_tn = kHidden / kON;
     const int rows_major = rows_major_split(rs.tiled, kK * 4, (size_t)kHidden * kK * 2);
-    proj_ksplit_kernel<kK><<<dim3(grid_tiles(rs.tiled, n_tn, rows_major, kOM)), dim3(kOThreads), 0, stream>>>(
-        attn, kK, rs.tiled, w_o, n_tm, n_tn, rows_major, om);
-  }
-  if (rs.tail > 0)
+    const int tail_blocks = (kHidden / 32) * ((rs.tail + 31) / 32);
+    proj_ksplit_kernel<kK>
+        <<<dim3(tail_blocks + grid_tiles(rs.tiled, n_tn, rows_major, kOM)), dim3(kOThreads), 0, stream>>>(
+            attn, kK, rs.tiled, w_o, n_tm, n_tn, rows_major, om, tail_blocks, rs.tail);
+  } else {
     proj_skinny_kernel<true><<<dim3(kHidden / 32, (rs.tail + 31) / 32), dim3(64 * kSkinnyWaves), 0, stream>>>(
-        attn + (size_t)rs.tiled * kK, kK, rs.tail, w_o, kK, shift_rows(om, rs.tiled));
+        attn, kK, rs.tail, w_o, kK, om);
+  }
   return hipGetLastError();
 }
 
