@@ -58,6 +58,9 @@ inline size_t prefill_workspace_bytes(int chunk_len) {
 
 // cu_budget: 0 = the whole device; else (with a workspace) the call's work is spread over
 // cu_budget / 8 workgroups per KV head, leaving the other CUs free.
+// Compute units of the calling thread's current device (queried once per device).
+int device_cus();
+
 hipError_t launch_prefill(const KvPools& kv, const uint16_t* q, int chunk_len, int prefix_len,
                           const int32_t* block_table, float scale, void* workspace, int cu_budget,
                           float* out, float* lse, hipStream_t stream);

@@ -233,20 +233,22 @@ __device__ __forceinline__ void skinny_block(const void* __restrict__ a_ptr, int
   }
 }
 
-// The first tail_blocks workgroups of a tiled launch compute the rows past its tiles (at most 64,
-// see split_rows) with the few-token algorithm, in LDS borrowed from the tiled kernel's stage
-// arrays: wave w stages in a0 / a1 / a2 (two waves each) or w0 / w1, and the slice sums of the
-// first and second 1024-input groups go to a0 and a1.  They come first in the grid, so they run
-// beside the first round of tiles rather than after the last.
+// Workgroups tail_base .. tail_base + tail_blocks - 1 of a tiled launch compute the rows past its
+// tiles (at most 64, see split_rows) with the few-token algorithm, block b of them being column
+// block b % (n_cols / 32), row block b / (n_cols / 32).  They borrow LDS from the tiled kernel's
+// stage arrays: wave w stages in a0 / a1 / a2 (two waves each) or w0 / w1, and the slice sums of the
+// first and second 1024-input groups go to a0 and a1.  When the tiles take more than one round of
+// the grid the tail comes first and runs beside the first round; when they fit one round it comes
+// last, so that no tile waits for a CU the tail holds (a tile started late re-reads W into L2).
 template <bool kAF32>
 __device__ __forceinline__ void tail_block(const void* a_ptr, int lda, int rows, int tail_rows,
-                                           const uint16_t* w, int k_dim, int n_cols, const OutMap& out,
+                                           const uint16_t* w, int k_dim, int n_cols, const OutMap& out, int b,
                                            uint8_t* a0, uint8_t* a1, uint8_t* a2, uint8_t* w0, uint8_t* w1) {
   const int ncb = n_cols / 32;
   const void* a_tail = kAF32 ? (const void*)(static_cast<const float*>(a_ptr) + (size_t)rows * lda)
                              : (const void*)(static_cast<const uint16_t*>(a_ptr) + (size_t)rows * lda);
   skinny_block<kAF32>(
-      a_tail, lda, tail_rows, w, k_dim, shift_rows(out, rows), blockIdx.x % ncb, blockIdx.x / ncb,
+      a_tail, lda, tail_rows, w, k_dim, shift_rows(out, rows), b % ncb, b / ncb,
       [&](int wave) -> uint8_t* {
         switch (wave) {
           case 0: return a0;
@@ -356,7 +358,7 @@ template <int kK>
 __global__ __launch_bounds__(kWThreads, 1) void proj_wide_kernel(const uint16_t* __restrict__ a, int lda, int rows,
                                                                 const uint16_t* __restrict__ w, int n_tm,
                                                                 int n_tn, int rows_major, OutMap out,
-                                                                int tail_blocks, int tail_rows) {
+                                                                int tail_base, int tail_blocks, int tail_rows) {
   // One array per stage, so that the compiler can see which stage each load and read touches.
   __shared__ __attribute__((aligned(1024))) uint8_t s_a0[kWStageA];
   __shared__ __attribute__((aligned(1024))) uint8_t s_a1[kWStageA];
@@ -374,12 +376,14 @@ __global__ __launch_bounds__(kWThreads, 1) void proj_wide_kernel(const uint16_t*
   static_assert(kWStageA >= 2 * kSkinnyStage && kWStageW >= kSkinnyStage && kWThreads == 64 * kSkinnyWaves &&
                     kWStageA >= kSliceGroup * 16 * 64 * 4,
                 "the tail blocks fit the stage arrays");
-  if ((int)blockIdx.x < tail_blocks) {
-    tail_block<false>(a, lda, rows, tail_rows, w, kK, n_tn * kWN, out, s_a0, s_a1, s_a2, s_w0, s_w1);
+  const int bid = blockIdx.x;
+  if (bid >= tail_base && bid < tail_base + tail_blocks) {
+    tail_block<false>(a, lda, rows, tail_rows, w, kK, n_tn * kWN, out, bid - tail_base, s_a0, s_a1, s_a2, s_w0,
+                       s_w1);
     return;
   }
   int tm, tn;
-  tile_of(blockIdx.x - tail_blocks, rows, kWM, n_tm, n_tn, rows_major, tm, tn);
+  tile_of(bid < tail_base ? bid : bid - tail_blocks, rows, kWM, n_tm, n_tn, rows_major, tm, tn);
   if (tm >= n_tm || tn >= n_tn) return;  // whole workgroup, before any barrier
   const int row0 = tm * kWM;
   const int col0 = tn * kWN;
@@ -530,7 +534,7 @@ template <int kK>
 __global__ __launch_bounds__(kOThreads, 1) void proj_ksplit_kernel(const float* __restrict__ a, int lda, int rows,
                                                                   const uint16_t* __restrict__ w, int n_tm,
                                                                   int n_tn, int rows_major, OutMap out,
-                                                                  int tail_blocks, int tail_rows) {
+                                                                  int tail_base, int tail_blocks, int tail_rows) {
   __shared__ __attribute__((aligned(1024))) uint8_t s_a0[2 * kOHalf];
   __shared__ __attribute__((aligned(1024))) uint8_t s_a1[2 * kOHalf];
   __shared__ __attribute__((aligned(1024))) uint8_t s_a2[2 * kOHalf];
@@ -549,12 +553,14 @@ __global__ __launch_bounds__(kOThreads, 1) void proj_ksplit_kernel(const float* 
   static_assert(2 * kOHalf >= 2 * kSkinnyStage && 2 * kOHalfW >= kSkinnyStage && kOThreads == 64 * kSkinnyWaves &&
                     2 * kOHalf >= kSliceGroup * 16 * 64 * 4,
                 "the tail blocks fit the stage arrays");
-  if ((int)blockIdx.x < tail_blocks) {
-    tail_block<true>(a, lda, rows, tail_rows, w, kK, n_tn * kON, out, s_a0, s_a1, s_a2, s_w0, s_w1);
+  const int bid = blockIdx.x;
+  if (bid >= tail_base && bid < tail_base + tail_blocks) {
+    tail_block<true>(a, lda, rows, tail_rows, w, kK, n_tn * kON, out, bid - tail_base, s_a0, s_a1, s_a2, s_w0,
+                       s_w1);
     return;
   }
   int tm, tn;
-  tile_of(blockIdx.x - tail_blocks, rows, kOM, n_tm, n_tn, rows_major, tm, tn);
+  tile_of(bid < tail_base ? bid : bid - tail_blocks, rows, kOM, n_tm, n_tn, rows_major, tm, tn);
   if (tm >= n_tm || tn >= n_tn) return;  // whole workgroup, before any barrier
   const int row0 = tm * kOM;
   const int col0 = tn * kON;
@@ -751,9 +757,9 @@ int rows_major_split(int rows, size_t a_row_bytes, size_t w_bytes) {
 }  // namespace
 
 // A call's rows: whole tiles go to the tiled kernel; a last partial tile of at most kSkinnyRows
-// rows goes to the tiled launch's first workgroups, which run the few-token algorithm (both give a
-// token the same bits), since as a tile of its own it would take a whole extra round of the grid
-// for a few rows.
+// rows goes to workgroups of the tiled launch that run the few-token algorithm (both give a token
+// the same bits), since as a tile of its own it would take a whole extra round of the grid for a
+// few rows.
 struct RowSplit {
   int tiled, tail;
 };
@@ -784,9 +790,10 @@ hipError_t launch_qkv_proj(const uint16_t* x, const uint16_t* w_qkv, int n_tok, 
                                ? kSplit2D
                                : rows_major_split(rs.tiled, kHidden * 2, (size_t)kN * kHidden * 2);
     const int tail_blocks = (kN / 32) * ((rs.tail + 31) / 32);
-    proj_wide_kernel<kHidden>
-        <<<dim3(tail_blocks + grid_tiles(rs.tiled, n_wn, rows_major, kWM)), dim3(kWThreads), 0, stream>>>(
-            x, kHidden, rs.tiled, w_qkv, n_wm, n_wn, rows_major, om, tail_blocks, rs.tail);
+    const int tiles = grid_tiles(rs.tiled, n_wn, rows_major, kWM);
+    proj_wide_kernel<kHidden><<<dim3(tail_blocks + tiles), dim3(kWThreads), 0, stream>>>(
+        x, kHidden, rs.tiled, w_qkv, n_wm, n_wn, rows_major, om, tiles > device_cus() ? 0 : tiles, tail_blocks,
+        rs.tail);
   } else {
     proj_skinny_kernel<false><<<dim3(kN / 32, (rs.tail + 31) / 32), dim3(64 * kSkinnyWaves), 0, stream>>>(
         x, kHidden, rs.tail, w_qkv, kHidden, om);
@@ -809,9 +816,10 @@ hipError_t launch_o_proj(const float* attn, const uint16_t* w_o, int n_tok, uint
     const int n_tn = kHidden / kON;
     const int rows_major = rows_major_split(rs.tiled, kK * 4, (size_t)kHidden * kK * 2);
     const int tail_blocks = (kHidden / 32) * ((rs.tail + 31) / 32);
-    proj_ksplit_kernel<kK>
-        <<<dim3(tail_blocks + grid_tiles(rs.tiled, n_tn, rows_major, kOM)), dim3(kOThreads), 0, stream>>>(
-            attn, kK, rs.tiled, w_o, n_tm, n_tn, rows_major, om, tail_blocks, rs.tail);
+    const int tiles = grid_tiles(rs.tiled, n_tn, rows_major, kOM);
+    proj_ksplit_kernel<kK><<<dim3(tail_blocks + tiles), dim3(kOThreads), 0, stream>>>(
+        attn, kK, rs.tiled, w_o, n_tm, n_tn, rows_major, om, tiles > device_cus() ? 0 : tiles, tail_blocks,
+        rs.tail);
   } else {
     proj_skinny_kernel<true><<<dim3(kHidden / 32, (rs.tail + 31) / 32), dim3(64 * kSkinnyWaves), 0, stream>>>(
         attn, kK, rs.tail, w_o, kK, om);
