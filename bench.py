@@ -959,7 +959,8 @@ class DecodeGraph:
     """Launch-bound decode: one request with the tiny workload's context (439 tokens and growing)
     through 28 layers; a step is 28 x (append its new token, decode).  The same step is timed as
     eager library calls and as one replay of a captured HIP graph (decode at concurrency 1 is where
-    graph capture pays off)."""
+    graph capture pays off), each both as mtd_kv_append + mtd_attn_decode (3 launches per layer) and
+    as mtd_attn_decode_append (2 launches per layer, same bits)."""
     name = "decode_graph"
     SLOTS = 8      # rotating input sets; one captured graph per set
     LAYERS = 28
@@ -989,20 +990,26 @@ class DecodeGraph:
         self.ws = torch.empty(mtd.decode_workspace_bytes(1, self.max_len), dtype=torch.uint8, device=dev)
         self.o = torch.empty((self.LAYERS, 1, W.HQ, W.HEAD_DIM), dtype=torch.float32, device=dev)
         self.lse = torch.empty((self.LAYERS, 1, W.HQ), dtype=torch.float32, device=dev)
-        self.graphs = []
+        self.graphs = {False: [], True: []}
         torch.cuda.synchronize()
-        for r in range(self.SLOTS):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                self._calls(r)
-            self.graphs.append(g)
+        for fused in (False, True):
+            for r in range(self.SLOTS):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    self._calls(r, fused=fused)
+                self.graphs[fused].append(g)
         torch.cuda.synchronize()
-        self.samples = {"eager_ms": None, "graph_ms": None, "decode_call_ms": []}
+        self.samples = {"eager_ms": None, "graph_ms": None, "eager_fused_ms": None, "graph_fused_ms": None,
+                        "decode_call_ms": []}
         self.n_steps = 0
 
-    def _calls(self, r, events=None):
+    def _calls(self, r, events=None, fused=False):
         mtd = self.mtd
         for l in range(self.LAYERS):
+            if fused:
+                mtd.mtd_attn_decode_append(self.k[l], self.v[l], self.q[r, l], self.k_new[r, l], self.v_new[r, l],
+                                           self.len, self.bt, self.max_len, W.SCALE, self.ws, self.o[l], self.lse[l])
+                continue
             mtd.mtd_kv_append(self.k[l], self.v[l], self.k_new[r, l], self.v_new[r, l], self.cu, self.pos, self.bt)
             if events is not None: events[l][0].record()
             mtd.mtd_attn_decode(self.k[l], self.v[l], self.q[r, l], self.len, self.bt, self.max_len, W.SCALE,
@@ -1015,16 +1022,16 @@ class DecodeGraph:
         self.pos.fill_(self.l0)
         self.len.fill_(self.l0 + 1)
 
-    def _pass(self, n, graph, events=None):
+    def _pass(self, n, graph, events=None, fused=False):
         for s in range(n):
             if graph:
-                self.graphs[s % self.SLOTS].replay()
+                self.graphs[fused][s % self.SLOTS].replay()
             else:
                 ev = None
                 if events is not None:
                     ev = [[self.torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(self.LAYERS)]
                     events.append(ev)
-                self._calls(s % self.SLOTS, ev)
+                self._calls(s % self.SLOTS, ev, fused=fused)
 
     def run(self, steps, warmup):
         """Eager and graph passes of `steps` steps each, after `warmup` untimed steps of each mode.
@@ -1034,24 +1041,27 @@ class DecodeGraph:
         if steps > self.ROOM:
             raise SystemExit(f"--steps {steps} exceeds the {self.ROOM} tokens of room per pass")
         walls = {}
-        for graph in (False, True):
-            self._reset()
-            self._pass(min(warmup, self.ROOM), graph)
-            self._reset()
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            self._pass(steps, graph)
-            torch.cuda.synchronize()
-            walls[graph] = time.perf_counter() - t0
+        for fused in (False, True):
+            for graph in (False, True):
+                self._reset()
+                self._pass(min(warmup, self.ROOM), graph, fused=fused)
+                self._reset()
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                self._pass(steps, graph, fused=fused)
+                torch.cuda.synchronize()
+                walls[(fused, graph)] = time.perf_counter() - t0
         self._reset()
         events = []
         self._pass(steps, False, events)
         torch.cuda.synchronize()
         self.samples["decode_call_ms"] = [e[0].elapsed_time(e[1]) for ev in events for e in ev]
-        self.samples["eager_ms"] = walls[False] * 1e3 / steps
-        self.samples["graph_ms"] = walls[True] * 1e3 / steps
+        self.samples["eager_ms"] = walls[(False, False)] * 1e3 / steps
+        self.samples["graph_ms"] = walls[(False, True)] * 1e3 / steps
+        self.samples["eager_fused_ms"] = walls[(True, False)] * 1e3 / steps
+        self.samples["graph_fused_ms"] = walls[(True, True)] * 1e3 / steps
         self.n_steps = steps
-        return walls[True]
+        return walls[(False, True)]
 
     def config(self):
         return {"workload": "decode_graph: 1 request (439-token context growing by one token per step) through "
@@ -1069,7 +1079,11 @@ class DecodeGraph:
                            "bytes": step_bytes / self.LAYERS,
                            "kernels": "decode_split_kernel + decode_merge_kernel (per layer call, eager pass)"},
                 "step": {"eager_ms": e, "graph_ms": g, "graph_speedup": e / g,
-                         "graph_step_gbs": step_bytes / (g * 1e-3) / 1e9, "launches_per_step": 3 * self.LAYERS + 2}}
+                         "graph_step_gbs": step_bytes / (g * 1e-3) / 1e9, "launches_per_step": 3 * self.LAYERS + 2},
+                "step_fused": {"eager_ms": self.samples["eager_fused_ms"], "graph_ms": self.samples["graph_fused_ms"],
+                               "graph_speedup_vs_unfused_graph": g / self.samples["graph_fused_ms"],
+                               "launches_per_step": 2 * self.LAYERS + 2,
+                               "calls": "mtd_attn_decode_append (store + decode split, merge) per layer"}}
 
     def dominant(self, res):
         return {"kernel": "decode_split_kernel+decode_merge_kernel", "bound": "hbm", "achieved": res["decode"]["value"],
@@ -1203,17 +1217,21 @@ class DecodeGraphBlock(DecodeGraph):
         self.xb = torch.empty((1, W.HIDDEN), dtype=torch.bfloat16, device=dev)
         super().__init__(dev)
 
-    def _calls(self, r, events=None):
+    def _calls(self, r, events=None, fused=False):
         mtd = self.mtd
         x = self.x0[r]
         for l in range(self.LAYERS):
             w_qkv, w_o = self.w[l]
             mtd.mtd_qkv_proj(x, w_qkv, self.qb, self.kb, self.vb)
-            mtd.mtd_kv_append(self.k[l], self.v[l], self.kb, self.vb, self.cu, self.pos, self.bt)
-            if events is not None: events[l][0].record()
-            mtd.mtd_attn_decode(self.k[l], self.v[l], self.qb, self.len, self.bt, self.max_len, W.SCALE,
-                                self.ws, self.o[l], self.lse[l])
-            if events is not None: events[l][1].record()
+            if fused:
+                mtd.mtd_attn_decode_append(self.k[l], self.v[l], self.qb, self.kb, self.vb, self.len, self.bt,
+                                           self.max_len, W.SCALE, self.ws, self.o[l], self.lse[l])
+            else:
+                mtd.mtd_kv_append(self.k[l], self.v[l], self.kb, self.vb, self.cu, self.pos, self.bt)
+                if events is not None: events[l][0].record()
+                mtd.mtd_attn_decode(self.k[l], self.v[l], self.qb, self.len, self.bt, self.max_len, W.SCALE,
+                                    self.ws, self.o[l], self.lse[l])
+                if events is not None: events[l][1].record()
             mtd.mtd_o_proj(self.o[l], w_o, self.xb)
             x = self.xb
         self.pos.add_(1)
@@ -1223,13 +1241,15 @@ class DecodeGraphBlock(DecodeGraph):
         c = super().config()
         c["workload"] = ("decode_graph_block: 1 request (439-token context growing by one token per step) through "
                          "28 attention blocks; step = 28 x (QKV projection, append, decode, output projection; "
-                         "random bf16 weights); eager calls vs one HIP-graph replay")
+                         "random bf16 weights); eager calls vs one HIP-graph replay, with append and decode as "
+                         "two calls and as mtd_attn_decode_append")
         c["hidden"] = W.HIDDEN
         return c
 
     def results(self):
         res = super().results()
         res["step"]["launches_per_step"] = 5 * self.LAYERS + 2
+        res["step_fused"]["launches_per_step"] = 4 * self.LAYERS + 2
         return res
 
 
@@ -1456,7 +1476,7 @@ def main():
             "per_launch": dom["per_launch"], "source_digest": source_digest(dom["kernel"]),
         },
     }
-    for k in ("decode", "prefill", "append", "step"):
+    for k in ("decode", "prefill", "append", "step", "step_fused"):
         if k in res:
             line[k] = {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in res[k].items()}
     if "buckets" in res:

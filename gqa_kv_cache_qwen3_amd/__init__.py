@@ -18,6 +18,8 @@ Names match the C entry points:
     mtd_o_proj(attn, w_o, out=None)
     mtd_attn_merge(o_parts, lse_parts, out=None, lse=None)
     mtd_attn_decode_noalloc(k_pages, v_pages, q, kv_lens, block_tables, max_kv_len, scale, out, lse)
+    mtd_attn_decode_append(k_pages, v_pages, q, k_new, v_new, kv_lens, block_tables, max_kv_len, scale,
+                           workspace=None, out=None, lse=None)
     mtd_measure_page_read(k_pages, v_pages, page_ids, pages_per_wave=8, sink=None)   (measurement aid)
 """
 
@@ -93,6 +95,9 @@ def lib() -> ctypes.CDLL:
         cdll.mtd_attn_decode.argtypes = [kvp, _P, _P, _P, _I, _I, _I, _I, ctypes.c_float, _P,
                                          ctypes.c_size_t, _P, _P, _P]
         cdll.mtd_attn_decode.restype = ctypes.c_int
+        cdll.mtd_attn_decode_append.argtypes = [kvp, _P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_float, _P,
+                                                ctypes.c_size_t, _P, _P, _P]
+        cdll.mtd_attn_decode_append.restype = ctypes.c_int
         cdll.mtd_qkv_proj.argtypes = [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P]
         cdll.mtd_qkv_proj.restype = ctypes.c_int
         cdll.mtd_o_proj.argtypes = [_P, _P, _I, _I, _I, _I, _P, _P]
@@ -267,6 +272,40 @@ def mtd_attn_decode(k_pages, v_pages, q, kv_lens, block_tables, max_kv_len: int,
                                  block_tables.data_ptr(), block_tables.shape[1], b,
                                  int(max_kv_len), hq, float(scale), workspace.data_ptr(),
                                  workspace.numel(), out.data_ptr(), lse.data_ptr(), _stream()))
+    return out, lse
+
+
+def mtd_attn_decode_append(k_pages, v_pages, q, k_new, v_new, kv_lens, block_tables, max_kv_len: int,
+                           scale: float, workspace=None, out=None, lse=None):
+    """One decode step: store each request's new K/V row ([B][Hkv][D] bf16) at position kv_lens[b] - 1,
+    then attend as mtd_attn_decode.  Returns (out float32 [B][Hq][D], lse float32 [B][Hq])."""
+    layer = kv_layer(k_pages, v_pages)
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k_new, "k_new", torch.bfloat16, 3)
+    _need(v_new, "v_new", torch.bfloat16, 3)
+    _need(kv_lens, "kv_lens", torch.int32, 1)
+    _need(block_tables, "block_tables", torch.int32, 2)
+    b, hq, d = q.shape
+    if kv_lens.shape[0] != b or block_tables.shape[0] != b:
+        raise ValueError("kv_lens and block_tables must have one entry/row per request")
+    if k_new.shape != v_new.shape or tuple(k_new.shape) != (b, layer.num_kv_heads, layer.head_dim):
+        raise ValueError(f"k_new/v_new must be [{b}][{layer.num_kv_heads}][{layer.head_dim}]")
+    need = decode_workspace_bytes(b, int(max_kv_len), hq, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _need(workspace, "workspace", torch.uint8, 1)
+    if out is None:
+        out = torch.empty((b, hq, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((b, hq), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, 3)
+    _need(lse, "lse", torch.float32, 2)
+    if tuple(out.shape) != (b, hq, d) or tuple(lse.shape) != (b, hq):
+        raise ValueError("out must be [B][Hq][D] and lse [B][Hq]")
+    _check(lib().mtd_attn_decode_append(ctypes.byref(layer), q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+                                        kv_lens.data_ptr(), block_tables.data_ptr(), block_tables.shape[1], b,
+                                        int(max_kv_len), hq, float(scale), workspace.data_ptr(),
+                                        workspace.numel(), out.data_ptr(), lse.data_ptr(), _stream()))
     return out, lse
 
 

@@ -16,6 +16,11 @@
 //   writes the split's normalised partial output and its log-sum-exp.
 // decode_merge: one workgroup per (request, query head) combines that request's partials with
 //   weights exp(lse_s - LSE), reducing over wavefronts and LDS.
+// With kAppend, decode_split also stores this step's token: the request's new K/V row goes to its
+//   slot at position kv_lens[b] - 1.  Only the last split of a request covers that position, so the
+//   wave of that split for KV head g writes head g's row (8 lanes, 32 bytes each) before it reads
+//   its pages, and the lanes that read those bytes are the lanes that wrote them; no other wave
+//   reads the slot, so nothing has to wait for the store.
 //
 // Lane layout inside decode_split for one 64-token page: lane = 8*sg + o.  The lane handles the
 // 8 slots {8a + sg : a = 0..7} and, of each slot row (128 dims = 256 bytes), the two 16-byte
@@ -66,11 +71,12 @@ __device__ __forceinline__ bool locate_split(const int32_t* __restrict__ kv_lens
   return false;
 }
 
+template <bool kAppend>
 __global__ __launch_bounds__(64) void decode_split_kernel(
-    const uint16_t* __restrict__ k_pages, const uint16_t* __restrict__ v_pages, int num_pages,
-    const uint16_t* __restrict__ q, const int32_t* __restrict__ kv_lens,
-    const int32_t* __restrict__ block_tables, int bt_stride, int batch, int max_kv_len,
-    float scale_log2, float* __restrict__ part_o, float* __restrict__ part_lse) {
+    uint16_t* __restrict__ k_pages, uint16_t* __restrict__ v_pages, int num_pages,
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+    const int32_t* __restrict__ kv_lens, const int32_t* __restrict__ block_tables, int bt_stride,
+    int batch, int max_kv_len, float scale_log2, float* __restrict__ part_o, float* __restrict__ part_lse) {
   const int lane = threadIdx.x;
   const int f = blockIdx.x / kKvHeads;
   const int g = blockIdx.x % kKvHeads;
@@ -102,6 +108,29 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
   const int tok0 = s * split_tokens(len);
   const int tok1 = min(tok0 + split_tokens(len), len);
   const int32_t* bt_row = block_tables + (size_t)b * bt_stride;
+  // kAppend: the new token sits at position len - 1 when the request's length is in [1, max_kv_len]
+  // (len is clamped to that range; a length outside it appends nothing).  Before reading any page,
+  // the wave of the last split stores head g's new row: the lanes of slot group (len - 1) % 8, 32
+  // bytes of K and 32 of V each.  The page loop below then loads exactly those bytes in the same
+  // lanes, so each lane reads back what it wrote itself (program order within a thread).
+  if (kAppend && tok1 == len && len >= 1 && kv_lens[b] == len) {
+    const int page = bt_row[(len - 1) / kPage];
+    if (page >= 0 && page < num_pages) {  // an out-of-pool page is neither stored nor read
+      const uint16_t* kn = k_new + ((size_t)b * kKvHeads + g) * kHeadDim;
+      const uint16_t* vn = v_new + ((size_t)b * kKvHeads + g) * kHeadDim;
+      const int ns = (len - 1) % kPage;
+      if ((ns & 7) == sg) {
+        const size_t row = (((size_t)page * kKvHeads + g) * kPage + ns) * kHeadDim;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          *reinterpret_cast<uint4*>(k_pages + row + (8 * c + o) * 8) =
+              *reinterpret_cast<const uint4*>(kn + (8 * c + o) * 8);
+          *reinterpret_cast<uint4*>(v_pages + row + (8 * c + o) * 8) =
+              *reinterpret_cast<const uint4*>(vn + (8 * c + o) * 8);
+        }
+      }
+    }
+  }
 
   for (int e0 = tok0 / kPage; e0 * kPage < tok1; ++e0) {
     const int page = bt_row[e0];
@@ -369,16 +398,22 @@ hipError_t decode_scratch(void** ptr) {
   return hipSuccess;
 }
 
-hipError_t launch_decode(const KvPools& kv, const uint16_t* q, const int32_t* kv_lens,
-                         const int32_t* block_tables, int bt_stride, int batch, int max_kv_len,
-                         float scale, void* workspace, float* out, float* lse, hipStream_t stream) {
+hipError_t launch_decode(const KvPools& kv, const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                         const int32_t* kv_lens, const int32_t* block_tables, int bt_stride, int batch,
+                         int max_kv_len, float scale, void* workspace, float* out, float* lse,
+                         hipStream_t stream) {
   const size_t parts = (size_t)batch * (size_t)split_parts_bound(max_kv_len);
   float* part_o = static_cast<float*>(workspace);
   float* part_lse = part_o + parts * kQHeads * kHeadDim;
   const unsigned n_waves = (unsigned)(parts * kKvHeads);
-  decode_split_kernel<<<dim3(n_waves), dim3(64), 0, stream>>>(
-      kv.k, kv.v, kv.num_pages, q, kv_lens, block_tables, bt_stride, batch, max_kv_len,
-      scale * kLog2e, part_o, part_lse);
+  if (k_new != nullptr)
+    decode_split_kernel<true><<<dim3(n_waves), dim3(64), 0, stream>>>(
+        kv.k, kv.v, kv.num_pages, q, k_new, v_new, kv_lens, block_tables, bt_stride, batch, max_kv_len,
+        scale * kLog2e, part_o, part_lse);
+  else
+    decode_split_kernel<false><<<dim3(n_waves), dim3(64), 0, stream>>>(
+        kv.k, kv.v, kv.num_pages, q, nullptr, nullptr, kv_lens, block_tables, bt_stride, batch,
+        max_kv_len, scale * kLog2e, part_o, part_lse);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   decode_merge_kernel<<<dim3(batch * kQHeads), dim3(256), 0, stream>>>(

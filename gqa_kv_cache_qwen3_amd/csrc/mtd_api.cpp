@@ -90,6 +90,39 @@ mtd::KvPools pools(const mtd_kv_layer_t* kv) {
                       kv->num_pages};
 }
 
+// mtd_attn_decode (k_new = v_new = NULL) and mtd_attn_decode_append (both set).
+int decode_call(const mtd_kv_layer_t* kv, const void* q, const void* k_new, const void* v_new,
+                const int32_t* kv_lens, const int32_t* block_tables, int32_t bt_stride, int32_t batch,
+                int32_t max_kv_len, int32_t num_q_heads, float scale, void* workspace, size_t workspace_bytes,
+                float* out, float* lse, void* stream) {
+  int st = check_layer(kv);
+  if (st != MTD_OK) return st;
+  if ((st = check_heads(num_q_heads, kv->num_kv_heads)) != MTD_OK) return st;
+  if ((st = check_scale(scale)) != MTD_OK) return st;
+  if (q == nullptr || kv_lens == nullptr || block_tables == nullptr || out == nullptr || lse == nullptr)
+    return fail(MTD_ERR_INVALID_ARG, "q / kv_lens / block_tables / out / lse is NULL");
+  if (!aligned16(q) || !aligned16(out) || !aligned16(workspace))
+    return fail(MTD_ERR_INVALID_ARG, "q / out / workspace not 16-byte aligned");
+  if (!aligned16(k_new) || !aligned16(v_new))
+    return fail(MTD_ERR_INVALID_ARG, "k_new / v_new not 16-byte aligned");
+  if (batch <= 0) return fail(MTD_ERR_INVALID_ARG, "batch = %d", batch);
+  if (max_kv_len <= 0) return fail(MTD_ERR_INVALID_ARG, "max_kv_len = %d", max_kv_len);
+  if (max_kv_len > MTD_MAX_CONTEXT)
+    return fail(MTD_ERR_CAPACITY, "max_kv_len %d exceeds %d", max_kv_len, MTD_MAX_CONTEXT);
+  const int64_t pages = ((int64_t)max_kv_len + mtd::kPage - 1) / mtd::kPage;
+  if (bt_stride < pages)
+    return fail(MTD_ERR_CAPACITY, "bt_stride %d < %lld pages for max_kv_len %d", bt_stride,
+                (long long)pages, max_kv_len);
+  const size_t need = mtd::decode_workspace_bytes(batch, max_kv_len);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(MTD_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  return hip_status(mtd::launch_decode(pools(kv), static_cast<const uint16_t*>(q),
+                                       static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
+                                       kv_lens, block_tables, bt_stride, batch, max_kv_len, scale,
+                                       workspace, out, lse, static_cast<hipStream_t>(stream)),
+                    "decode launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -176,29 +209,17 @@ int mtd_attn_decode(const mtd_kv_layer_t* kv, const void* q, const int32_t* kv_l
                     const int32_t* block_tables, int32_t bt_stride, int32_t batch,
                     int32_t max_kv_len, int32_t num_q_heads, float scale, void* workspace,
                     size_t workspace_bytes, float* out, float* lse, void* stream) {
-  int st = check_layer(kv);
-  if (st != MTD_OK) return st;
-  if ((st = check_heads(num_q_heads, kv->num_kv_heads)) != MTD_OK) return st;
-  if ((st = check_scale(scale)) != MTD_OK) return st;
-  if (q == nullptr || kv_lens == nullptr || block_tables == nullptr || out == nullptr || lse == nullptr)
-    return fail(MTD_ERR_INVALID_ARG, "q / kv_lens / block_tables / out / lse is NULL");
-  if (!aligned16(q) || !aligned16(out) || !aligned16(workspace))
-    return fail(MTD_ERR_INVALID_ARG, "q / out / workspace not 16-byte aligned");
-  if (batch <= 0) return fail(MTD_ERR_INVALID_ARG, "batch = %d", batch);
-  if (max_kv_len <= 0) return fail(MTD_ERR_INVALID_ARG, "max_kv_len = %d", max_kv_len);
-  if (max_kv_len > MTD_MAX_CONTEXT)
-    return fail(MTD_ERR_CAPACITY, "max_kv_len %d exceeds %d", max_kv_len, MTD_MAX_CONTEXT);
-  const int64_t pages = ((int64_t)max_kv_len + mtd::kPage - 1) / mtd::kPage;
-  if (bt_stride < pages)
-    return fail(MTD_ERR_CAPACITY, "bt_stride %d < %lld pages for max_kv_len %d", bt_stride,
-                (long long)pages, max_kv_len);
-  const size_t need = mtd::decode_workspace_bytes(batch, max_kv_len);
-  if (workspace == nullptr || workspace_bytes < need)
-    return fail(MTD_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
-  return hip_status(mtd::launch_decode(pools(kv), static_cast<const uint16_t*>(q), kv_lens,
-                                       block_tables, bt_stride, batch, max_kv_len, scale,
-                                       workspace, out, lse, static_cast<hipStream_t>(stream)),
-                    "decode launch");
+  return decode_call(kv, q, nullptr, nullptr, kv_lens, block_tables, bt_stride, batch, max_kv_len, num_q_heads,
+                     scale, workspace, workspace_bytes, out, lse, stream);
+}
+
+int mtd_attn_decode_append(const mtd_kv_layer_t* kv, const void* q, const void* k_new, const void* v_new,
+                           const int32_t* kv_lens, const int32_t* block_tables, int32_t bt_stride,
+                           int32_t batch, int32_t max_kv_len, int32_t num_q_heads, float scale,
+                           void* workspace, size_t workspace_bytes, float* out, float* lse, void* stream) {
+  if (k_new == nullptr || v_new == nullptr) return fail(MTD_ERR_INVALID_ARG, "k_new / v_new is NULL");
+  return decode_call(kv, q, k_new, v_new, kv_lens, block_tables, bt_stride, batch, max_kv_len, num_q_heads,
+                     scale, workspace, workspace_bytes, out, lse, stream);
 }
 
 int mtd_attn_decode_noalloc(const mtd_kv_layer_t* kv, const void* q, const int32_t* kv_lens,
@@ -228,7 +249,7 @@ int mtd_attn_decode_noalloc(const mtd_kv_layer_t* kv, const void* q, const int32
                 batch, max_kv_len, need, mtd::kDecodeScratchBytes);
   void* scratch = nullptr;
   if ((st = hip_status(mtd::decode_scratch(&scratch), "decode scratch lookup")) != MTD_OK) return st;
-  return hip_status(mtd::launch_decode(pools(kv), static_cast<const uint16_t*>(q), kv_lens,
+  return hip_status(mtd::launch_decode(pools(kv), static_cast<const uint16_t*>(q), nullptr, nullptr, kv_lens,
                                        block_tables, bt_stride, batch, max_kv_len, scale, scratch,
                                        out, lse, static_cast<hipStream_t>(stream)),
                     "decode launch");

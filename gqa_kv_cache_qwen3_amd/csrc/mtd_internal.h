@@ -80,9 +80,12 @@ constexpr size_t kDecodeScratchBytes = size_t(64) << 20;
 constexpr int kMaxDevices = 64;
 hipError_t decode_scratch(void** ptr);
 
-hipError_t launch_decode(const KvPools& kv, const uint16_t* q, const int32_t* kv_lens,
-                         const int32_t* block_tables, int bt_stride, int batch, int max_kv_len,
-                         float scale, void* workspace, float* out, float* lse, hipStream_t stream);
+// k_new / v_new: NULL, or bf16 [batch][kKvHeads][kHeadDim] rows that the split kernel stores at
+// position kv_lens[b] - 1 of each request (and attends to) in the same launch.
+hipError_t launch_decode(const KvPools& kv, const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                         const int32_t* kv_lens, const int32_t* block_tables, int bt_stride, int batch,
+                         int max_kv_len, float scale, void* workspace, float* out, float* lse,
+                         hipStream_t stream);
 
 // The projections around the attention (n_tok >= 1; pointers 16-byte aligned):
 //   x bf16 [n_tok][kHidden], w_qkv bf16 [(kQHeads + 2 kKvHeads) kHeadDim][kHidden]

@@ -70,7 +70,7 @@
 extern "C" {
 #endif
 
-#define MTD_ABI_VERSION 7
+#define MTD_ABI_VERSION 8
 
 /* Status codes. */
 #define MTD_OK               0
@@ -224,6 +224,33 @@ int mtd_attn_decode(const mtd_kv_layer_t* kv, const void* q, const int32_t* kv_l
                     const int32_t* block_tables, int32_t bt_stride, int32_t batch,
                     int32_t max_kv_len, int32_t num_q_heads, float scale, void* workspace,
                     size_t workspace_bytes, float* out, float* lse, void* stream);
+
+/*
+ * mtd_attn_decode_append - one decode step in one call: store each request's new K/V row, then
+ * attend exactly as mtd_attn_decode does.
+ *
+ * Every autoregressive step adds the token it feeds to the KV cache and attends over the whole
+ * cache including it ("Optimizing ASR Models ...", section ASR Model Primer, "Autoregressive
+ * Decode").  At low concurrency that step is replayed from a captured graph (section Optimization
+ * Strategies, AR Decode, "CUDA Graph"), and a replay pays for each launch it holds, so here the
+ * store rides in the decode's split kernel: two launches per step instead of three.
+ *
+ *   k_new, v_new    bf16 [batch][num_kv_heads][head_dim] on the device, 16-byte aligned: the K and V
+ *                   rows of each request's new token
+ *   all other arguments as for mtd_attn_decode (kv_lens counts the new token)
+ *
+ * For kv_lens[b] in [1, max_kv_len], the pools and out / lse after the call are bit for bit those
+ * of mtd_kv_append with one new row per request (cu_new = 0, 1, .., batch; start_pos[b] =
+ * kv_lens[b] - 1; the same block tables) followed on the same stream by mtd_attn_decode with
+ * these arguments.  A request whose kv_lens[b] lies outside that range stores nothing; a new token
+ * whose page id is outside the pool is neither stored nor attended to, as with the two calls.
+ * Errors: those of mtd_attn_decode, and MTD_ERR_INVALID_ARG when k_new or v_new is NULL or not
+ * 16-byte aligned.
+ */
+int mtd_attn_decode_append(const mtd_kv_layer_t* kv, const void* q, const void* k_new, const void* v_new,
+                           const int32_t* kv_lens, const int32_t* block_tables, int32_t bt_stride,
+                           int32_t batch, int32_t max_kv_len, int32_t num_q_heads, float scale,
+                           void* workspace, size_t workspace_bytes, float* out, float* lse, void* stream);
 
 /* Bytes of the static device scratch mtd_attn_decode_noalloc uses on each GPU (64 MiB). */
 #define MTD_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)

@@ -22,8 +22,10 @@ hipError_t launch_kv_append(const KvPools&, const uint16_t*, const uint16_t*, co
                             const int32_t*, int, int, int, hipStream_t) { reached("kv_append"); }
 hipError_t launch_prefill(const KvPools&, const uint16_t*, int, int, const int32_t*, float, void*, int, float*,
                           float*, hipStream_t) { reached("prefill"); }
-hipError_t launch_decode(const KvPools&, const uint16_t*, const int32_t*, const int32_t*, int, int, int, float,
-                         void*, float*, float*, hipStream_t) { reached("decode"); }
+hipError_t launch_decode(const KvPools&, const uint16_t*, const uint16_t*, const uint16_t*, const int32_t*,
+                         const int32_t*, int, int, int, float, void*, float*, float*, hipStream_t) {
+  reached("decode");
+}
 hipError_t launch_qkv_proj(const uint16_t*, const uint16_t*, int, uint16_t*, uint16_t*, uint16_t*, hipStream_t) {
   reached("qkv_proj");
 }
@@ -119,6 +121,15 @@ int main() {
          "decode: bt_stride");
   expect(mtd_attn_decode(&kv, P, I, I, 16, 2, 1000, 16, 0.088f, P, 1 << 30, F, nullptr, nullptr),
          MTD_ERR_INVALID_ARG, "decode: lse NULL");
+  expect(mtd_attn_decode_append(&kv, P, nullptr, P, I, I, 16, 2, 1000, 16, 0.088f, P, 1 << 30, F, F, nullptr),
+         MTD_ERR_INVALID_ARG, "decode_append: k_new NULL");
+  expect(mtd_attn_decode_append(&kv, P, P, (const char*)P + 8, I, I, 16, 2, 1000, 16, 0.088f, P, 1 << 30, F, F,
+                                nullptr),
+         MTD_ERR_INVALID_ARG, "decode_append: v_new misaligned");
+  expect(mtd_attn_decode_append(&kv, P, P, P, I, I, 16, 2, 1000, 16, 0.088f, nullptr, 0, F, F, nullptr),
+         MTD_ERR_WORKSPACE, "decode_append: no workspace");
+  expect(mtd_attn_decode_append(&kv, P, P, P, I, I, 15, 2, 1000, 16, 0.088f, P, 1 << 30, F, F, nullptr),
+         MTD_ERR_CAPACITY, "decode_append: bt_stride");
   expect(mtd_attn_decode_noalloc(&kv, P, I, I, 2048, INT_MAX, MTD_MAX_CONTEXT, 16, 0.088f, F, F, nullptr),
          MTD_ERR_WORKSPACE, "decode_noalloc: beyond the scratch");
   expect(mtd_attn_decode_noalloc(&kv, P, I, I, 2048, 2, 0, 16, 0.088f, F, F, nullptr), MTD_ERR_INVALID_ARG,

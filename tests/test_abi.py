@@ -201,6 +201,37 @@ def test_decode_validation(lib, kw, code):
     assert decode(lib, layer(), **kw) == code
 
 
+def decode_append(lib, kv, **kw):
+    a = dict(q=FAKE, k_new=FAKE, v_new=FAKE, lens=FAKE, bt=FAKE, stride=16, batch=2, max_len=1000, hq=16,
+             scale=0.088, ws=FAKE, ws_bytes=None, out=FAKE, lse=FAKE)
+    a.update(kw)
+    if a["ws_bytes"] is None:
+        a["ws_bytes"] = lib.mtd_attn_decode_workspace_bytes(max(a["batch"], 1), 16, max(min(a["max_len"], 131072), 1), 128)
+    return lib.mtd_attn_decode_append(ctypes.byref(kv) if kv is not None else None, a["q"], a["k_new"], a["v_new"],
+                                      a["lens"], a["bt"], a["stride"], a["batch"], a["max_len"], a["hq"], a["scale"],
+                                      a["ws"], a["ws_bytes"], a["out"], a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k_new=None), mtd.MTD_ERR_INVALID_ARG),
+    (dict(v_new=None), mtd.MTD_ERR_INVALID_ARG),
+    (dict(k_new=FAKE + 8), mtd.MTD_ERR_INVALID_ARG),                 # not 16-byte aligned
+    (dict(v_new=FAKE + 4), mtd.MTD_ERR_INVALID_ARG),
+    (dict(hq=8), mtd.MTD_ERR_UNSUPPORTED),
+    (dict(q=None), mtd.MTD_ERR_INVALID_ARG),
+    (dict(batch=0), mtd.MTD_ERR_INVALID_ARG),
+    (dict(max_len=1025, stride=16), mtd.MTD_ERR_CAPACITY),
+    (dict(ws=None), mtd.MTD_ERR_WORKSPACE),
+])
+def test_decode_append_validation(lib, kw, code):
+    assert decode_append(lib, layer(), **kw) == code
+
+
+def test_decode_append_checks_the_layer(lib):
+    assert decode_append(lib, None) == mtd.MTD_ERR_INVALID_ARG
+    assert decode_append(lib, layer(num_pages=0)) == mtd.MTD_ERR_INVALID_ARG
+
+
 def test_prefill_workspace_size_formula(lib):
     # one part of every split item, partial O and LSE: chunk_len rows of 16 heads x (128 + 1) floats
     for c in (1, 2, 127, 128, 129, 4096, 131072):
