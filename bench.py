@@ -1141,8 +1141,11 @@ class DecodeGraphBuckets:
         o = torch.empty((self.LAYERS, bucket, W.HQ, W.HEAD_DIM), dtype=torch.float32, device=dev)
         lse = torch.empty((self.LAYERS, bucket, W.HQ), dtype=torch.float32, device=dev)
 
-        def calls():
+        def calls(fused=False):
             for l in range(self.LAYERS):
+                if fused:  # padding requests (length 0) store nothing, as with the two calls
+                    mtd.mtd_attn_decode_append(k, v, q[l], kn[l], vn[l], lens, bt, bound, W.SCALE, ws, o[l], lse[l])
+                    continue
                 mtd.mtd_kv_append(k, v, kn[l], vn[l], cu, pos, bt)
                 mtd.mtd_attn_decode(k, v, q[l], lens, bt, bound, W.SCALE, ws, o[l], lse[l])
             pos.add_(step_add)
@@ -1154,27 +1157,31 @@ class DecodeGraphBuckets:
                                        device=dev))
 
         torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            calls()
+        graphs = {}
+        for fused in (False, True):
+            graphs[fused] = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graphs[fused]):
+                calls(fused)
         out = {}
-        for use_graph in (False, True):
+        for name, use_graph, fused in (("eager_ms", False, False), ("graph_ms", True, False),
+                                       ("graph_fused_ms", True, True)):
             reset()
             for _ in range(warmup):
-                graph.replay() if use_graph else calls()
+                graphs[fused].replay() if use_graph else calls(fused)
             reset()
             torch.cuda.synchronize()
             t0 = time.perf_counter()
             for _ in range(steps):
-                graph.replay() if use_graph else calls()
+                graphs[fused].replay() if use_graph else calls(fused)
             torch.cuda.synchronize()
-            out["graph_ms" if use_graph else "eager_ms"] = (time.perf_counter() - t0) * 1e3 / steps
+            out[name] = (time.perf_counter() - t0) * 1e3 / steps
         step_bytes = self.LAYERS * decode_bytes(lens0 + 1 + steps // 2)
-        del graph, k, v
+        del graphs, k, v
         torch.cuda.empty_cache()
         return {"case": label, "bucket": bucket, "requests": b, "kv_tokens": int(lens0.sum()),
                 "eager_ms": out["eager_ms"], "graph_ms": out["graph_ms"], "speedup": out["eager_ms"] / out["graph_ms"],
-                "graph_gbs": step_bytes / (out["graph_ms"] * 1e-3) / 1e9}
+                "graph_gbs": step_bytes / (out["graph_ms"] * 1e-3) / 1e9, "graph_fused_ms": out["graph_fused_ms"],
+                "fused_speedup": out["graph_ms"] / out["graph_fused_ms"]}
 
     def run(self, steps, warmup):
         t0 = time.perf_counter()
@@ -1186,7 +1193,8 @@ class DecodeGraphBuckets:
 
     def config(self):
         return {"workload": "decode_graph_buckets: decode batches padded to buckets 1..64, one HIP graph per bucket, "
-                            "28 x (append, decode) per step; eager calls vs graph replays",
+                            "28 x (append, decode) per step; eager calls vs graph replays, and graph replays of "
+                            "28 x mtd_attn_decode_append",
                 "layers": self.LAYERS, "cases": [c[0] for c in self.cases]}
 
     def results(self):
