@@ -18,7 +18,7 @@
 // (256 x 128 tiles) and proj_ksplit_kernel for the output map (128 x 128 tiles with K split
 // between two sets of waves); see their comments.  Calls of at most 64 tokens run
 // proj_skinny_kernel, which spreads K over the waves, and a tiled launch computes a last partial
-// tile of at most 64 rows with the same algorithm in its first workgroups (tail_block).  All three add the products in one order (fixed K slices and groups of them,
+// tile of at most 64 rows the same way in its first workgroups (tail_block).  All three add the products in one order (fixed K slices and groups of them,
 // see kKSlice), so a token's result is the same whatever the token count and whichever kernel
 // runs.  The MFMA is v_mfma_f32_32x32x16_bf16 with fp32 accumulators throughout.
 //
@@ -111,9 +111,9 @@ __device__ __forceinline__ void tile_of(int id, int rows, int tm_rows, int n_tm,
   }
 }
 
-// Few tokens (at most 64): the weights dominate the bytes, so the grid is spread over K instead
-// of tokens.  Workgroup (column block x, row block y) = 32 columns of W against 32 tokens, 8
-// waves; wave w takes the K slices w * q .. w * q + q - 1 (q = k_dim / kKSlice / 8: 1 for QKV,
+// The last partial tile of a tiled launch (at most 64 rows, few beside the tiles' rows): as with
+// few tokens, the grid is spread over K.  Workgroup (column block x, row block y) = 32 columns of
+// W against 32 tokens, 8 waves, in LDS the tiled kernel already holds; wave w takes the K slices w * q .. w * q + q - 1 (q = k_dim / kKSlice / 8: 1 for QKV,
 // 2 for o_proj).  For each slice the wave stages its 32 x 128 pieces of A and W in its own 16 KiB
 // of LDS with coalesced loads (each direct-to-LDS instruction fetches 8 rows x 128 contiguous
 // bytes; the float32 A comes through registers, 512 contiguous bytes per row, and is rounded to
@@ -728,16 +728,114 @@ __global__ __launch_bounds__(kOThreads, 1) void proj_ksplit_kernel(const float* 
     }
 }
 
-template <bool kAF32>
-__global__ __launch_bounds__(64 * kSkinnyWaves) void proj_skinny_kernel(
-    const void* __restrict__ a_ptr, int lda, int rows, const uint16_t* __restrict__ w, int k_dim,
-    OutMap out) {
-  __shared__ __attribute__((aligned(1024))) uint8_t s_mem[kSkinnyWaves * kSkinnyStage];
-  skinny_block<kAF32>(
-      a_ptr, lda, rows, w, k_dim, out, blockIdx.x, blockIdx.y,
-      [&](int wave) { return s_mem + wave * kSkinnyStage; },
-      [&](int slice) { return reinterpret_cast<float*>(s_mem) + slice * 16 * 64; });
+// Calls of at most 64 tokens.  Workgroup (column block x, row block y) = 32 columns of W against
+// kRB tokens (32 for QKV, 8 for the output map), with one wave per K slice (8 for QKV, 16 for the
+// output map), so that all of the block's weights are in flight at once: a call of one token has
+// only 128 (QKV) or 32 (output map) workgroups, and its time is each CU's fetch of its share of W.
+// Wave w copies its 32 x 128 piece of W into its own 8 KiB of LDS with the direct-to-LDS
+// instructions of dma_piece32 (whole 128-byte lines per instruction: loading the MFMA fragments
+// straight into registers touches 32 partial lines per instruction and measured slower), while the
+// workgroup stages its valid rows of A once, as bf16, for all of K (the output map's float32 rows
+// go through registers and are rounded on the way).  Row r's 16-byte chunks are permuted within
+// groups of 16 (chunk c at (c & ~15) | ((c ^ r) & 15)), so that 16 lanes reading one chunk of 16
+// different rows hit distinct banks; fragment rows past the call's end read its last row.  LDS:
+// 64 KiB of W and 64 KiB of A for QKV; 128 KiB and 32 KiB for the output map.  The MFMA chain of
+// each slice and the order in which the slice sums are added are those of skinny_block, so the
+// bits are those of the tiled kernels.
+template <int kK>
+__device__ __forceinline__ int a_slot_bytes(int r, int c) {
+  return 16 * (r * (kK / 8) + ((c & ~15) | ((c ^ r) & 15)));
 }
+
+template <bool kAF32, int kK, int kRB>
+__global__ __launch_bounds__(64 * (kK / kKSlice)) void proj_skinny_kernel(
+    const void* __restrict__ a_ptr, int lda, int rows, const uint16_t* __restrict__ w, OutMap out) {
+  constexpr int kWaves = kK / kKSlice;
+  constexpr int kChunks = kK / 8;  // 16-byte bf16 chunks per staged row of A
+  constexpr int kSteps = kKSlice / 16;
+  constexpr int kWBytes = kWaves * 8192;
+  static_assert(kK % (kSliceGroup * kKSlice) == 0, "whole groups of slices");
+  static_assert(kRB <= 32 && (kRB * kChunks) % 64 == 0, "A's stage is whole 1 KiB direct-to-LDS blocks");
+  // W pieces (later the slice sums: 4 KiB per slice), then A
+  __shared__ __attribute__((aligned(1024))) uint8_t s_mem[kWBytes + kRB * kK * 2];
+  uint8_t* const s_a = s_mem + kWBytes;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int n = lane & 31, hk = lane >> 5;
+  const int col0 = 32 * blockIdx.x, row0 = kRB * blockIdx.y;
+  const int rows_valid = min(kRB, rows - row0);
+  const int k0 = wave * kKSlice;
+  uint8_t* const w_lds = s_mem + wave * 8192;
+  dma_piece32(w, kK, col0, 32, k0, w_lds, lane);
+
+  if constexpr (kAF32) {
+    for (int i = tid; i < rows_valid * kChunks; i += 64 * kWaves) {
+      const int r = i / kChunks, c = i % kChunks;
+      const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(a_ptr) +
+                                                          (size_t)(row0 + r) * lda + 8 * c);
+      const float4 lo = src[0], hi = src[1];
+      *reinterpret_cast<uint4*>(s_a + a_slot_bytes<kK>(r, c)) =
+          make_uint4(pack_bf16x2(lo.x, lo.y), pack_bf16x2(lo.z, lo.w), pack_bf16x2(hi.x, hi.y),
+                     pack_bf16x2(hi.z, hi.w));
+    }
+  } else {
+    // Instruction i fills the 64 slots 64 i .. 64 i + 63 of the permuted layout; slot p holds row
+    // p / kChunks, chunk (cp & ~15) | ((cp ^ r) & 15) with cp = p % kChunks (the permutation is its
+    // own inverse).  Slots of rows past the call's end take its last row and are never read.
+    const int n_instr = (rows_valid * kChunks + 63) / 64;
+    for (int i = wave; i < n_instr; i += kWaves) {
+      const int p = 64 * i + lane;
+      const int r = p / kChunks, cp = p % kChunks;
+      const int c = (cp & ~15) | ((cp ^ r) & 15);
+      const int rs = r < rows_valid ? r : rows_valid - 1;
+      __builtin_amdgcn_global_load_lds(
+          (global_cvoid_t*)(static_cast<const uint16_t*>(a_ptr) + (size_t)(row0 + rs) * lda + 8 * c),
+          (lds_void_t*)(s_a + 1024 * i), 16, 0, 0);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's direct-to-LDS copies have landed
+  __syncthreads();
+
+  floatx16_t acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+  const int ra = min(n, rows_valid - 1);
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) {
+    const bf16x8_t af = __builtin_bit_cast(
+        bf16x8_t, *reinterpret_cast<const uint4*>(s_a + a_slot_bytes<kK>(ra, (k0 >> 3) + 2 * s + hk)));
+    const bf16x8_t wf =
+        __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(w_lds + slot32_bytes(n, 2 * s + hk)));
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, wf, acc, 0, 0, 0);
+  }
+  __syncthreads();  // every wave is done with its piece of W; that LDS now takes the slice sums
+  float* const s_part = reinterpret_cast<float*>(s_mem);  // slice w at [w][accumulator element][lane]
+#pragma unroll
+  for (int v = 0; v < 16; ++v) s_part[(wave * 16 + v) * 64 + lane] = acc[v];
+  __syncthreads();
+
+  // Element e = (accumulator element v, lane l): C[row0 + 8(v/4) + 4(l/32) + v%4][col0 + l%32].
+  const int reg = (col0 >= out.lo[2]) ? 2 : (col0 >= out.lo[1]) ? 1 : 0;
+  uint16_t* dst = out.dst[reg];
+  const int ld = out.ld[reg];
+  for (int e = tid; e < 16 * 64; e += 64 * kWaves) {
+    const int v = e >> 6, l = e & 63;
+    const int rr = 8 * (v >> 2) + 4 * (l >> 5) + (v & 3);
+    if (rr >= rows_valid) continue;
+    float total = 0.f;
+#pragma unroll
+    for (int g0 = 0; g0 < kWaves; g0 += kSliceGroup) {
+      float group = 0.f;
+#pragma unroll
+      for (int sl = g0; sl < g0 + kSliceGroup; ++sl) group += s_part[(sl * 16 + v) * 64 + l];
+      total += group;
+    }
+    dst[(size_t)(row0 + rr) * ld + col0 - out.lo[reg] + (l & 31)] = (uint16_t)pack_bf16x2(total, 0.f);
+  }
+}
+
+constexpr int kQkvSkinnyRows = 32;  // tokens per few-token QKV workgroup
+constexpr int kOSkinnyRows = 8;     // tokens per few-token output-map workgroup (LDS: 128 + 32 KiB)
 
 // Workgroups launched for the tiles of `rows` rows x n_tn tile columns.  Rows owned by XCD: whole
 // tile rows padded to groups of 8, plus a partly filled last row dealt out over the XCDs by column.
@@ -795,8 +893,9 @@ hipError_t launch_qkv_proj(const uint16_t* x, const uint16_t* w_qkv, int n_tok, 
         x, kHidden, rs.tiled, w_qkv, n_wm, n_wn, rows_major, om, tiles > device_cus() ? 0 : tiles, tail_blocks,
         rs.tail);
   } else {
-    proj_skinny_kernel<false><<<dim3(kN / 32, (rs.tail + 31) / 32), dim3(64 * kSkinnyWaves), 0, stream>>>(
-        x, kHidden, rs.tail, w_qkv, kHidden, om);
+    proj_skinny_kernel<false, kHidden, kQkvSkinnyRows>
+        <<<dim3(kN / 32, (rs.tail + kQkvSkinnyRows - 1) / kQkvSkinnyRows), dim3(64 * (kHidden / kKSlice)), 0,
+           stream>>>(x, kHidden, rs.tail, w_qkv, om);
   }
   return hipGetLastError();
 }
@@ -821,8 +920,9 @@ hipError_t launch_o_proj(const float* attn, const uint16_t* w_o, int n_tok, uint
         attn, kK, rs.tiled, w_o, n_tm, n_tn, rows_major, om, tiles > device_cus() ? 0 : tiles, tail_blocks,
         rs.tail);
   } else {
-    proj_skinny_kernel<true><<<dim3(kHidden / 32, (rs.tail + 31) / 32), dim3(64 * kSkinnyWaves), 0, stream>>>(
-        attn, kK, rs.tail, w_o, kK, om);
+    proj_skinny_kernel<true, kK, kOSkinnyRows>
+        <<<dim3(kHidden / 32, (rs.tail + kOSkinnyRows - 1) / kOSkinnyRows), dim3(64 * (kK / kKSlice)), 0, stream>>>(
+            attn, kK, rs.tail, w_o, om);
   }
   return hipGetLastError();
 }
