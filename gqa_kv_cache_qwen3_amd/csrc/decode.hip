@@ -9,13 +9,18 @@
 //
 // decode_split: one wavefront per work item = (request b, split s, KV head g), where split s is
 //   the logical tokens [T s, min(T s + T, L_b)) with T = split_tokens(L_b) (64 or 512 tokens, by
-//   length).  Items are numbered densely: the flat split index f counts the splits of requests
-//   0..b-1 first, so the grid is 8 * sum_b split_parts(L_b) waves plus a tail of waves that find f
-//   beyond the total and exit.
+//   length).  Every request owns S = split_parts_bound(max_kv_len) slots: item (b, s, g) is wave
+//   8 (S b + s) + g, and its partial goes to slot S b + s of the workspace.  So a wave knows its
+//   request and split from its index alone and loads the length and the table entry of page s in
+//   one round (a dense numbering would need the lengths of the requests before it first); the
+//   waves of slots past a request's split count exit there, and the others load the query rows
+//   beside their first page.
 //   Both query heads of the GQA group (2g, 2g+1) are served from the same K/V loads.  The wave
 //   writes the split's normalised partial output and its log-sum-exp.
 // decode_merge: one workgroup per (request, query head) combines that request's partials with
-//   weights exp(lse_s - LSE), reducing over wavefronts and LDS.
+//   weights exp(lse_s - LSE), reducing over wavefronts and LDS.  It loads the slots' LSEs and the
+//   first partial of each lane group together with the length, so a request of at most 16 splits
+//   costs one round of loads.
 // With kAppend, decode_split also stores this step's token: the request's new K/V row goes to its
 //   slot at position kv_lens[b] - 1.  Only the last split of a request covers that position, so the
 //   wave of that split for KV head g writes head g's row (8 lanes, 32 bytes each) before it reads
@@ -45,32 +50,6 @@ __device__ __forceinline__ uint4 stream_load16(const uint16_t* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-// Locate flat split f: request b, split s within b, and b's KV length.  Wave-uniform.
-// kv_lens are clamped to [0, max_kv_len] so the number of partials never exceeds the workspace.
-__device__ __forceinline__ bool locate_split(const int32_t* __restrict__ kv_lens, int batch,
-                                             int max_kv_len, int f, int lane, int& b, int& s,
-                                             int& len_b) {
-  int carry = 0;
-  for (int c0 = 0; c0 < batch; c0 += 64) {
-    const int idx = c0 + lane;
-    int len = idx < batch ? kv_lens[idx] : 0;
-    len = min(max(len, 0), max_kv_len);
-    const int n = split_parts(len);
-    const int incl = wave_incl_scan(n, lane);
-    const int chunk_total = __shfl(incl, 63, 64);
-    if (f < carry + chunk_total) {
-      const unsigned long long hit = __ballot(carry + incl > f);
-      const int lb = __ffsll(hit) - 1;
-      b = c0 + lb;
-      s = f - (carry + __shfl(incl - n, lb, 64));
-      len_b = __shfl(len, lb, 64);
-      return true;
-    }
-    carry += chunk_total;
-  }
-  return false;
-}
-
 template <bool kAppend>
 __global__ __launch_bounds__(64) void decode_split_kernel(
     uint16_t* __restrict__ k_pages, uint16_t* __restrict__ v_pages, int num_pages,
@@ -80,13 +59,22 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
   const int lane = threadIdx.x;
   const int f = blockIdx.x / kKvHeads;
   const int g = blockIdx.x % kKvHeads;
-  int b, s, len;
-  if (!locate_split(kv_lens, batch, max_kv_len, f, lane, b, s, len)) return;
+  const int n_slots = split_parts_bound(max_kv_len);
+  const int b = f / n_slots, s = f % n_slots;
+  const int32_t* bt_row = block_tables + (size_t)b * bt_stride;
 
   const int sg = lane >> 3;  // slot group: slots 8a + sg
   const int o = lane & 7;    // chunks o and 8 + o of each row
 
-  // Query rows of heads 2g and 2g+1, this lane's 16 dims of each (as packed bf16 pairs).
+  // The length and the table entry of page s go out together (s < n_slots <= bt_stride); the
+  // query rows follow once the wave knows it has work, beside its first page's loads.
+  int len = kv_lens[b];
+  const int page_s = bt_row[s];
+  asm volatile("" ::"v"(len), "v"(page_s));
+  const int len_raw = len;
+  len = min(max(len, 0), max_kv_len);
+  if (s >= split_parts(len)) return;
+  // This lane's 16 dims of the query rows of heads 2g and 2g+1 (as packed bf16 pairs).
   uint4 qv[2][2];
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh) {
@@ -107,14 +95,13 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
 
   const int tok0 = s * split_tokens(len);
   const int tok1 = min(tok0 + split_tokens(len), len);
-  const int32_t* bt_row = block_tables + (size_t)b * bt_stride;
   // kAppend: the new token sits at position len - 1 when the request's length is in [1, max_kv_len]
   // (len is clamped to that range; a length outside it appends nothing).  Before reading any page,
   // the wave of the last split stores head g's new row: the lanes of slot group (len - 1) % 8, 32
   // bytes of K and 32 of V each.  The page loop below then loads exactly those bytes in the same
   // lanes, so each lane reads back what it wrote itself (program order within a thread).
-  if (kAppend && tok1 == len && len >= 1 && kv_lens[b] == len) {
-    const int page = bt_row[(len - 1) / kPage];
+  if (kAppend && tok1 == len && len >= 1 && len_raw == len) {
+    const int page = (len - 1) / kPage == s ? page_s : bt_row[(len - 1) / kPage];
     if (page >= 0 && page < num_pages) {  // an out-of-pool page is neither stored nor read
       const uint16_t* kn = k_new + ((size_t)b * kKvHeads + g) * kHeadDim;
       const uint16_t* vn = v_new + ((size_t)b * kKvHeads + g) * kHeadDim;
@@ -133,7 +120,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
   }
 
   for (int e0 = tok0 / kPage; e0 * kPage < tok1; ++e0) {
-    const int page = bt_row[e0];
+    const int page = e0 == s ? page_s : bt_row[e0];
     if (page < 0 || page >= num_pages) continue;
     const int nvalid = min(kPage, tok1 - e0 * kPage);
     const size_t blk = ((size_t)page * kKvHeads + g) * (kPage * kHeadDim);
@@ -273,42 +260,37 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
 // (a lane covers 8 dims with two 16-byte loads), so all partial rows of the request are in flight
 // at once instead of one after another; the 16 group sums are added in LDS.
 __global__ __launch_bounds__(256) void decode_merge_kernel(
-    const int32_t* __restrict__ kv_lens, int batch, int max_kv_len,
+    const int32_t* __restrict__ kv_lens, int max_kv_len,
     const float* __restrict__ part_o, const float* __restrict__ part_lse, float* __restrict__ out,
     float* __restrict__ lse_out) {
   __shared__ float s_w[kMaxParts];
   __shared__ float s_red[16][kHeadDim];
   __shared__ float s_wave[4];
-  __shared__ int s_first, s_n;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int h = blockIdx.x % kQHeads;
   const int b = blockIdx.x / kQHeads;
 
-  if (wave == 0) {
-    // first flat split of request b = sum over earlier requests of their split counts
-    int first = 0, len = 0;
-    for (int c0 = 0; c0 <= b; c0 += 64) {
-      const int idx = c0 + lane;
-      int ln = idx < batch ? kv_lens[idx] : 0;
-      ln = min(max(ln, 0), max_kv_len);
-      const int n = split_parts(ln);
-      if (b < c0 + 64) {
-        first += wave_sum_int(idx < b ? n : 0);
-        len = __shfl(ln, b - c0, 64);
-      } else {
-        first += wave_sum_int(n);
-      }
-    }
-    if (lane == 0) {
-      s_first = first;
-      s_n = split_parts(len);
-    }
+  // Request b's partials sit at b * n_slots ..; its length, the LSE of each slot and the first
+  // partial of each lane group (see below) are loaded together, and slots past the request's split
+  // count are ignored.
+  const int n_slots = split_parts_bound(max_kv_len);  // at most kMaxParts = blockDim.x
+  const int first = b * n_slots;
+  const int grp = tid >> 4;       // parts grp, grp + 16, ...
+  const int c = tid & 15;         // dims 8c .. 8c+7
+  float lse_t = kNegInf;
+  if (tid < n_slots) lse_t = part_lse[(size_t)(first + tid) * kQHeads + h];
+  float4 pre0 = make_float4(0.f, 0.f, 0.f, 0.f), pre1 = pre0;
+  if (grp < n_slots) {
+    const float4* src = reinterpret_cast<const float4*>(part_o + ((size_t)(first + grp) * kQHeads + h) * kHeadDim + 8 * c);
+    pre0 = src[0];
+    pre1 = src[1];
   }
-  __syncthreads();
-  const int first = s_first;
-  const int n_parts = s_n;
+  int len = kv_lens[b];
+  asm volatile("" ::"v"(len), "v"(lse_t), "v"(pre0.x), "v"(pre1.x));  // all loads out before the first wait
+  len = min(max(len, 0), max_kv_len);
+  const int n_parts = split_parts(len);
   float* orow = out + ((size_t)b * kQHeads + h) * kHeadDim;
   if (n_parts == 0) {  // no keys: zero output, LSE = -inf
     if (tid < kHeadDim) orow[tid] = 0.f;
@@ -318,10 +300,9 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
 
   // LSE of every part -> LDS, block max
   float mx = kNegInf;
-  for (int p = tid; p < n_parts; p += 256) {
-    const float v = part_lse[(size_t)(first + p) * kQHeads + h];
-    s_w[p] = v;
-    mx = fmaxf(mx, v);
+  if (tid < n_parts) {
+    s_w[tid] = lse_t;
+    mx = lse_t;
   }
   mx = wave_max(mx);
   if (lane == 0) s_wave[wave] = mx;
@@ -346,11 +327,14 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
   ws = s_wave[0] + s_wave[1] + s_wave[2] + s_wave[3];
 
   // weighted sum of the partial outputs
-  const int grp = tid >> 4;       // parts grp, grp + 16, ...
-  const int c = tid & 15;         // dims 8c .. 8c+7
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (grp < n_parts) {
+    const float w = s_w[grp];
+    acc[0] += w * pre0.x; acc[1] += w * pre0.y; acc[2] += w * pre0.z; acc[3] += w * pre0.w;
+    acc[4] += w * pre1.x; acc[5] += w * pre1.y; acc[6] += w * pre1.z; acc[7] += w * pre1.w;
+  }
 #pragma unroll 4
-  for (int p = grp; p < n_parts; p += 16) {
+  for (int p = grp + 16; p < n_parts; p += 16) {
     const float w = s_w[p];
     const float4* src = reinterpret_cast<const float4*>(part_o + ((size_t)(first + p) * kQHeads + h) * kHeadDim + 8 * c);
     const float4 v0 = src[0];
@@ -417,7 +401,7 @@ hipError_t launch_decode(const KvPools& kv, const uint16_t* q, const uint16_t* k
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   decode_merge_kernel<<<dim3(batch * kQHeads), dim3(256), 0, stream>>>(
-      kv_lens, batch, max_kv_len, part_o, part_lse, out, lse);
+      kv_lens, max_kv_len, part_o, part_lse, out, lse);
   return hipGetLastError();
 }
 

@@ -66,7 +66,8 @@ hipError_t launch_prefill(const KvPools& kv, const uint16_t* q, int chunk_len, i
                           float* out, float* lse, hipStream_t stream);
 
 // Workspace layout of the decode: partial O float32 [max_parts][kQHeads][kHeadDim], then partial
-// LSE float32 [max_parts][kQHeads], max_parts = batch * split_parts_bound(max_kv_len).
+// LSE float32 [max_parts][kQHeads], max_parts = batch * split_parts_bound(max_kv_len); split s of
+// request b uses part b * split_parts_bound(max_kv_len) + s.
 inline size_t decode_workspace_bytes(int batch, int max_kv_len) {
   const size_t parts = (size_t)batch * (size_t)split_parts_bound(max_kv_len);
   return parts * kQHeads * (kHeadDim + 1) * sizeof(float);
