@@ -1417,8 +1417,12 @@ def main():
     wl = WORKLOAD_CLASSES[args.workload](dev)
     torch.cuda.synchronize()
     if not isinstance(wl, (DecodeGraph, DecodeGraphBuckets)):
+        evented = not isinstance(wl, (FullDepth, Prefill90))
         for _ in range(args.warmup):
-            wl.step()
+            # The timed steps record HIP events; the warm-up records them too, since the first few dozen
+            # timing events of a process have been seen to slow the launches around them (about 3x for
+            # the launch-bound tiny workload) when they fell in the timed region.
+            wl.step(wl.timer.step_events() if evented else None)
     torch.cuda.synchronize()
     if isinstance(wl, FullDepth):
         wl.step_idx = 0  # the timed pass starts again at step 0 (appends rewrite the same slots)
