@@ -8,7 +8,7 @@
 // off the memory critical path.
 //
 // decode_split: one wavefront per work item = (request b, split s, KV head g), where split s is
-//   the logical tokens [T s, min(T s + T, L_b)) with T = split_tokens(L_b) (64 or 512 tokens, by
+//   the logical tokens [T s, min(T s + T, L_b)) with T = split_tokens(L_b) (64 to 512 tokens, by
 //   length).  Every request owns S = split_parts_bound(max_kv_len) slots: item (b, s, g) is wave
 //   8 (S b + s) + g, and its partial goes to slot S b + s of the workspace.  So a wave knows its
 //   request and split from its index alone and loads the length and the table entry of page s in

@@ -16,20 +16,26 @@ constexpr int kPage = 64;
 constexpr int kMaxContext = 131072;
 constexpr int kHidden = 1024;  // decoder hidden size (input of the QKV map, output of o_proj)
 // Decode split-K partition of a request of len tokens: consecutive runs of split_tokens(len)
-// logical tokens (whole pages).  A request of up to 1024 tokens is cut into one split per page
-// (up to 16), so even a lone short request spreads over many wavefronts; longer ones use 512-token
-// splits, where the per-split costs (query load, partial write, merge) stay under 1 % of the K/V
-// bytes and a large batch streams at full rate.  The partition depends only on the request's own
-// length, in logical token space, so a request's result never depends on the batch or on page
-// placement.
-__host__ __device__ constexpr int split_tokens(int len) { return len <= 1024 ? 64 : 512; }
+// logical tokens (whole pages).  The run doubles from 64 tokens with each doubling of the length
+// past 1024 and stops at 512: 64 up to 1024 tokens, 128 up to 2048, 256 up to 4096, 512 beyond.
+// So every request of up to 8192 tokens has between 9 and 16 splits (one page each up to 1024
+// tokens), and even a lone request spreads over many wavefronts, while long requests keep
+// 512-token splits, where the per-split costs (query load, partial write, merge) stay under 1 % of
+// the K/V bytes and a large batch streams at full rate.  The partition depends only on the
+// request's own length, in logical token space, so a request's result never depends on the batch
+// or on page placement.
+__host__ __device__ constexpr int split_shift(int len) {
+  return 6 + (len > 1024) + (len > 2048) + (len > 4096);
+}
+__host__ __device__ constexpr int split_tokens(int len) { return 1 << split_shift(len); }
 __host__ __device__ constexpr int split_parts(int len) {
-  return len <= 0 ? 0 : (len + split_tokens(len) - 1) / split_tokens(len);
+  return len <= 0 ? 0 : (len + split_tokens(len) - 1) >> split_shift(len);
 }
 // Most partials one request can have (131072 tokens in 512-token splits).
 constexpr int kMaxParts = split_parts(kMaxContext);
 // Most partials any request of at most max_len tokens can have: split_parts rises within each
-// length band and drops where the split grows, so the maximum sits at a band's upper end.
+// length band and drops where the split grows, so the maximum sits at a band's upper end, and
+// each band below 4096 tokens ends at 16 splits.
 __host__ __device__ constexpr int split_parts_bound(int max_len) {
   const int a = split_parts(max_len < 1024 ? max_len : 1024);
   const int b = split_parts(max_len);

@@ -190,8 +190,8 @@ size_t mtd_attn_prefill_workspace_bytes(int32_t chunk_len, int32_t num_q_heads, 
  * longest request holds at most max_kv_len tokens.  Returns 0 for arguments mtd_attn_decode would
  * reject.  The size is batch * P(max_kv_len) * num_q_heads * (head_dim + 1) * 4 bytes (split-K
  * partial outputs and log-sum-exps): a request of L tokens is split into runs of 64 tokens if
- * L <= 1024 and of 512 tokens above, and P(M) is the most runs any L <= M can have
- * (ceil(M / 64) up to 1024, 16 up to 8192, ceil(M / 512) above).
+ * L <= 1024, 128 if L <= 2048, 256 if L <= 4096 and 512 above, and P(M) is the most runs any
+ * L <= M can have (ceil(M / 64) up to 1024, 16 up to 8192, ceil(M / 512) above).
  */
 size_t mtd_attn_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t max_kv_len,
                                        int32_t head_dim);

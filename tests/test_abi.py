@@ -243,8 +243,9 @@ def test_prefill_workspace_size_formula(lib):
 
 
 def _split_tokens(n):
-    # the documented partition: 64-token runs up to 1024 tokens, else 512
-    return 64 if n <= 1024 else 512
+    # the documented partition: 64-token runs up to 1024 tokens, 128 up to 2048, 256 up to 4096,
+    # else 512
+    return 64 if n <= 1024 else 128 if n <= 2048 else 256 if n <= 4096 else 512
 
 
 # most partials of any length 1..M, by brute force over every length

@@ -34,9 +34,10 @@ def test_decode_ragged_small():
 
 
 def test_decode_split_bands():
-    """Lengths on both sides of the change of split size (64 to 512 tokens) and of 512-token split
-    boundaries, in one batch."""
-    lens = [960, 1023, 1024, 1025, 1300, 1536, 1537, 2048, 2049, 3000, 4096, 4097, 4609, 9000]
+    """Lengths on both sides of each change of split size (64, 128, 256 and 512 tokens at 1024, 2048
+    and 4096 tokens) and of split boundaries within each band, in one batch."""
+    lens = [960, 1023, 1024, 1025, 1152, 1153, 1300, 1536, 1537, 2048, 2049, 2304, 2305, 3000, 4095, 4096,
+            4097, 4609, 9000]
     log(f"decode split bands lens={lens}")
     batch = DecodeBatch(lens, 104)
     out, lse = run(batch)
@@ -44,7 +45,7 @@ def test_decode_split_bands():
     compare(out, lse, o_ref, l_ref, "decode split bands")
     # a request's split depends on its own length only: a sub-batch (other order, other bound)
     # gives the same bits
-    sub = [13, 0, 5, 9]
+    sub = [18, 0, 8, 11, 15]
     idx = torch.tensor(sub, device="cuda")
     out2, lse2 = mtd.mtd_attn_decode(batch.k, batch.v, batch.q[idx].contiguous(), batch.kv_lens[idx].contiguous(),
                                      batch.bt[idx].contiguous(), int(max(lens[i] for i in sub)), W.SCALE)

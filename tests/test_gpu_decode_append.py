@@ -58,9 +58,9 @@ def check_against_two_calls(batch: DecodeBatch, k_new, v_new, max_len, what):
 
 
 def test_decode_append_equals_append_then_decode():
-    """Ragged lengths around page (64) and split (64 / 512 tokens) boundaries; the pool after the call
+    """Ragged lengths around page (64) and split (64 to 512 tokens) boundaries; the pool after the call
     and the outputs equal the two-call sequence bit for bit, and match the oracle over that pool."""
-    lens = [1, 2, 63, 64, 65, 127, 511, 512, 513, 1000, 1025, 1536, 2049, 4097, 9000]
+    lens = [1, 2, 63, 64, 65, 127, 511, 512, 513, 1000, 1025, 1153, 1536, 2049, 2305, 4096, 4097, 9000]
     log(f"decode_append ragged lens={lens}")
     batch = DecodeBatch(lens, 301)
     poison_new_slots(batch)
