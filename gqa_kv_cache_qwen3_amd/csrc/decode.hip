@@ -19,8 +19,8 @@
 //   writes the split's normalised partial output and its log-sum-exp.
 // decode_merge: one workgroup per (request, query head) combines that request's partials with
 //   weights exp(lse_s - LSE), reducing over wavefronts and LDS.  It loads the slots' LSEs and the
-//   first partial of each lane group together with the length, so a request of at most 16 splits
-//   costs one round of loads.
+//   first partial rows of each lane group together with the length, so a request of at most 16
+//   splits (64 when the batch has at most 64 slots per request) costs one round of loads.
 // With kAppend, decode_split also stores this step's token: the request's new K/V row goes to its
 //   slot at position kv_lens[b] - 1.  Only the last split of a request covers that position, so the
 //   wave of that split for KV head g writes head g's row (8 lanes, 32 bytes each) before it reads
@@ -259,6 +259,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
 // w_s = exp(lse_s - LSE) go to LDS; then 16 lane groups of 16 lanes each take every 16th partial
 // (a lane covers 8 dims with two 16-byte loads), so all partial rows of the request are in flight
 // at once instead of one after another; the 16 group sums are added in LDS.
+template <int kPre>
 __global__ __launch_bounds__(256) void decode_merge_kernel(
     const int32_t* __restrict__ kv_lens, int max_kv_len,
     const float* __restrict__ part_o, const float* __restrict__ part_lse, float* __restrict__ out,
@@ -272,23 +273,36 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
   const int h = blockIdx.x % kQHeads;
   const int b = blockIdx.x / kQHeads;
 
-  // Request b's partials sit at b * n_slots ..; its length, the LSE of each slot and the first
-  // partial of each lane group (see below) are loaded together, and slots past the request's split
-  // count are ignored.
+  // Request b's partials sit at b * n_slots ..; its length, the LSE of each slot and the first kPre
+  // partial rows of each lane group (parts grp + 16 k, k < kPre; see below) are loaded together,
+  // and slots past the request's split count are ignored.  The launcher takes kPre = 4 for 17 to
+  // 64 slots, so that a request of up to 64 splits has all its partials in flight in one round,
+  // and kPre = 1 otherwise: with at most 16 slots one row per group covers them, and with more
+  // than 64 the rows past a request's split count would cost more than the round they save.
   const int n_slots = split_parts_bound(max_kv_len);  // at most kMaxParts = blockDim.x
   const int first = b * n_slots;
   const int grp = tid >> 4;       // parts grp, grp + 16, ...
   const int c = tid & 15;         // dims 8c .. 8c+7
   float lse_t = kNegInf;
   if (tid < n_slots) lse_t = part_lse[(size_t)(first + tid) * kQHeads + h];
-  float4 pre0 = make_float4(0.f, 0.f, 0.f, 0.f), pre1 = pre0;
-  if (grp < n_slots) {
-    const float4* src = reinterpret_cast<const float4*>(part_o + ((size_t)(first + grp) * kQHeads + h) * kHeadDim + 8 * c);
-    pre0 = src[0];
-    pre1 = src[1];
+  // Unconditional loads (a row past the request's slots is clamped into them), so that no branch
+  // joins force a wait between them.
+  float4 pre[kPre][2];
+#pragma unroll
+  for (int k = 0; k < kPre; ++k) {
+    const int p = min(grp + 16 * k, n_slots - 1);
+    const float4* src = reinterpret_cast<const float4*>(part_o + ((size_t)(first + p) * kQHeads + h) * kHeadDim + 8 * c);
+    pre[k][0] = src[0];
+    pre[k][1] = src[1];
   }
   int len = kv_lens[b];
-  asm volatile("" ::"v"(len), "v"(lse_t), "v"(pre0.x), "v"(pre1.x));  // all loads out before the first wait
+  // all loads out before the first wait
+  static_assert(kPre == 1 || kPre == 4, "prefetch depths the launcher uses");
+  if constexpr (kPre == 1)
+    asm volatile("" ::"v"(len), "v"(lse_t), "v"(pre[0][0].x), "v"(pre[0][1].x));
+  else
+    asm volatile("" ::"v"(len), "v"(lse_t), "v"(pre[0][0].x), "v"(pre[0][1].x), "v"(pre[1][0].x),
+                 "v"(pre[1][1].x), "v"(pre[2][0].x), "v"(pre[2][1].x), "v"(pre[3][0].x), "v"(pre[3][1].x));
   len = min(max(len, 0), max_kv_len);
   const int n_parts = split_parts(len);
   float* orow = out + ((size_t)b * kQHeads + h) * kHeadDim;
@@ -328,13 +342,18 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
 
   // weighted sum of the partial outputs
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  if (grp < n_parts) {
-    const float w = s_w[grp];
-    acc[0] += w * pre0.x; acc[1] += w * pre0.y; acc[2] += w * pre0.z; acc[3] += w * pre0.w;
-    acc[4] += w * pre1.x; acc[5] += w * pre1.y; acc[6] += w * pre1.z; acc[7] += w * pre1.w;
+#pragma unroll
+  for (int k = 0; k < kPre; ++k) {
+    const int p = grp + 16 * k;
+    if (p < n_parts) {
+      const float w = s_w[p];
+      const float4 v0 = pre[k][0], v1 = pre[k][1];
+      acc[0] += w * v0.x; acc[1] += w * v0.y; acc[2] += w * v0.z; acc[3] += w * v0.w;
+      acc[4] += w * v1.x; acc[5] += w * v1.y; acc[6] += w * v1.z; acc[7] += w * v1.w;
+    }
   }
 #pragma unroll 4
-  for (int p = grp + 16; p < n_parts; p += 16) {
+  for (int p = grp + 16 * kPre; p < n_parts; p += 16) {
     const float w = s_w[p];
     const float4* src = reinterpret_cast<const float4*>(part_o + ((size_t)(first + p) * kQHeads + h) * kHeadDim + 8 * c);
     const float4 v0 = src[0];
@@ -400,8 +419,13 @@ hipError_t launch_decode(const KvPools& kv, const uint16_t* q, const uint16_t* k
         max_kv_len, scale * kLog2e, part_o, part_lse);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  decode_merge_kernel<<<dim3(batch * kQHeads), dim3(256), 0, stream>>>(
-      kv_lens, max_kv_len, part_o, part_lse, out, lse);
+  const int n_slots = split_parts_bound(max_kv_len);
+  if (n_slots > 16 && n_slots <= 64)
+    decode_merge_kernel<4><<<dim3(batch * kQHeads), dim3(256), 0, stream>>>(
+        kv_lens, max_kv_len, part_o, part_lse, out, lse);
+  else
+    decode_merge_kernel<1><<<dim3(batch * kQHeads), dim3(256), 0, stream>>>(
+        kv_lens, max_kv_len, part_o, part_lse, out, lse);
   return hipGetLastError();
 }
 
