@@ -55,7 +55,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
     uint16_t* __restrict__ k_pages, uint16_t* __restrict__ v_pages, int num_pages,
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
     const int32_t* __restrict__ kv_lens, const int32_t* __restrict__ block_tables, int bt_stride,
-    int batch, int max_kv_len, float scale_log2, float* __restrict__ part_o, float* __restrict__ part_lse) {
+    int max_kv_len, float scale_log2, float* __restrict__ part_o, float* __restrict__ part_lse) {
   const int lane = threadIdx.x;
   const int f = blockIdx.x / kKvHeads;
   const int g = blockIdx.x % kKvHeads;
@@ -411,11 +411,11 @@ hipError_t launch_decode(const KvPools& kv, const uint16_t* q, const uint16_t* k
   const unsigned n_waves = (unsigned)(parts * kKvHeads);
   if (k_new != nullptr)
     decode_split_kernel<true><<<dim3(n_waves), dim3(64), 0, stream>>>(
-        kv.k, kv.v, kv.num_pages, q, k_new, v_new, kv_lens, block_tables, bt_stride, batch, max_kv_len,
+        kv.k, kv.v, kv.num_pages, q, k_new, v_new, kv_lens, block_tables, bt_stride, max_kv_len,
         scale * kLog2e, part_o, part_lse);
   else
     decode_split_kernel<false><<<dim3(n_waves), dim3(64), 0, stream>>>(
-        kv.k, kv.v, kv.num_pages, q, nullptr, nullptr, kv_lens, block_tables, bt_stride, batch,
+        kv.k, kv.v, kv.num_pages, q, nullptr, nullptr, kv_lens, block_tables, bt_stride,
         max_kv_len, scale * kLog2e, part_o, part_lse);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
