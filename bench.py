@@ -452,7 +452,7 @@ class Tiny:
         for e in evs:
             t.collect(e)
         return {"prefill_ms": t.mean_ms("prefill"), "decode_ms_per_step": t.mean_ms("decode") / self.steps,
-                "note": "eager library calls, host-launch-bound: varies with the host (1.0-4.3 ms per whole step measured)"}
+                "note": "eager library calls: bound by the host's launch rate, which varies between runs and hosts"}
 
     def config(self):
         return {"workload": "tiny: one 439-token one-shot prefill (30 s of audio + 64 prompt tokens), then 32 decode "
